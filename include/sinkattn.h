@@ -1,0 +1,192 @@
+/*
+ * sinkattn.h -- C ABI of the MI355X (gfx950) sink-GQA attention library.
+ *
+ * One attention layer of the gpt-oss family on its hot path: YaRN /
+ * NTK-by-parts rotary embedding at global positions, an append-only KV cache
+ * with snapshot/restore, and grouped-query attention under a full causal
+ * mask or a sliding band, with a learned per-head sink logit appended as an
+ * extra softmax column that is dropped after normalisation.  Prefill and
+ * single-token decode.
+ *
+ * Sources (page title, section):
+ *   "MoE-Xtend" README  -- DESIGN CONTRACTS (global positions, mask alignment,
+ *       append-only cache, GQA shape contract), ATTENTION STACK (scores,
+ *       causal/window masks, sink column), ROPE + SCALING (YaRN blend and
+ *       concentration), KV CACHE (layout, extend, snapshot/restore, sizing),
+ *       ARCHITECTURE (prefill writes the prompt KV once; decode appends one
+ *       row per step).
+ *   "GQA Attention" study note on gpt-oss -- How it works (q_mult grouping,
+ *       band p-W < j <= p, sinks per query head, sm_scale = 1/sqrt(d_h)).
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns an sa_status (0 = SA_OK).  On any non-OK status
+ *     nothing has been enqueued and no library state has changed;
+ *     sa_last_error() returns a message for the calling thread.
+ *   - Device pointers are HIP device memory on the current device, owned by
+ *     the caller; the library never allocates or frees device memory and
+ *     never synchronises.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and completes asynchronously.
+ *   - Tensors are dense and row-major.  Element type is bf16 (SA_BF16) or
+ *     fp32 (SA_F32); one call uses one type for all of its activations and
+ *     cache rows.  Sinks are always fp32.
+ *   - Sizes are element counts unless a name ends in _bytes.
+ *
+ * Cache memory layout (per layer; C = capacity rows, a multiple of 32):
+ *   K: [B, C, n_kv, d_h]                     -- the pages' [B, T_cache, H_kv, d]
+ *   V: [B, C/32, n_kv, d_h, 32]              -- V[b, j, g, e] lives at
+ *        (((b*(C/32) + j/32)*n_kv + g)*d_h + e)*32 + j%32
+ *   The V blocking puts 32 consecutive keys of one (head, coordinate) next
+ *   to each other, which is the operand order of the gfx950 matrix cores for
+ *   the probability x value product.  Both buffers hold
+ *   B*C*n_kv*d_h elements.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_ARG = -1,       /* null pointer, non-positive size, bad parameter   */
+  SA_ERR_SHAPE = -2,     /* n_q % n_kv != 0, unsupported d_h, shape differs
+                            from the cache's, capacity not a multiple of 32  */
+  SA_ERR_DTYPE = -3,     /* unknown dtype, or dtype differs from the cache's */
+  SA_ERR_CAPACITY = -4,  /* append past capacity, or queries past the rows
+                            already in the cache                             */
+  SA_ERR_SNAPSHOT = -5,  /* snapshot of another cache, or rows below it were
+                            rewritten since it was taken                     */
+  SA_ERR_HIP = -6        /* a HIP launch error                               */
+} sa_status;
+
+typedef enum { SA_BF16 = 0, SA_F32 = 1 } sa_dtype;
+
+/* YaRN / NTK-by-parts parameters ("MoE-Xtend" README, ROPE + SCALING).
+ * factor = s (1.0 = plain RoPE, theta_i = base^(-2i/d)); orig_ctx = L_train;
+ * ntk_alpha < ntk_beta are the cutpoint turn counts.  Requires d_h even and
+ * positive, base > 1, factor >= 1, 0 < ntk_alpha < ntk_beta, orig_ctx > 0. */
+typedef struct {
+  int32_t d_h;
+  double base;
+  double factor;
+  int64_t orig_ctx;
+  double ntk_alpha;
+  double ntk_beta;
+} sa_yarn;
+
+/* Message describing the calling thread's last non-OK status ("" if none).
+ * The pointer stays valid until the thread's next library call. */
+const char* sa_last_error(void);
+
+/* Host only.  The blended per-pair angular rates inv_freq[0 .. d_h/2) and
+ * the concentration c = 0.1*ln(s) + 1, in fp64 ("MoE-Xtend" README, ROPE +
+ * SCALING).  inv_freq: host array of d_h/2 doubles, caller-owned. */
+int sa_yarn_inv_freq(const sa_yarn* y, double* inv_freq, double* concentration);
+
+/* Host only.  KV bytes of L layers: 2*L*B*T*H_kv*d*dtype_bytes ("MoE-Xtend"
+ * README, KV CACHE, memory scaling).  Returns -1 if an argument is negative
+ * or the product overflows int64. */
+int64_t sa_kv_cache_bytes(int64_t L, int64_t B, int64_t T, int64_t H_kv,
+                          int64_t d, int64_t dtype_bytes);
+
+/* Rotate x in place at global positions offset + t ("MoE-Xtend" README,
+ * DESIGN CONTRACTS and ROPE + SCALING).  x: device [B, T, n_heads, d_h] of
+ * `dtype`.  Coordinate i pairs with i + d_h/2:
+ *   y_i       = c*(x_i cos a - x_{i+d/2} sin a)
+ *   y_{i+d/2} = c*(x_{i+d/2} cos a + x_i sin a),  a = (offset+t)*inv_freq_i.
+ * Angles, rates and the rotation are evaluated in fp64 and rounded once to
+ * `dtype` (round to nearest, ties to even).  Positions are never wrapped.
+ * Apply to Q (n_heads = n_q) and K (n_heads = n_kv), never to V.
+ * Requires d_h == y->d_h, d_h % 8 == 0, d_h <= 256, offset >= 0. */
+int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h,
+                    int64_t offset, const sa_yarn* y, void* stream);
+
+/* Opaque host-side handle of one layer's cache.  K/V storage is the
+ * caller's (layout above); the handle records the shape, the offset (rows
+ * written: the next append goes to row `offset` of every sequence; one
+ * offset is shared by the batch), and the write log used to validate
+ * snapshots. */
+typedef struct sa_kv_cache sa_kv_cache;
+
+typedef struct {
+  int64_t offset;
+  uint64_t cache_id;
+  uint64_t stamp;
+} sa_kv_snapshot;
+
+/* Create a handle over caller-owned buffers k, v (device, B*capacity*n_kv*
+ * d_h elements each).  `offset` rows (0 .. capacity) are taken as already
+ * written (a pre-filled prefix; K rows already rotated).  capacity must be
+ * a positive multiple of 32. */
+int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B,
+                    int64_t capacity, int n_kv, int d_h, int64_t offset);
+int kv_cache_destroy(sa_kv_cache* c);
+/* Rows written so far; -1 for a null handle. */
+int64_t kv_cache_offset(const sa_kv_cache* c);
+
+/* Append T_new rows to every sequence ("MoE-Xtend" README, KV CACHE: extend
+ * writes [offset, offset+T_new) then advances offset).  k_rot: device
+ * [B, T_new, n_kv, d_h], already rotated; v: device [B, T_new, n_kv, d_h],
+ * unrotated.  Rows are copied bit for bit (V into its blocked layout).  The
+ * offset advances at enqueue time.  A decode step appends T_new = 1.
+ * SA_ERR_CAPACITY if offset + T_new > capacity. */
+int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v,
+                    int T_new, void* stream);
+
+/* O(1) host bookkeeping ("prefill once, decode many").  A snapshot records
+ * the offset; restore rewinds the offset to it.  Restoring is refused with
+ * SA_ERR_SNAPSHOT if the snapshot belongs to another cache or if any append
+ * made after it started below its offset (its rows were overwritten). */
+int kv_cache_snapshot(const sa_kv_cache* c, sa_kv_snapshot* out);
+int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap);
+
+/* Sink attention of T_q new queries against the cache ("MoE-Xtend" README,
+ * ATTENTION STACK; "GQA Attention" study note, How it works).
+ *   q:    device [B, T_q, n_q, d_h], already rotated; query t sits at global
+ *         position p = q_offset + t.
+ *   sinks: device fp32 [n_q], one logit per query head in scaled-logit
+ *         units (not multiplied by sm_scale); -inf disables a head's sink.
+ *   out:  device [B, T_q, n_q, d_h].
+ * For query head h, KV head g = h / (n_q/n_kv), allowed keys
+ *   A(p) = { j : max(0, p - window + 1) <= j <= p }  (window > 0: band of
+ *   `window` keys including the diagonal) or { j : 0 <= j <= p } (window
+ *   <= 0: full causal), and l_j = sm_scale * <q, K_j>:
+ *   out = sum_{j in A} e^{l_j} V_j / (e^{sigma_h} + sum_{j in A} e^{l_j}).
+ * Requires q_offset + T_q <= kv_cache_offset(c) (append first); n_kv and
+ * d_h must equal the cache's.  bf16: d_h in {64, 96, 128},
+ * n_q/n_kv <= 128, matrix-core kernel with fp32 accumulation; fp32: d_h % 8
+ * == 0, d_h <= 256, vector kernel. */
+int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks,
+                     void* out, int B, int T_q, int n_q, int n_kv, int d_h,
+                     int window, float sm_scale, int64_t q_offset,
+                     void* stream);
+
+/* Bytes of fp32 workspace that sinkattn_decode needs for any cache offset up
+ * to `capacity` with these shapes (0 on invalid arguments). */
+size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h,
+                                       int64_t capacity);
+
+/* One decode step's attention: the single query token of each sequence sits
+ * at position p = kv_cache_offset(c) - 1 (its own K/V row appended just
+ * before, "MoE-Xtend" README, ARCHITECTURE: append KV at offset=t, then
+ * t++).  q: device [B, 1, n_q, d_h]; out: device [B, 1, n_q, d_h];
+ * workspace: device scratch of at least
+ * sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, capacity) bytes, whose
+ * contents are overwritten.  The allowed key set is split into chunks
+ * reduced in parallel and merged in a fixed order (deterministic), with the
+ * sink added once at the merge.  bf16: d_h in {64, 96, 128}, n_q/n_kv <= 16;
+ * fp32: as sinkattn_prefill. */
+int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks,
+                    void* out, int B, int n_q, int n_kv, int d_h, int window,
+                    float sm_scale, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

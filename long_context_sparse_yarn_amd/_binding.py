@@ -1,0 +1,277 @@
+"""ctypes binding over libsinkattn.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module turns
+torch tensors into device pointers, torch's current stream into the HIP
+stream argument, and non-OK statuses into exceptions.  It loads the library
+at import and fails loudly when it is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
+
+SA_BF16, SA_F32 = 0, 1
+STATUS = {0: "SA_OK", -1: "SA_ERR_ARG", -2: "SA_ERR_SHAPE", -3: "SA_ERR_DTYPE",
+          -4: "SA_ERR_CAPACITY", -5: "SA_ERR_SNAPSHOT", -6: "SA_ERR_HIP"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libsinkattn.so is not built (%s); run `python -m long_context_sparse_yarn_amd.build` "
+        "or __graft_entry__.build()" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _u64, _f32, _f64 = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                                ctypes.c_float, ctypes.c_double)
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+
+
+class SaYarn(ctypes.Structure):
+    _fields_ = [("d_h", ctypes.c_int32), ("base", _f64), ("factor", _f64),
+                ("orig_ctx", _i64), ("ntk_alpha", _f64), ("ntk_beta", _f64)]
+
+
+class SaSnapshot(ctypes.Structure):
+    _fields_ = [("offset", _i64), ("cache_id", _u64), ("stamp", _u64)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sa_last_error = _sig("sa_last_error", ctypes.c_char_p)
+_sa_yarn_inv_freq = _sig("sa_yarn_inv_freq", _i32, ctypes.POINTER(SaYarn),
+                         ctypes.POINTER(_f64), ctypes.POINTER(_f64))
+_sa_kv_cache_bytes = _sig("sa_kv_cache_bytes", _i64, _i64, _i64, _i64, _i64, _i64, _i64)
+_yarn_rope_apply = _sig("yarn_rope_apply", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                        ctypes.POINTER(SaYarn), _vp)
+_kv_cache_create = _sig("kv_cache_create", _i32, ctypes.POINTER(_vp), _vp, _vp, _i32, _i32,
+                        _i64, _i32, _i32, _i64)
+_kv_cache_destroy = _sig("kv_cache_destroy", _i32, _vp)
+_kv_cache_offset = _sig("kv_cache_offset", _i64, _vp)
+_kv_cache_append = _sig("kv_cache_append", _i32, _vp, _vp, _vp, _i32, _vp)
+_kv_cache_snapshot = _sig("kv_cache_snapshot", _i32, _vp, ctypes.POINTER(SaSnapshot))
+_kv_cache_restore = _sig("kv_cache_restore", _i32, _vp, ctypes.POINTER(SaSnapshot))
+_sinkattn_prefill = _sig("sinkattn_prefill", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                         _i32, _i32, _f32, _i64, _vp)
+_sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
+_sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                        _i32, _f32, _vp, _sz, _vp)
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), msg))
+        self.status = status
+
+
+def last_error() -> str:
+    return (_sa_last_error() or b"").decode()
+
+
+def _check(st: int) -> None:
+    if st != 0:
+        raise SinkAttnError(st, last_error())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+@dataclass(frozen=True)
+class Yarn:
+    d_h: int
+    base: float = 150000.0
+    factor: float = 32.0
+    orig_ctx: int = 4096
+    ntk_alpha: float = 1.0
+    ntk_beta: float = 32.0
+
+    def c_struct(self) -> SaYarn:
+        return SaYarn(self.d_h, self.base, self.factor, self.orig_ctx, self.ntk_alpha,
+                      self.ntk_beta)
+
+
+def yarn_inv_freq(y: Yarn):
+    """Host table: (inv_freq list of d_h/2 floats, concentration)."""
+    arr = (_f64 * (y.d_h // 2))()
+    c = _f64()
+    s = y.c_struct()
+    _check(_sa_yarn_inv_freq(ctypes.byref(s), arr, ctypes.byref(c)))
+    return list(arr), c.value
+
+
+def kv_cache_bytes(L, B, T, H_kv, d, dtype_bytes) -> int:
+    return int(_sa_kv_cache_bytes(L, B, T, H_kv, d, dtype_bytes))
+
+
+def yarn_rope_apply(x: torch.Tensor, offset: int, y: Yarn, stream=None) -> torch.Tensor:
+    """In place on x [B, T, H, d]; returns x."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B, T, H, d]")
+    B, T, H, d = x.shape
+    s = y.c_struct()
+    _check(_yarn_rope_apply(_dev(x, "x"), _dtype_code(x), B, T, H, d, int(offset),
+                            ctypes.byref(s), _stream(stream)))
+    return x
+
+
+def v_cache_shape(B: int, C: int, n_kv: int, d: int):
+    """Shape of the blocked V buffer: [B, C/32, n_kv, d, 32]."""
+    return (B, C // 32, n_kv, d, 32)
+
+
+def v_rows(v_buf: torch.Tensor) -> torch.Tensor:
+    """View a blocked V buffer [B, C/32, n_kv, d, 32] as rows [B, C, n_kv, d]."""
+    B, nb, n_kv, d, w = v_buf.shape
+    return v_buf.permute(0, 1, 4, 2, 3).reshape(B, nb * w, n_kv, d)
+
+
+def v_blocked(v_rows_t: torch.Tensor) -> torch.Tensor:
+    """Rows [B, C, n_kv, d] -> blocked layout [B, C/32, n_kv, d, 32] (a copy)."""
+    B, C, n_kv, d = v_rows_t.shape
+    return v_rows_t.reshape(B, C // 32, 32, n_kv, d).permute(0, 1, 3, 4, 2).contiguous()
+
+
+class KVCache:
+    """One layer's cache over caller-owned buffers k [B,C,n_kv,d] and
+    v [B,C/32,n_kv,d,32] (see v_cache_shape)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, offset: int = 0):
+        if k.dim() != 4 or v.dim() != 5:
+            raise ValueError("k must be [B,C,n_kv,d], v [B,C/32,n_kv,d,32]")
+        B, C, n_kv, d = k.shape
+        if tuple(v.shape) != v_cache_shape(B, C, n_kv, d) or v.dtype != k.dtype:
+            raise ValueError("v buffer shape/dtype does not match k")
+        self.k, self.v = k, v
+        self.B, self.capacity, self.n_kv, self.d = B, C, n_kv, d
+        self.dtype = k.dtype
+        h = _vp()
+        _check(_kv_cache_create(ctypes.byref(h), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
+                                B, C, n_kv, d, int(offset)))
+        self._h = h
+
+    @classmethod
+    def empty(cls, B, C, n_kv, d, dtype=torch.bfloat16, device="cuda", fill=None):
+        k = torch.empty((B, C, n_kv, d), dtype=dtype, device=device)
+        v = torch.empty(v_cache_shape(B, C, n_kv, d), dtype=dtype, device=device)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        return cls(k, v)
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def offset(self) -> int:
+        return int(_kv_cache_offset(self._h))
+
+    def append(self, k_rot: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        if k_rot.shape != v.shape or k_rot.dim() != 4:
+            raise ValueError("k_rot and v must both be [B, T_new, n_kv, d]")
+        if k_rot.dtype != self.dtype or v.dtype != self.dtype:
+            raise TypeError("dtype differs from the cache's")
+        if (k_rot.shape[0], k_rot.shape[2], k_rot.shape[3]) != (self.B, self.n_kv, self.d):
+            raise ValueError("shape differs from the cache's")
+        _check(_kv_cache_append(self._h, _dev(k_rot, "k_rot"), _dev(v, "v"),
+                                int(k_rot.shape[1]), _stream(stream)))
+
+    def snapshot(self) -> SaSnapshot:
+        s = SaSnapshot()
+        _check(_kv_cache_snapshot(self._h, ctypes.byref(s)))
+        return s
+
+    def restore(self, snap: SaSnapshot) -> None:
+        _check(_kv_cache_restore(self._h, ctypes.byref(snap)))
+
+    def v_rows(self) -> torch.Tensor:
+        return v_rows(self.v)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _kv_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sinkattn_prefill(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window: int,
+                     sm_scale: float, q_offset: int, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """q [B, T_q, n_q, d] (rotated), sinks fp32 [n_q] -> out [B, T_q, n_q, d]."""
+    B, T_q, n_q, d = q.shape
+    if sinks.dtype != torch.float32 or sinks.numel() != n_q:
+        raise ValueError("sinks must be float32 [n_q]")
+    if q.dtype != cache.dtype:
+        raise TypeError("q dtype differs from the cache's")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_sinkattn_prefill(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"), _dev(out, "out"),
+                             B, T_q, n_q, cache.n_kv, d, int(window), float(sm_scale),
+                             int(q_offset), _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(B, n_q, n_kv, d, capacity) -> int:
+    return int(_sinkattn_decode_ws(B, n_q, n_kv, d, capacity))
+
+
+def decode_workspace(cache: KVCache, n_q: int) -> torch.Tensor:
+    n = decode_workspace_bytes(cache.B, n_q, cache.n_kv, cache.d, cache.capacity)
+    return torch.empty(max(1, n // 4), dtype=torch.float32, device=cache.k.device)
+
+
+def sinkattn_decode(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window: int,
+                    sm_scale: float, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q [B, 1, n_q, d] of the token at position cache.offset - 1."""
+    B, T1, n_q, d = q.shape
+    if T1 != 1:
+        raise ValueError("decode takes exactly one query token per sequence")
+    if sinks.dtype != torch.float32 or sinks.numel() != n_q:
+        raise ValueError("sinks must be float32 [n_q]")
+    if q.dtype != cache.dtype:
+        raise TypeError("q dtype differs from the cache's")
+    if workspace is None:
+        workspace = decode_workspace(cache, n_q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_sinkattn_decode(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"), _dev(out, "out"),
+                            B, n_q, cache.n_kv, d, int(window), float(sm_scale),
+                            _dev(workspace, "workspace"), workspace.numel() * 4,
+                            _stream(stream)))
+    return out

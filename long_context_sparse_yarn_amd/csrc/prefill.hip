@@ -1,0 +1,282 @@
+// sinkattn_prefill (bf16): sink-augmented grouped-query attention of a chunk
+// of queries against the KV cache, on the gfx950 matrix cores.
+//
+// What is computed ("MoE-Xtend" README, ATTENTION STACK; "GQA Attention"
+// study note, How it works): for query head h of KV group g = h / q_mult at
+// global position p, softmax over the allowed scores sm_scale*<q, K_j>
+// (j <= p, and j > p - W for a band of W keys) together with one extra
+// column holding the head's sink logit; the sink column is dropped after
+// normalisation and the remaining weights mix V.
+//
+// How (gfx950 design):
+//  * A workgroup (4 waves) owns one (b, g) pair and a block of query
+//    positions.  All q_mult heads of the group are stacked, so every 64-key
+//    K/V tile staged in LDS feeds 128 (or 256) query rows at once.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16:
+//    each lane then owns one query column and 16 of the tile's keys, so the
+//    softmax state (running max m, partial sum l) is per lane.  K rows are
+//    read from LDS in a permuted order chosen so that each lane's keys are 8
+//    consecutive keys per 32-key half; its exp'd scores packed to bf16 are
+//    directly the B operand of O^T += V^T P^T, and V^T comes from the
+//    blocked V cache layout (32 keys contiguous per coordinate).
+//  * Online softmax in base 2 (log2 e folded into the scale and the sink),
+//    seeded with the sink: m = sigma*log2e, l = 1 (sigma = -inf: m = -inf,
+//    l = 0).  Masks are computed from positions, only on tiles that cross
+//    the diagonal or the band edge; rows at or past the last query position
+//    are zero-filled in LDS, so unwritten cache rows are never read.
+//  * K/V tiles are double-buffered: the next tile's global loads are in
+//    flight while the current tile is multiplied.
+//  * Workgroups of the same (b, g) are spread so that, when B*n_kv is a
+//    multiple of 8, every XCD serves fixed KV heads and their K/V stays in
+//    that XCD's L2; the longest (latest) query blocks start first.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 64;  // keys per tile
+
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
+  constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
+  constexpr int DT = D / 16;          // coordinate tiles of O^T
+  constexpr int KP = D + 8;           // LDS row pitch of K (elements)
+  constexpr int VP = 32 + 8;          // LDS row pitch of V^T (elements)
+  constexpr int KCH = kTile * D / 8 / kThreads;   // 16-byte K chunks per thread
+  constexpr int VCH = 2 * D * 4 / kThreads;       // 16-byte V chunks per thread
+  static_assert(KCH * kThreads * 8 == kTile * D, "K tile split");
+  static_assert(VCH * kThreads == 2 * D * 4, "V tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTile * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * D * VP];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int pairs = a.B * a.n_kv;
+  const int pair = blockIdx.x % pairs;
+  const int qb = n_qb - 1 - (int)(blockIdx.x / pairs);
+  const int b = pair / a.n_kv;
+  const int g = pair - b * a.n_kv;
+  const int p0 = qb * BQ;
+  const int t_end = min(p0 + BQ, a.T_q);
+  const int64_t C = a.C;
+
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc);
+
+  // ---- this lane's query rows (one per 16-wide N tile)
+  int tpos[NT], head[NT];
+  bool rvalid[NT];
+  u32x4 qop[NT][KS];
+  float m_run[NT], l_run[NT];
+  f32x4 O[DT][NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int r = (wave * NT + n) * 16 + j;
+    const int m = r % a.q_mult;
+    int tp = p0 + r / a.q_mult;
+    rvalid[n] = (r < BQ * a.q_mult) && (tp < a.T_q);
+    if (!rvalid[n]) tp = t_end - 1;
+    tpos[n] = tp;
+    head[n] = g * a.q_mult + m;
+    const uint16_t* qrow = q + (((int64_t)b * a.T_q + tp) * a.n_q + head[n]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[n][ks] = rvalid[n] ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
+    const float sg = a.sinks[head[n]] * SA_LOG2E;
+    m_run[n] = sg;                                   // -inf when the sink is off
+    l_run[n] = (g4 == 0 && sg != -INFINITY) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const float scale = a.sm_scale * SA_LOG2E;
+  const int64_t P_min = a.q_offset + p0;
+  const int64_t P_max = a.q_offset + t_end - 1;
+  const int64_t lo = a.window > 0 ? max((int64_t)0, P_min - a.window + 1) : 0;
+  const int64_t hi = P_max + 1;   // keys >= hi are masked for every row here
+  const int64_t t_first = lo / kTile, t_last = (hi - 1) / kTile;
+
+  u32x4 kreg[KCH], vreg[VCH];
+  auto load_tile = [&](int64_t t) {
+    const int64_t k0 = t * kTile;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (D / 8), ch = c - row * (D / 8);
+      const int64_t key = k0 + row;
+      kreg[i] = key < hi ? ld16(kc + ((b * C + key) * a.n_kv + g) * D + 8 * ch)
+                         : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int blk = c / (D * 4);
+      const int rem = c - blk * (D * 4);
+      const int dd = rem >> 2, ch = rem & 3;
+      const int64_t key0 = k0 + 32 * blk + 8 * ch;
+      u32x4 v = {0, 0, 0, 0};
+      if (key0 < hi) {
+        const int64_t kb = k0 / 32 + blk;
+        v = ld16(vc + ((b * (C / 32) + kb) * a.n_kv + g) * (int64_t)(D * 32) + dd * 32 + 8 * ch);
+        if (key0 + 8 > hi) {       // zero the keys past the last query
+          const int valid = (int)(hi - key0);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t keep = (2 * w + 1 < valid) ? 0xFFFFFFFFu : (2 * w < valid ? 0x0000FFFFu : 0u);
+            v[w] &= keep;
+          }
+        }
+      }
+      vreg[i] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (D / 8), ch = c - row * (D / 8);
+      st16(&Ks[buf][row * KP + 8 * ch], kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int blk = c / (D * 4);
+      const int rem = c - blk * (D * 4);
+      const int dd = rem >> 2, ch = rem & 3;
+      st16(&Vs[buf][(blk * D + dd) * VP + 8 * ch], vreg[i]);
+    }
+  };
+
+  load_tile(t_first);
+  store_tile(0);
+  __syncthreads();
+
+  int buf = 0;
+  for (int64_t t = t_first; t <= t_last; ++t) {
+    const bool more = t < t_last;
+    if (more) load_tile(t + 1);
+    const int64_t k0 = t * kTile;
+
+    // ---- S^T = K Q^T over the tile: 4 M tiles of 16 keys
+    f32x4 S[4][NT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) S[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int krow = 32 * (mt >> 1) + 8 * (j >> 2) + 4 * (mt & 1) + (j & 3);
+        const u32x4 A = ld16(&Ks[buf][krow * KP + 32 * ks + 8 * g4]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[mt][n] = mfma16x16x32(A, qop[n][ks], S[mt][n]);
+      }
+    }
+    // lane (j, g4) now holds, for M tile mt and element r, the score of key
+    // k0 + 32*(mt>>1) + 8*g4 + 4*(mt&1) + r.
+    const bool need_mask = (k0 + kTile - 1 > P_min) ||
+                           (a.window > 0 && k0 < P_max - a.window + 1);
+    u32x4 Pk[2][NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (need_mask) {
+        const int64_t P = a.q_offset + tpos[n];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t key = k0 + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1) + r;
+            const bool ok = key <= P && (a.window <= 0 || key > P - a.window);
+            if (!ok) S[mt][n][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[mt][n][r]);
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      const float m_new = fmaxf(m_run[n], mx * scale);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[n] - m_use);
+      float ls = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(S[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
+          ls += p[e];
+        }
+        Pk[h][n] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      }
+      l_run[n] = l_run[n] * alpha + ls;
+      m_run[n] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
+    }
+    // ---- O^T += V^T P^T, two 32-key halves
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 A = ld16(&Vs[buf][(h * D + 16 * dt + j) * VP + 8 * g4]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[h][n], O[dt][n]);
+      }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // ---- normalise and store: lane holds O^T[16*dt + 4*g4 + r][query]
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float l = l_run[n];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    if (!rvalid[n]) continue;
+    uint16_t* orow = out + (((int64_t)b * a.T_q + tpos[n]) * a.n_q + head[n]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 o = O[dt][n] * inv;
+      u32x2 w = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+      *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * g4) = w;
+    }
+  }
+}
+
+template <int D, int NT>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  const int rows = kWaves * NT * 16;
+  const int BQ = rows / a.q_mult;
+  const int n_qb = (a.T_q + BQ - 1) / BQ;
+  const int64_t grid = (int64_t)n_qb * a.B * a.n_kv;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NT>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     a, BQ, n_qb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return launch_d<64, 2>(a, s);
+    case 96: return launch_d<96, 2>(a, s);
+    case 128: return launch_d<128, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}

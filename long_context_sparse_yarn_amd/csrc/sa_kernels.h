@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (sinkattn_abi.hip) and the
+// kernel translation units.  Every launcher enqueues on `s` and returns the
+// HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SA_MAX_HALF 128   // d_h <= 256
+
+struct RopeArgs {
+  void* x;
+  int64_t offset;
+  int BT, T, H, d;
+  double conc;
+  double inv_freq[SA_MAX_HALF];
+};
+hipError_t launch_rope(const RopeArgs& a, int elt_bytes, hipStream_t s);
+
+struct AppendArgs {
+  const void* k_src;
+  const void* v_src;
+  void* kc;
+  void* vc;
+  int B, T_new, n_kv, d;
+  int64_t C, o;
+};
+hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;        // [B, T_q, n_q, d]
+  const void* kc;       // [B, C, n_kv, d]
+  const void* vc;       // [B, C/32, n_kv, d, 32]
+  const float* sinks;   // [n_q]
+  void* out;            // [B, T_q, n_q, d]
+  int B, T_q, n_q, n_kv, d, q_mult, window;
+  int64_t C;            // capacity (rows)
+  int64_t q_offset;     // global position of query 0
+  float sm_scale;
+};
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_rows_f32(const AttnArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  AttnArgs at;          // T_q == 1, q_offset == cache offset - 1
+  float* ws;            // workspace (fp32)
+  int n_splits;
+};
+int decode_splits(int B, int n_kv, int64_t span_rows);
+int decode_max_splits(int B, int n_kv, int64_t capacity);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

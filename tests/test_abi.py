@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sinkattn.h declares, its host logic (YaRN table, KV byte count,
+snapshot bookkeeping) agrees with the oracle, and every argument error is
+reported before anything is enqueued (no call here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+sa = pytest.importorskip("long_context_sparse_yarn_amd",
+                         reason="libsinkattn.so not built (run __graft_entry__.build())")
+from long_context_sparse_yarn_amd import _binding as B  # noqa: E402
+from oracle.yarn import yarn_concentration, yarn_inv_freq  # noqa: E402
+
+SA_OK, SA_ERR_ARG, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_CAPACITY, SA_ERR_SNAPSHOT = 0, -1, -2, -3, -4, -5
+FAKE_K, FAKE_V = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)   # never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\**\s*([A-Za-z_]\w*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("yarn_rope_apply", "kv_cache_append", "kv_cache_snapshot", "kv_cache_restore",
+              "sinkattn_prefill", "sinkattn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("d,base,s,L,a,b", [(64, 150000.0, 32.0, 4096, 1.0, 32.0),
+                                            (96, 150000.0, 32.0, 4096, 1.0, 32.0),
+                                            (64, 10000.0, 1.0, 4096, 1.0, 32.0),
+                                            (128, 500000.0, 8.0, 8192, 2.0, 16.0)])
+def test_host_yarn_table_matches_oracle(d, base, s, L, a, b):
+    inv, c = sa.yarn_inv_freq(sa.Yarn(d, base, s, L, a, b))
+    np.testing.assert_allclose(inv, yarn_inv_freq(d, base, s, L, a, b), rtol=4e-16, atol=0)
+    assert c == pytest.approx(yarn_concentration(s), rel=1e-15)
+
+
+def test_yarn_bad_parameters():
+    with pytest.raises(sa.SinkAttnError):
+        sa.yarn_inv_freq(sa.Yarn(64, 150000.0, 0.5))
+    with pytest.raises(sa.SinkAttnError):
+        sa.yarn_inv_freq(sa.Yarn(64, ntk_alpha=32.0, ntk_beta=1.0))
+
+
+def test_kv_cache_bytes():
+    assert sa.kv_cache_bytes(24, 1, 131072, 8, 64, 2) == 6442450944   # the printed 6.0 GiB
+    assert sa.kv_cache_bytes(1, 8, 131136, 8, 64, 2) == 2 * 8 * 131136 * 8 * 64 * 2
+    assert sa.kv_cache_bytes(1 << 40, 1 << 40, 2, 2, 2, 2) == -1
+    assert sa.kv_cache_bytes(-1, 1, 1, 1, 1, 1) == -1
+
+
+def create(dtype=0, Bn=2, C=256, n_kv=2, d=64, offset=0):
+    h = ctypes.c_void_p()
+    st = B._kv_cache_create(ctypes.byref(h), FAKE_K, FAKE_V, dtype, Bn, C, n_kv, d, offset)
+    return st, h
+
+
+def test_cache_create_validation():
+    assert create(C=100)[0] == SA_ERR_SHAPE          # not a multiple of 32
+    assert create(C=0)[0] == SA_ERR_SHAPE
+    assert create(dtype=7)[0] == SA_ERR_DTYPE
+    assert create(d=60)[0] == SA_ERR_SHAPE
+    assert create(offset=300)[0] == SA_ERR_CAPACITY
+    h = ctypes.c_void_p()
+    assert B._kv_cache_create(ctypes.byref(h), None, FAKE_V, 0, 2, 256, 2, 64, 0) == SA_ERR_ARG
+    assert "null" in sa.last_error()
+    st, h = create(offset=40)
+    assert st == SA_OK and B._kv_cache_offset(h) == 40
+    assert B._kv_cache_offset(None) == -1
+    assert B._kv_cache_destroy(h) == SA_OK
+
+
+def test_errors_are_reported_before_any_launch():
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    assert st == SA_OK
+    q, o, s = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000)
+    # append past capacity
+    assert B._kv_cache_append(h, q, q, 247, None) == SA_ERR_CAPACITY
+    assert B._kv_cache_append(h, q, q, 0, None) == SA_ERR_ARG
+    assert B._kv_cache_offset(h) == 10                                    # unchanged
+    # prefill: queries past the rows in the cache; GQA contract; head dim
+    P = B._sinkattn_prefill
+    assert P(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 6, None) == SA_ERR_CAPACITY
+    assert P(q, h, s, o, 2, 5, 7, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE
+    assert P(q, h, s, o, 2, 5, 8, 4, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE   # n_kv != cache
+    assert P(q, h, s, o, 3, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE   # B != cache
+    assert P(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.0, 0, None) == SA_ERR_ARG
+    assert P(None, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_ARG
+    assert P(q, h, s, o, 2, 0, 8, 2, 64, 0, 0.125, 0, None) == SA_OK          # nothing to do
+    # decode: q_mult > 16 on bf16, workspace too small
+    D = B._sinkattn_decode
+    assert D(q, h, s, o, 2, 64, 2, 64, 0, 0.125, o, 1 << 30, None) == SA_ERR_SHAPE
+    need = B._sinkattn_decode_ws(2, 8, 2, 64, 256)
+    assert need > 0
+    assert D(q, h, s, o, 2, 8, 2, 64, 0, 0.125, o, need - 4, None) == SA_ERR_ARG
+    assert D(q, h, s, o, 2, 8, 2, 64, 0, 0.125, None, need, None) == SA_ERR_ARG
+    B._kv_cache_destroy(h)
+    # bf16 attention head dims
+    st, h80 = create(d=80, offset=10)
+    assert st == SA_OK
+    assert P(q, h80, s, o, 2, 5, 8, 2, 80, 0, 0.125, 0, None) == SA_ERR_SHAPE
+    B._kv_cache_destroy(h80)
+    # rope
+    y = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
+    R = B._yarn_rope_apply
+    assert R(q, 9, 1, 4, 8, 64, 0, ctypes.byref(y), None) == SA_ERR_DTYPE
+    assert R(q, 0, 1, 4, 8, 60, 0, ctypes.byref(y), None) == SA_ERR_SHAPE
+    assert R(q, 0, 1, 4, 8, 96, 0, ctypes.byref(y), None) == SA_ERR_SHAPE   # yarn d_h 64
+    assert R(q, 0, 1, 4, 8, 64, -1, ctypes.byref(y), None) == SA_ERR_ARG
+    assert R(q, 0, 1, 0, 8, 64, 0, ctypes.byref(y), None) == SA_OK          # T = 0
+
+
+def test_snapshot_bookkeeping_without_appends():
+    st, h = create(offset=64)
+    st2, other = create(offset=64)
+    snap = B.SaSnapshot()
+    assert B._kv_cache_snapshot(h, ctypes.byref(snap)) == SA_OK
+    assert snap.offset == 64
+    assert B._kv_cache_restore(other, ctypes.byref(snap)) == SA_ERR_SNAPSHOT   # foreign
+    assert B._kv_cache_restore(h, ctypes.byref(snap)) == SA_OK
+    bad = B.SaSnapshot(64, snap.cache_id, snap.stamp + 5)                      # from the future
+    assert B._kv_cache_restore(h, ctypes.byref(bad)) == SA_ERR_SNAPSHOT
+    B._kv_cache_destroy(h)
+    B._kv_cache_destroy(other)
+
+
+def test_decode_workspace_size_bound():
+    # grows with capacity until the split cap, never zero for valid shapes
+    a = B._sinkattn_decode_ws(8, 64, 8, 64, 131136)
+    b = B._sinkattn_decode_ws(8, 64, 8, 64, 256)
+    assert a >= b > 0
+    assert B._sinkattn_decode_ws(8, 63, 8, 64, 256) == 0
