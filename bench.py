@@ -1,0 +1,295 @@
+"""Throughput of the sink-GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extra] [--no-cpu]
+
+One step = the whole hot path over one batch of the GPT-OSS-Lite-shaped
+prefill (B=4, T=4096, n_q=8, n_kv=4, d_h=96, bf16, YaRN s=32 base 1.5e5):
+for each of its two layer kinds (128-token band, full causal) a fresh copy
+of the raw Q and K, RoPE on Q and K at offset 0, the cache rewound to 0 and
+K/V appended, and sink attention over the chunk.  Inputs are resident in HBM
+before timing starts.  The value is algorithmic attention TFLOP/s of the
+step (4*d*n_q*B*sum_p|A(p)| flops: allowed query/key pairs only).
+
+Extra objects on the same JSON line:
+  roofline      the full-causal prefill kernel (the step's dominant kernel),
+                timed with HIP events on its stream, against dense bf16 MFMA
+  cpu_baseline  the fp64 oracle on a bounded sample of the same step
+  extra         gpt-oss-shaped prefill (B1 T8192 64/8 d64) and long-context
+                decode (B8, 131072 cached rows, 64/8 d64) per-kernel figures
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def pairs_allowed(q_offset, T, window):
+    p = q_offset + np.arange(T, dtype=np.int64)
+    n = p + 1
+    if window > 0:
+        n = np.minimum(n, window)
+    return int(n.sum())
+
+
+def attn_flops(B, n_q, d, q_offset, T, window):
+    return 4.0 * d * n_q * B * pairs_allowed(q_offset, T, window)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Layer:
+    """Device state of one layer of a prefill workload."""
+
+    def __init__(self, w, layer, sa, torch):
+        import workloads as wl
+        x = wl.prefill_inputs(w, layer)
+        dt = torch.bfloat16
+        up = lambda a: torch.from_numpy(a).cuda().to(dt)
+        self.host = x
+        self.window = w.windows[layer]
+        self.q0, self.k0, self.v = up(x["q"]), up(x["k"]), up(x["v"])
+        self.qw, self.kw = torch.empty_like(self.q0), torch.empty_like(self.k0)
+        self.sinks = torch.from_numpy(x["sinks"]).cuda()
+        self.cache = sa.KVCache.empty(w.B, w.capacity, w.n_kv, w.d_h, dtype=dt)
+        if w.prefix:
+            self.cache.append(up(x["prefix_k"]), up(x["prefix_v"]))
+        self.snap = self.cache.snapshot()
+        self.out = torch.empty_like(self.q0)
+        self.yarn = sa.Yarn(w.d_h, w.yarn.base, w.yarn.factor, w.yarn.orig_ctx, w.yarn.alpha,
+                            w.yarn.beta)
+
+
+def run_layer(L, w, sa, ev=None):
+    L.qw.copy_(L.q0)
+    L.kw.copy_(L.k0)
+    L.cache.restore(L.snap)
+    o = L.cache.offset
+    sa.yarn_rope_apply(L.qw, o, L.yarn)
+    sa.yarn_rope_apply(L.kw, o, L.yarn)
+    L.cache.append(L.kw, L.v)
+    if ev is not None:
+        ev[0].record()
+    sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, o, out=L.out)
+    if ev is not None:
+        ev[1].record()
+
+
+def time_prefill_step(w, sa, torch, steps, warmup):
+    layers = [Layer(w, i, sa, torch) for i in range(len(w.windows))]
+    for _ in range(warmup):
+        for L in layers:
+            run_layer(L, w, sa)
+    torch.cuda.synchronize()
+    evs = {i: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] for i in range(len(layers))}
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, L in enumerate(layers):
+            run_layer(L, w, sa, evs[i][s])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    kern_ms = {i: float(np.mean([a.elapsed_time(b) for a, b in evs[i]])) for i in evs}
+    return layers, ms_step, kern_ms
+
+
+def prefill_figures(w, L, ms):
+    fl = attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window)
+    elt = 2
+    # algorithmic bytes: Q read + O written + each allowed K/V row read once
+    lo = max(0, w.prefix - L.window + 1) if L.window > 0 else 0
+    rows = (w.prefix + w.T) - lo
+    by = (2 * w.B * w.T * w.n_q * w.d_h + 2 * w.B * rows * w.n_kv * w.d_h) * elt
+    tf = fl / (ms * 1e-3) / 1e12
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"window": L.window, "kernel_ms": round(ms, 4), "gflop": round(fl / 1e9, 3),
+            "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
+            "alg_mb": round(by / 1e6, 2), "gbs": round(gbs, 1),
+            "frac_bound": round(tf / min(PEAK_BF16_TFLOPS, fl / by * PEAK_HBM_GBS / 1e3), 4)}
+
+
+def decode_extra(sa, torch, steps_warm=4):
+    import workloads as wl
+    w = wl.LONG_DECODE
+    dt = torch.bfloat16
+    up = lambda a: torch.from_numpy(a).cuda().to(dt)
+    res = {}
+    pre = wl.prefix_inputs(w, 0)
+    pk, pv = up(pre["prefix_k"]), up(pre["prefix_v"])
+    del pre
+    y = sa.Yarn(w.d_h, w.yarn.base, w.yarn.factor, w.yarn.orig_ctx, w.yarn.alpha, w.yarn.beta)
+    for layer, W in enumerate(w.windows):
+        cache = sa.KVCache.empty(w.B, w.capacity, w.n_kv, w.d_h, dtype=dt)
+        cache.append(pk, pv)             # the band layer reuses the full layer's prefix draw
+        sinks = torch.from_numpy(wl.sinks(w, layer)).cuda()
+        toks = [wl.decode_token(w, layer, s) for s in range(w.decode_steps)]
+        toks = [{k: up(v) for k, v in t.items()} for t in toks]
+        ws = sa.decode_workspace(cache, w.n_q)
+        snap = cache.snapshot()
+        qbuf = torch.empty_like(toks[0]["q"])
+        kbuf = torch.empty_like(toks[0]["k"])
+        out = torch.empty_like(qbuf)
+
+        def step(s, ev=None):
+            qbuf.copy_(toks[s]["q"])
+            kbuf.copy_(toks[s]["k"])
+            o = cache.offset
+            sa.yarn_rope_apply(qbuf, o, y)
+            sa.yarn_rope_apply(kbuf, o, y)
+            cache.append(kbuf, toks[s]["v"])
+            if ev is not None:
+                ev[0].record()
+            sa.sinkattn_decode(qbuf, cache, sinks, W, w.sm_scale, workspace=ws, out=out)
+            if ev is not None:
+                ev[1].record()
+
+        for s in range(steps_warm):
+            step(s)
+        cache.restore(snap)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(w.decode_steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for s in range(w.decode_steps):
+            step(s, evs[s])
+        t1.record()
+        torch.cuda.synchronize()
+        kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        step_ms = t0.elapsed_time(t1) / w.decode_steps
+        rows = [min(w.prefix + s + 1, W) if W > 0 else w.prefix + s + 1
+                for s in range(w.decode_steps)]
+        by = np.mean([(r * w.n_kv * w.d_h * 2 * 2 + 2 * w.n_q * w.d_h * 2) * w.B for r in rows])
+        gbs = by / (kms * 1e-3) / 1e9
+        res["full" if W == 0 else "band%d" % W] = {
+            "attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+            "alg_mb_per_step": round(by / 1e6, 3), "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del cache, ws, toks
+        torch.cuda.empty_cache()
+    return {"workload": w.name, **res}
+
+
+def cpu_baseline(w, layers, budget_s):
+    """The oracle as it stands on a bounded sample of the timed step:
+    RoPE of all of Q and K (fp64) and attention for a seeded sample of query
+    rows per layer, scaled to the whole step by algorithmic flops."""
+    from threadpoolctl import threadpool_info
+    from oracle.attention import attend_query
+    from oracle.rounding import round_to
+    from oracle.yarn import rope_apply, yarn_concentration, yarn_inv_freq
+
+    y = w.yarn
+    inv = yarn_inv_freq(w.d_h, y.base, y.factor, y.orig_ctx, y.alpha, y.beta)
+    c = yarn_concentration(y.factor)
+    rng = np.random.default_rng(0)
+    t_rope = 0.0
+    t_attn = 0.0
+    fl_sample = 0.0
+    fl_total = 0.0
+    n_rows = 0
+    checks = []
+    per_layer = budget_s / len(layers)
+    for L in layers:
+        x = L.host
+        t = time.perf_counter()
+        q_rot = round_to(rope_apply(x["q"].astype(np.float64), 0, inv, c), "bf16")
+        k_rot = round_to(rope_apply(x["k"].astype(np.float64), 0, inv, c), "bf16")
+        t_rope += time.perf_counter() - t
+        V = x["v"]
+        fl_total += attn_flops(w.B, w.n_q, w.d_h, 0, w.T, L.window)
+        out_gpu = L.out.float().cpu().numpy()
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < per_layer:
+            b = int(rng.integers(w.B))
+            tq = int(rng.integers(w.T))
+            t = time.perf_counter()
+            o = attend_query(q_rot[b, tq], k_rot[b], V[b], x["sinks"], tq, L.window, w.sm_scale)
+            t_attn += time.perf_counter() - t
+            n = min(tq + 1, L.window) if L.window > 0 else tq + 1
+            fl_sample += 4.0 * w.d_h * w.n_q * n
+            n_rows += 1
+            checks.append(float(np.max(np.abs(o - out_gpu[b, tq]))))
+    est = t_rope + t_attn * (fl_total / fl_sample)
+    info = threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    return {"value": round(fl_total / est / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "fp64 numpy oracle: RoPE of all Q and K of both layers (%.2f s) plus "
+                      "attention of %d seeded random query rows (all heads, %.2f s, %.3g of the "
+                      "step's flops); whole-step time extrapolated by flops" % (
+                          t_rope, n_rows, t_attn, fl_sample / fl_total),
+            "est_step_s": round(est, 2),
+            "parity_sample_max_abs": round(max(checks), 5) if checks else None}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import long_context_sparse_yarn_amd as sa
+
+    torch.cuda.set_device(0)
+    w = wl.LITE_PREFILL
+    layers, ms_step, kern_ms = time_prefill_step(w, sa, torch, args.steps, args.warmup)
+    fl_step = sum(attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window) for L in layers)
+    value = fl_step / (ms_step * 1e-3) / 1e12
+    per_layer = [prefill_figures(w, L, kern_ms[i]) for i, L in enumerate(layers)]
+    full = [p for p in per_layer if p["window"] == 0][0]
+    full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
+    roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": full["frac_mfma"], "traffic": None,
+                "kernel": "prefill_bf16_kernel<96,2> (full causal)",
+                "kernel_ms": round(kern_ms[full_i], 4)}
+    line = {
+        "metric": "sink-GQA attention prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": w.B, "seq_len": w.T, "n_q": w.n_q,
+                   "n_kv": w.n_kv, "d_h": w.d_h, "windows": list(w.windows),
+                   "yarn": {"base": w.yarn.base, "factor": w.yarn.factor,
+                            "orig_ctx": w.yarn.orig_ctx}, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "layers": per_layer,
+    }
+    if not args.no_extra:
+        g = wl.GPTOSS_PREFILL
+        gl, gms, gk = time_prefill_step(g, sa, torch, 10, 3)
+        line["extra"] = {"gpt_oss_prefill": {"workload": g.name, "ms_per_step": round(gms, 4),
+                                             "layers": [prefill_figures(g, L, gk[i])
+                                                        for i, L in enumerate(gl)]}}
+        del gl
+        torch.cuda.empty_cache()
+        line["extra"]["long_decode"] = decode_extra(sa, torch)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, layers, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
