@@ -15,8 +15,11 @@
 //    load serves all heads of the group.  K operands load straight from HBM
 //    in the row layout; V^T operands load straight from the blocked V
 //    layout (8 consecutive keys of one coordinate = one 16-byte load); no
-//    LDS round trip.  The next block's loads are issued before the current
-//    block is multiplied.
+//    LDS round trip.  A wave works on 64 keys at a time while the loads of
+//    the next 64 keys are in flight.
+//  * Lazy running max, as in prefill: the cross-lane max and the rescale of
+//    the accumulators happen only when a score passes the running max by
+//    more than 2^8.
 //  * Each wave writes a partial (m, l, acc) in base-2 units to the
 //    workspace; a merge kernel folds the partials of a head in a fixed order
 //    and adds the sink exactly once:
@@ -32,6 +35,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTargetWaves = 4096;
 constexpr int kMaxSplits = 256;
+constexpr float kSlack = 8.0f;
 
 template <int D>
 struct BlockOps {
@@ -103,66 +107,94 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   const uint16_t* vpair = vc + ((int64_t)b * (C / 32) * a.n_kv + g) * (int64_t)(D * 32);
   const int64_t vbstride = (int64_t)a.n_kv * D * 32;                      // per 32-key block
 
-  BlockOps<D> cur, nxt;
-  if (b0 < b1) load_block<D>(cur, kpair + b0 * 32 * kstride, vpair + b0 * vbstride, kstride, j, g4);
-  for (int64_t kb = b0; kb < b1; ++kb) {
-    if (kb + 1 < b1)
-      load_block<D>(nxt, kpair + (kb + 1) * 32 * kstride, vpair + (kb + 1) * vbstride, kstride, j, g4);
-    const int64_t k0 = kb * 32;
-    const bool partial = (k0 < lo) || (k0 + 32 > hi);
-    if (k0 + 32 > hi) {    // zero V of keys past the query (unwritten rows)
-      const int valid = (int)(hi - (k0 + 8 * g4));
+  BlockOps<D> cur[2], nxt[2];
+  auto load2 = [&](BlockOps<D>(&ops)[2], int64_t kb) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int u = 0; u < 2; ++u)
+      if (kb + u < b1)
+        load_block<D>(ops[u], kpair + (kb + u) * 32 * kstride, vpair + (kb + u) * vbstride,
+                      kstride, j, g4);
+  };
+  if (b0 < b1) load2(cur, b0);
+  for (int64_t kb = b0; kb < b1; kb += 2) {
+    if (kb + 2 < b1) load2(nxt, kb + 2);
+    const bool two = kb + 1 < b1;
+    f32x4 Sc[2][2];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t keep = (2 * w + 1 < valid) ? 0xFFFFFFFFu : (2 * w < valid ? 0x0000FFFFu : 0u);
-          cur.v[dt][w] &= keep;
-        }
+    for (int u = 0; u < 2; ++u) {
+      Sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u == 1 && !two) break;
+      const int64_t k0 = (kb + u) * 32;
+      if (k0 + 32 > hi) {    // zero V of keys past the query (unwritten rows)
+        const int valid = (int)(hi - (k0 + 8 * g4));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t keep = (2 * w + 1 < valid) ? 0xFFFFFFFFu : (2 * w < valid ? 0x0000FFFFu : 0u);
+            cur[u].v[dt][w] &= keep;
+          }
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) Sc[u][mt] = mfma16x16x32(cur[u].k[mt][ks], qop[ks], Sc[u][mt]);
+      // lane (j, g4), element (mt, r): key k0 + 8*g4 + 4*mt + r
+      if (k0 < lo || k0 + 32 > hi) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t key = k0 + 8 * g4 + 4 * mt + r;
+            if (key < lo || key >= hi) Sc[u][mt][r] = -INFINITY;
+          }
+      }
     }
-    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) S[mt] = mfma16x16x32(cur.k[mt][ks], qop[ks], S[mt]);
-    // lane (j, g4), element (mt, r): key k0 + 8*g4 + 4*mt + r
-    if (partial) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = k0 + 8 * g4 + 4 * mt + r;
-          if (key < lo || key >= hi) S[mt][r] = -INFINITY;
-        }
+    if (!two) {
+      Sc[1][0] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      Sc[1][1] = Sc[1][0];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[mt][r]);
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx * scale);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float p[8], ls = 0.f;
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(fmaf(S[e >> 2][e & 3], scale, -m_use));
-      ls += p[e];
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, Sc[u][mt][r]);
+    if (__builtin_amdgcn_ballot_w64(mx * scale > m_run + kSlack) != 0) {
+      const float m_new = fmaxf(m_run, max_over_col(mx) * scale);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+      m_run = m_new;
     }
-    const u32x4 Pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] = mfma16x16x32(cur.v[dt], Pk, O[dt] * alpha);
-    if (kb + 1 < b1) cur = nxt;
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e = 2 * e2;
+        const float p0 = fast_exp2(fmaf(Sc[u][e >> 2][e & 3], scale, -m_use));
+        const float p1 = fast_exp2(fmaf(Sc[u][(e + 1) >> 2][(e + 1) & 3], scale, -m_use));
+        w[e2] = pack_bf16x2(p0, p1);
+        l_run = sum_bf16x2(w[e2], l_run);
+      }
+      const u32x4 Pk = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] = mfma16x16x32(cur[u].v[dt], Pk, O[dt]);
+    }
+    if (kb + 2 < b1) {
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
+    }
   }
 
   // ---- partial of this split: lanes (j < q_mult)
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = sum_over_col(l_run);
   if (j < a.q_mult) {
     const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + j;
     float* acc = da.ws + slot * D;
@@ -177,9 +209,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   }
 }
 
-// One wave per (b, h): fold the partials of its splits in split order.
+// One wave per (b, h).  Lanes read the splits' (m, l) in parallel; the
+// weighted sum over splits runs in split order for every coordinate.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs da) {
+  __shared__ float wsh[kMaxSplits];
   const AttnArgs& a = da.at;
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;
@@ -190,25 +224,33 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs da) {
   const int pair = b * a.n_kv + g;
   const float* ml = da.ws + (int64_t)pairs * S * a.q_mult * D;
   const float sg = a.sinks[h] * SA_LOG2E;
+  auto slot = [&](int s) { return ((int64_t)pair * S + s) * a.q_mult + jq; };
 
-  float M = sg;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * (((int64_t)pair * S + s) * a.q_mult + jq)]);
-  float L = (sg == -INFINITY) ? 0.f : fast_exp2(sg - M);
+  float mloc = -INFINITY;
+  for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, ml[2 * slot(s)]);
+  const float M = fmaxf(sg, wave_max(mloc));
+  float lsum = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float m = ml[2 * slot(s)];
+    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+    wsh[s] = w;
+    lsum += ml[2 * slot(s) + 1] * w;
+  }
+  const float L = wave_sum(lsum) + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
+  __syncthreads();
   constexpr int PER = (D + 63) / 64;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  const float* base = da.ws + slot(0) * D;
+  const int64_t sstride = (int64_t)a.q_mult * D;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const int64_t slot = ((int64_t)pair * S + s) * a.q_mult + jq;
-    const float m = ml[2 * slot];
-    if (m == -INFINITY) continue;
-    const float w = fast_exp2(m - M);
-    L += ml[2 * slot + 1] * w;
-    const float* src = da.ws + slot * D;
+    const float w = wsh[s];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int dd = lane + 64 * i;
-      if (dd < D) acc[i] += src[dd] * w;
+      if (dd < D) acc[i] = fmaf(base[s * sstride + dd], w, acc[i]);
     }
   }
   const float inv = 1.0f / L;

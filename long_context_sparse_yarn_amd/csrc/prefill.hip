@@ -21,9 +21,15 @@
 //    blocked V cache layout (32 keys contiguous per coordinate).
 //  * Online softmax in base 2 (log2 e folded into the scale and the sink),
 //    seeded with the sink: m = sigma*log2e, l = 1 (sigma = -inf: m = -inf,
-//    l = 0).  Masks are computed from positions, only on tiles that cross
-//    the diagonal or the band edge; rows at or past the last query position
-//    are zero-filled in LDS, so unwritten cache rows are never read.
+//    l = 0).  The running max is lazy: it moves (with a cross-lane max and a
+//    rescale of O and l) only when some score exceeds it by more than 2^8,
+//    so most tiles need no cross-lane traffic and no accumulator rescale;
+//    the exponentials stay below 2^8 either way.  Probabilities are rounded
+//    to bf16 once (v_cvt_pk_bf16_f32) and the row sums accumulate those same
+//    rounded values (v_dot2c_f32_bf16), so numerator and denominator agree.
+//  * Masks are computed from positions, only on tiles that cross the
+//    diagonal or the band edge; rows past the last query position are
+//    zero-filled in LDS, so unwritten cache rows are never read.
 //  * K/V tiles are double-buffered: the next tile's global loads are in
 //    flight while the current tile is multiplied.
 //  * Workgroups of the same (b, g) are spread so that, when B*n_kv is a
@@ -37,6 +43,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 64;  // keys per tile
+constexpr float kSlack = 8.0f;  // log2 headroom of the lazy running max
 
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
@@ -188,13 +195,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (need_mask) {
-        const int64_t P = a.q_offset + tpos[n];
+        const int rel0 = (int)(k0 - (a.q_offset + tpos[n]));   // key - p at (mt, r) = 0
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t key = k0 + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1) + r;
-            const bool ok = key <= P && (a.window <= 0 || key > P - a.window);
+            const int rel = rel0 + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1) + r;
+            const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
             if (!ok) S[mt][n][r] = -INFINITY;
           }
       }
@@ -203,27 +210,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[mt][n][r]);
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[n], mx * scale);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[n] - m_use);
-      float ls = 0.f;
+      // Lazy max: keep the running reference while no score passes it by
+      // more than 2^kSlack; only then (wave-uniform branch) take the column
+      // max across lanes and rescale the partial sums.
+      if (__builtin_amdgcn_ballot_w64(mx * scale > m_run[n] + kSlack) != 0) {
+        const float m_new = fmaxf(m_run[n], max_over_col(mx) * scale);
+        // m_run == -inf: nothing accumulated yet (and m_new may be -inf too)
+        const float alpha = (m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
+        l_run[n] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
+        m_run[n] = m_new;
+      }
+      const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
+      float ls = l_run[n];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        float p[8];
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(S[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
-          ls += p[e];
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e = 2 * e2;
+          const float p0 = fast_exp2(fmaf(S[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
+          const float p1 = fast_exp2(fmaf(S[2 * h + ((e + 1) >> 2)][n][(e + 1) & 3], scale, -m_use));
+          w[e2] = pack_bf16x2(p0, p1);
+          ls = sum_bf16x2(w[e2], ls);
         }
-        Pk[h][n] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        Pk[h][n] = u32x4{w[0], w[1], w[2], w[3]};
       }
-      l_run[n] = l_run[n] * alpha + ls;
-      m_run[n] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
+      l_run[n] = ls;
     }
     // ---- O^T += V^T P^T, two 32-key halves
 #pragma unroll
@@ -244,10 +258,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    float l = l_run[n];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / sum_over_col(l_run[n]);
     if (!rvalid[n]) continue;
     uint16_t* orow = out + (((int64_t)b * a.T_q + tpos[n]) * a.n_q + head[n]) * D;
 #pragma unroll
