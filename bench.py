@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized buffer 3 times (reference dispatch for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -254,6 +257,15 @@ def main():
     import long_context_sparse_yarn_amd as sa
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}))
+        return
     w = wl.LITE_PREFILL
     layers, ms_step, kern_ms = time_prefill_step(w, sa, torch, args.steps, args.warmup)
     fl_step = sum(attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window) for L in layers)
@@ -263,7 +275,7 @@ def main():
     full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
     roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": full["frac_mfma"], "traffic": None,
-                "kernel": "prefill_bf16_kernel<96,2> (full causal)",
+                "kernel": "prefill_bf16_kernel<96,2,8> (full causal)",
                 "kernel_ms": round(kern_ms[full_i], 4)}
     line = {
         "metric": "sink-GQA attention prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",

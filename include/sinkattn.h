@@ -30,6 +30,9 @@
  *     fp32 (SA_F32); one call uses one type for all of its activations and
  *     cache rows.  Sinks are always fp32.
  *   - Sizes are element counts unless a name ends in _bytes.
+ *   - Every device pointer (activations, cache buffers, workspace) must be
+ *     16-byte aligned (SA_ERR_ARG otherwise): the kernels move 16-byte
+ *     vectors.
  *
  * Cache memory layout (per layer; C = capacity rows, a multiple of 32):
  *   K: [B, C, n_kv, d_h]                     -- the pages' [B, T_cache, H_kv, d]

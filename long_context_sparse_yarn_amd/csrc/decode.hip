@@ -209,13 +209,33 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   }
 }
 
-// One wave per (b, h).  Lanes read the splits' (m, l) in parallel; the
-// weighted sum over splits runs in split order for every coordinate.
+// One workgroup per (b, h).  Thread s < S takes split s's (m, l); the
+// weighted sum of the accumulators runs with the splits dealt round-robin to
+// thread groups (16-byte loads), then the groups are added in group order.
+// Every sum has a fixed order, so the result is deterministic.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs da) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs da) {
+  constexpr int CPS = D / 4;                        // f32x4 vectors per split
+  constexpr int G = kMergeThreads / CPS;            // split groups
   __shared__ float wsh[kMaxSplits];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4 part[G][CPS];
   const AttnArgs& a = da.at;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.n_q, h = bh - b * a.n_q;
   const int g = h / a.q_mult, jq = h - g * a.q_mult;
@@ -224,41 +244,32 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs da) {
   const int pair = b * a.n_kv + g;
   const float* ml = da.ws + (int64_t)pairs * S * a.q_mult * D;
   const float sg = a.sinks[h] * SA_LOG2E;
-  auto slot = [&](int s) { return ((int64_t)pair * S + s) * a.q_mult + jq; };
+  const int64_t slot0 = ((int64_t)pair * S) * a.q_mult + jq;   // slot of split 0
+  const int64_t sstride = a.q_mult;                            // slots between splits
 
-  float mloc = -INFINITY;
-  for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, ml[2 * slot(s)]);
-  const float M = fmaxf(sg, wave_max(mloc));
-  float lsum = 0.f;
-  for (int s = lane; s < S; s += 64) {
-    const float m = ml[2 * slot(s)];
-    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-    wsh[s] = w;
-    lsum += ml[2 * slot(s) + 1] * w;
+  const float m = tid < S ? ml[2 * (slot0 + tid * sstride)] : -INFINITY;
+  const float M = fmaxf(sg, block_reduce(m, red, true));
+  const float w = (tid < S && m != -INFINITY) ? fast_exp2(m - M) : 0.f;
+  if (tid < S) wsh[tid] = w;
+  const float lpart = tid < S ? ml[2 * (slot0 + tid * sstride) + 1] * w : 0.f;
+  const float L = block_reduce(lpart, red, false) + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
+
+  const int grp = tid / CPS, c = tid - grp * CPS;
+  if (grp < G) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* src = da.ws + slot0 * D + 4 * c;
+    for (int s = grp; s < S; s += G)
+      acc += *reinterpret_cast<const f32x4*>(src + s * sstride * D) * wsh[s];
+    part[grp][c] = acc;
   }
-  const float L = wave_sum(lsum) + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
   __syncthreads();
-  constexpr int PER = (D + 63) / 64;
-  float acc[PER];
+  if (tid < CPS) {
+    f32x4 o = part[0][tid];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  const float* base = da.ws + slot(0) * D;
-  const int64_t sstride = (int64_t)a.q_mult * D;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float w = wsh[s];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int dd = lane + 64 * i;
-      if (dd < D) acc[i] = fmaf(base[s * sstride + dd], w, acc[i]);
-    }
-  }
-  const float inv = 1.0f / L;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int dd = lane + 64 * i;
-    if (dd < D) out[dd] = (uint16_t)f32_to_bf16_bits(acc[i] * inv);
+    for (int i = 1; i < G; ++i) o += part[i][tid];
+    o *= 1.0f / L;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D + 4 * tid;
+    *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
   }
 }
 
@@ -269,7 +280,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -38,25 +38,37 @@
 #include "sa_device.h"
 #include "sa_kernels.h"
 
+#include <type_traits>
+
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 64;  // keys per tile
 constexpr float kSlack = 8.0f;  // log2 headroom of the lazy running max
 
-template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
+// LDS placement of K row r, 16-byte chunk k (in elements).  The operand
+// reads take rows 32h + 8q + 4t + r' (q, r' < 4) across 16 lanes; a padded
+// pitch (D + 8) and shifts of 4, 8 and 11 sixteen-byte slots for rows with
+// bit 3, 4 and 5 set put every such read on distinct banks, whether the LDS
+// serves 16-byte reads 8 lanes (128 B) or 16 lanes (256 B) at a time, and no
+// two rows overlap.
+template <int D>
+__device__ __forceinline__ int k_lds(int r, int k) {
+  return r * (D + 8) + 8 * k + 32 * ((r >> 3) & 1) + 64 * ((r >> 4) & 1) + 88 * (r >> 5);
+}
+
+template <int D, int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
+  constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
   constexpr int DT = D / 16;          // coordinate tiles of O^T
-  constexpr int KP = D + 8;           // LDS row pitch of K (elements)
   constexpr int VP = 32 + 8;          // LDS row pitch of V^T (elements)
-  constexpr int KCH = kTile * D / 8 / kThreads;   // 16-byte K chunks per thread
-  constexpr int VCH = 2 * D * 4 / kThreads;       // 16-byte V chunks per thread
-  static_assert(KCH * kThreads * 8 == kTile * D, "K tile split");
-  static_assert(VCH * kThreads == 2 * D * 4, "V tile split");
+  constexpr int KTOT = kTile * D / 8; // 16-byte K chunks per tile
+  constexpr int VTOT = 2 * D * 4;     // 16-byte V chunks per tile
+  constexpr int KCH = (KTOT + kThreads - 1) / kThreads;   // per thread
+  constexpr int VCH = (VTOT + kThreads - 1) / kThreads;
+  constexpr int KBUF = kTile * (D + 8) + 184;   // last row's shift: 32 + 64 + 88
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTile * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * D * VP];
 
   const int lane = threadIdx.x & 63;
@@ -74,8 +86,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
   const int64_t C = a.C;
 
   const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc);
 
   // ---- this lane's query rows (one per 16-wide N tile)
   int tpos[NT], head[NT];
@@ -110,28 +120,55 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
   const int64_t hi = P_max + 1;   // keys >= hi are masked for every row here
   const int64_t t_first = lo / kTile, t_last = (hi - 1) / kTile;
 
+  // ---- per-thread load slots: K chunk (row, ch) and V chunk (blk, dd, ch)
+  const int64_t krow_stride = (int64_t)a.n_kv * D;                  // elements per cache row
+  const int64_t vblk_stride = (int64_t)a.n_kv * D * 32;             // elements per 32-key block
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.kc) + ((int64_t)b * C * a.n_kv + g) * D;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.vc) +
+                          ((int64_t)b * (C / 32) * a.n_kv + g) * (int64_t)(D * 32);
+  int k_row[KCH], k_off[KCH], k_lds_off[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int c = min((int)threadIdx.x + i * kThreads, KTOT - 1);   // excess slots repeat the last
+    k_row[i] = c / (D / 8);
+    const int ch = c - k_row[i] * (D / 8);
+    k_off[i] = 8 * ch;
+    k_lds_off[i] = k_lds<D>(k_row[i], ch);
+  }
+  int v_key[VCH], v_off[VCH], v_lds_off[VCH];
+#pragma unroll
+  for (int i = 0; i < VCH; ++i) {
+    const int c = min((int)threadIdx.x + i * kThreads, VTOT - 1);
+    const int blk = c / (D * 4);
+    const int rem = c - blk * (D * 4);
+    const int dd = rem >> 2, ch = rem & 3;
+    v_key[i] = 32 * blk + 8 * ch;                                  // first key of the chunk
+    v_off[i] = (int)(blk * vblk_stride) + dd * 32 + 8 * ch;
+    v_lds_off[i] = (blk * D + dd) * VP + 8 * ch;
+  }
+
   u32x4 kreg[KCH], vreg[VCH];
   auto load_tile = [&](int64_t t) {
     const int64_t k0 = t * kTile;
+    const uint16_t* kt = kbase + k0 * krow_stride;
+    const uint16_t* vt = vbase + (k0 / 32) * vblk_stride;
+    if (k0 + kTile <= hi) {                // whole tile below the last query
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c / (D / 8), ch = c - row * (D / 8);
-      const int64_t key = k0 + row;
-      kreg[i] = key < hi ? ld16(kc + ((b * C + key) * a.n_kv + g) * D + 8 * ch)
-                         : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < KCH; ++i) kreg[i] = ld16(kt + k_row[i] * krow_stride + k_off[i]);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) vreg[i] = ld16(vt + v_off[i]);
+      return;
     }
 #pragma unroll
+    for (int i = 0; i < KCH; ++i)
+      kreg[i] = k0 + k_row[i] < hi ? ld16(kt + k_row[i] * krow_stride + k_off[i])
+                                   : u32x4{0, 0, 0, 0};
+#pragma unroll
     for (int i = 0; i < VCH; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int blk = c / (D * 4);
-      const int rem = c - blk * (D * 4);
-      const int dd = rem >> 2, ch = rem & 3;
-      const int64_t key0 = k0 + 32 * blk + 8 * ch;
+      const int64_t key0 = k0 + v_key[i];
       u32x4 v = {0, 0, 0, 0};
       if (key0 < hi) {
-        const int64_t kb = k0 / 32 + blk;
-        v = ld16(vc + ((b * (C / 32) + kb) * a.n_kv + g) * (int64_t)(D * 32) + dd * 32 + 8 * ch);
+        v = ld16(vt + v_off[i]);
         if (key0 + 8 > hi) {       // zero the keys past the last query
           const int valid = (int)(hi - key0);
 #pragma unroll
@@ -146,32 +183,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c / (D / 8), ch = c - row * (D / 8);
-      st16(&Ks[buf][row * KP + 8 * ch], kreg[i]);
-    }
+    for (int i = 0; i < KCH; ++i) st16(&Ks[buf][k_lds_off[i]], kreg[i]);
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int blk = c / (D * 4);
-      const int rem = c - blk * (D * 4);
-      const int dd = rem >> 2, ch = rem & 3;
-      st16(&Vs[buf][(blk * D + dd) * VP + 8 * ch], vreg[i]);
-    }
+    for (int i = 0; i < VCH; ++i) st16(&Vs[buf][v_lds_off[i]], vreg[i]);
   };
 
-  load_tile(t_first);
-  store_tile(0);
-  __syncthreads();
+  // LDS read offsets of this lane's operands
+  int ka_off[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int krow = 32 * (mt >> 1) + 8 * (j >> 2) + 4 * (mt & 1) + (j & 3);
+    ka_off[mt] = k_lds<D>(krow, g4);     // chunk g4 of k-step 0; k-step ks adds 4 chunks
+  }
+  const int va_off = j * VP + 8 * g4;
 
-  int buf = 0;
-  for (int64_t t = t_first; t <= t_last; ++t) {
-    const bool more = t < t_last;
-    if (more) load_tile(t + 1);
-    const int64_t k0 = t * kTile;
-
-    // ---- S^T = K Q^T over the tile: 4 M tiles of 16 keys
+  // One tile of keys: S^T = K Q^T, softmax update, O^T += V^T P^T.
+  auto tile = [&](int buf, int64_t k0, auto masked) {
     f32x4 S[4][NT];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -181,20 +208,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int krow = 32 * (mt >> 1) + 8 * (j >> 2) + 4 * (mt & 1) + (j & 3);
-        const u32x4 A = ld16(&Ks[buf][krow * KP + 32 * ks + 8 * g4]);
+        const u32x4 A = ld16(&Ks[buf][ka_off[mt] + 32 * ks]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) S[mt][n] = mfma16x16x32(A, qop[n][ks], S[mt][n]);
       }
     }
     // lane (j, g4) now holds, for M tile mt and element r, the score of key
     // k0 + 32*(mt>>1) + 8*g4 + 4*(mt&1) + r.
-    const bool need_mask = (k0 + kTile - 1 > P_min) ||
-                           (a.window > 0 && k0 < P_max - a.window + 1);
     u32x4 Pk[2][NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      if (need_mask) {
+      if constexpr (decltype(masked)::value) {
         const int rel0 = (int)(k0 - (a.q_offset + tpos[n]));   // key - p at (mt, r) = 0
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -244,11 +268,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 A = ld16(&Vs[buf][(h * D + 16 * dt + j) * VP + 8 * g4]);
+        const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * VP]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[h][n], O[dt][n]);
       }
+  };
 
+  load_tile(t_first);
+  store_tile(0);
+  __syncthreads();
+
+  int buf = 0;
+  for (int64_t t = t_first; t <= t_last; ++t) {
+    const bool more = t < t_last;
+    if (more) load_tile(t + 1);
+    const int64_t k0 = t * kTile;
+    const bool need_mask = (k0 + kTile - 1 > P_min) ||
+                           (a.window > 0 && k0 < P_max - a.window + 1);
+    if (need_mask)
+      tile(buf, k0, std::true_type{});
+    else
+      tile(buf, k0, std::false_type{});
     if (more) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -270,24 +310,37 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(AttnArgs a, int 
   }
 }
 
-template <int D, int NT>
+template <int D, int NT, int NW>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-  const int rows = kWaves * NT * 16;
+  const int rows = NW * NT * 16;
+  if (a.q_mult > rows) return hipErrorInvalidValue;
   const int BQ = rows / a.q_mult;
   const int n_qb = (a.T_q + BQ - 1) / BQ;
   const int64_t grid = (int64_t)n_qb * a.B * a.n_kv;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NT>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s,
                      a, BQ, n_qb);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile shape per head dimension: N tiles (16 queries each) per wave and
+// waves per workgroup.  Overridable at build time for tuning sweeps.
+#ifndef SA_PF64
+#define SA_PF64 2, 4
+#endif
+#ifndef SA_PF96
+#define SA_PF96 2, 8
+#endif
+#ifndef SA_PF128
+#define SA_PF128 2, 4
+#endif
+
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_d<64, 2>(a, s);
-    case 96: return launch_d<96, 2>(a, s);
-    case 128: return launch_d<128, 2>(a, s);
+    case 64: return launch_d<64, SA_PF64>(a, s);
+    case 96: return launch_d<96, SA_PF96>(a, s);
+    case 128: return launch_d<128, SA_PF128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,15 +41,19 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
                                          __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
 }
 
-// fp64 -> bf16 with one rounding: first round toward zero to fp32 and fold
-// the discarded bits into the last fp32 bit (round to odd, which keeps the
-// fp32 value off every bf16 tie it did not sit on exactly), then round that
-// to bf16 to nearest even.  fp32 carries 16 more significand bits than bf16,
-// so the two steps equal a single direct rounding.
+// fp64 -> bf16 with one rounding (to nearest, ties to even).  First round
+// to fp32 to nearest (hardware).  A bf16 rounding midpoint is itself an fp32
+// value, so that first step can only land ON a midpoint, never across one;
+// when it lands on one (low 16 bits 0x8000) without being exact, the fp64
+// value says which side it came from and the bf16 rounding goes that way.
+// Otherwise rounding the fp32 value to bf16 to nearest even is exact.
 __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
-  float t = __double2float_rz(x);
+  const float t = (float)x;
   uint32_t u = __float_as_uint(t);
-  if ((double)t != x) u |= 1u;
+  if ((u & 0xFFFFu) == 0x8000u && (double)t != x) {
+    const bool away = fabs(x) > fabs((double)t);
+    return (away ? u + 0x8000u : u) >> 16;
+  }
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }

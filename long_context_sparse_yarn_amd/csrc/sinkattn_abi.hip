@@ -34,6 +34,8 @@ int ok() {
   return SA_OK;
 }
 
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 int elt_bytes(int dtype) { return dtype == SA_BF16 ? 2 : (dtype == SA_F32 ? 4 : 0); }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -112,6 +114,7 @@ int64_t sa_kv_cache_bytes(int64_t L, int64_t B, int64_t T, int64_t H_kv, int64_t
 int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int64_t offset,
                     const sa_yarn* y, void* stream) {
   if (!x) return fail(SA_ERR_ARG, "x is null");
+  if (misaligned(x)) return fail(SA_ERR_ARG, "x must be 16-byte aligned");
   const int eb = elt_bytes(dtype);
   if (!eb) return fail(SA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (B <= 0 || T < 0 || n_heads <= 0 || offset < 0)
@@ -138,6 +141,7 @@ int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int6
 int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity,
                     int n_kv, int d_h, int64_t offset) {
   if (!out || !k || !v) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(k) || misaligned(v)) return fail(SA_ERR_ARG, "k and v must be 16-byte aligned");
   if (!elt_bytes(dtype)) return fail(SA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (B <= 0 || n_kv <= 0 || d_h <= 0) return fail(SA_ERR_ARG, "need B, n_kv, d_h > 0");
   if (capacity <= 0 || capacity % 32)
@@ -174,6 +178,7 @@ int64_t kv_cache_offset(const sa_kv_cache* c) { return c ? c->offset : -1; }
 
 int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v, int T_new, void* stream) {
   if (!c || !k_rot || !v) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(k_rot) || misaligned(v)) return fail(SA_ERR_ARG, "k_rot and v must be 16-byte aligned");
   if (T_new <= 0) return fail(SA_ERR_ARG, "T_new must be positive");
   if (c->offset + T_new > c->capacity)
     return fail(SA_ERR_CAPACITY, "append of %d rows at offset %lld exceeds capacity %lld", T_new,
@@ -222,6 +227,7 @@ int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap) {
 static int check_attn(const void* q, const sa_kv_cache* c, const float* sinks, const void* out,
                       int B, int T_q, int n_q, int n_kv, int d_h) {
   if (!q || !c || !sinks || !out) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(q) || misaligned(out)) return fail(SA_ERR_ARG, "q and out must be 16-byte aligned");
   if (B <= 0 || T_q < 0 || n_q <= 0 || n_kv <= 0 || d_h <= 0)
     return fail(SA_ERR_ARG, "non-positive size");
   if (n_q % n_kv) return fail(SA_ERR_SHAPE, "n_q %d is not a multiple of n_kv %d", n_q, n_kv);
@@ -306,7 +312,7 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
       return fail(SA_ERR_SHAPE, "bf16 attention supports d_h in {64, 96, 128}, got %d", d_h);
     if (q_mult > 16) return fail(SA_ERR_SHAPE, "bf16 decode needs n_q/n_kv <= 16");
     const size_t need = sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, c->capacity);
-    if (!workspace || ws_bytes < need)
+    if (!workspace || ws_bytes < need || misaligned(workspace))
       return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     const int64_t span = a.window > 0 ? (a.window < c->offset ? a.window : c->offset) : c->offset;
     DecodeArgs da;

@@ -81,6 +81,9 @@ def test_cache_create_validation():
     h = ctypes.c_void_p()
     assert B._kv_cache_create(ctypes.byref(h), None, FAKE_V, 0, 2, 256, 2, 64, 0) == SA_ERR_ARG
     assert "null" in sa.last_error()
+    h2 = ctypes.c_void_p()
+    assert B._kv_cache_create(ctypes.byref(h2), ctypes.c_void_p(0x10008), FAKE_V, 0, 2, 256, 2,
+                              64, 0) == SA_ERR_ARG                      # not 16-byte aligned
     st, h = create(offset=40)
     assert st == SA_OK and B._kv_cache_offset(h) == 40
     assert B._kv_cache_offset(None) == -1
@@ -103,6 +106,7 @@ def test_errors_are_reported_before_any_launch():
     assert P(q, h, s, o, 3, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE   # B != cache
     assert P(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.0, 0, None) == SA_ERR_ARG
     assert P(None, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_ARG
+    assert P(ctypes.c_void_p(0x30004), h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_ARG
     assert P(q, h, s, o, 2, 0, 8, 2, 64, 0, 0.125, 0, None) == SA_OK          # nothing to do
     # decode: q_mult > 16 on bf16, workspace too small
     D = B._sinkattn_decode
