@@ -31,6 +31,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
+# HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
+# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
+# valid only for the kernel sources it was measured on.
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "66b90877f1d3a2e4", "bytes": (33363 * 2 + 34701) * 1024}
+KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_kernels.h")
+
+
+def kernel_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_yarn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def pairs_allowed(q_offset, T, window):
     p = q_offset + np.arange(T, dtype=np.int64)
@@ -274,7 +289,11 @@ def main():
     full = [p for p in per_layer if p["window"] == 0][0]
     full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
     roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": full["frac_mfma"], "traffic": None,
+                "unit": "TFLOP/s", "frac": full["frac_mfma"],
+                "traffic": (TRAFFIC_FULL_PREFILL["bytes"]
+                            if kernel_sources_hash() == TRAFFIC_FULL_PREFILL["sources_sha256_16"]
+                            else None),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                 "kernel": "prefill_bf16_kernel<96,2,8> (full causal)",
                 "kernel_ms": round(kern_ms[full_i], 4)}
     line = {
