@@ -9,7 +9,9 @@
 // built to keep HBM busy.
 //  * Split-KV: each wave owns one (b, g) pair and one contiguous run of
 //    32-key blocks of the allowed range; the pairs x splits give thousands
-//    of independent waves for 256 CUs.
+//    of independent waves for 256 CUs.  Consecutive waves take the KV heads
+//    of one (b, split), so the waves in flight together read whole cache
+//    rows (the heads of a row are contiguous) and whole V blocks.
 //  * Matrix cores on 8 of 16 columns: the q_mult query heads of the group
 //    form the N side of S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so one K row
 //    load serves all heads of the group.  K operands load straight from HBM
@@ -25,7 +27,9 @@
 //    and adds the sink exactly once:
 //      M = max(sigma', max_c m_c), L = 2^(sigma'-M) + sum_c l_c 2^(m_c-M),
 //      out = sum_c acc_c 2^(m_c-M) / L        (sigma' = sigma * log2 e).
-//    Splits with no allowed key carry m = -inf, l = 0 and drop out.
+//    Splits with no allowed key carry m = -inf, l = 0 and drop out.  A span
+//    of at most 256 rows (a band layer) runs as one split per (b, g), whose
+//    wave adds the sink and writes the output itself.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -33,8 +37,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTargetWaves = 4096;
+#ifndef SA_DEC_WAVES
+#define SA_DEC_WAVES 2048
+#endif
+constexpr int kTargetWaves = SA_DEC_WAVES;
 constexpr int kMaxSplits = 256;
+constexpr int64_t kSingleSplitRows = 256;   // spans this short skip the split/merge
 constexpr float kSlack = 8.0f;
 
 template <int D>
@@ -73,9 +81,12 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   const int S = da.n_splits;
   const int pairs = a.B * a.n_kv;
   if (wid >= pairs * S) return;
-  const int split = wid % S;
-  const int pair = wid / S;
-  const int b = pair / a.n_kv, g = pair - b * a.n_kv;
+  // KV head fastest: waves running side by side read whole cache rows
+  // (all heads of a row are contiguous) and whole 32-key V blocks.
+  const int g = wid % a.n_kv;
+  const int split = (wid / a.n_kv) % S;
+  const int b = wid / (a.n_kv * S);
+  const int pair = b * a.n_kv + g;
   const int64_t C = a.C;
 
   const int64_t P = a.q_offset;                         // query position
@@ -193,8 +204,27 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
     }
   }
 
-  // ---- partial of this split: lanes (j < q_mult)
   l_run = sum_over_col(l_run);
+  if (S == 1) {
+    // One split: fold in the sink here and write the output (no merge pass).
+    if (j < a.q_mult) {
+      const int h = g * a.q_mult + j;
+      const float sg = a.sinks[h] * SA_LOG2E;
+      const float M = fmaxf(m_run, sg);
+      const float wr = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+      const float L = l_run * wr + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
+      const float f = wr / L;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 o = O[dt] * f;
+        *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * g4) =
+            u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+      }
+    }
+    return;
+  }
+  // ---- partial of this split: lanes (j < q_mult)
   if (j < a.q_mult) {
     const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + j;
     float* acc = da.ws + slot * D;
@@ -279,7 +309,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const int grid = (waves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -287,6 +317,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 int decode_splits(int B, int n_kv, int64_t span_rows) {
+  if (span_rows <= kSingleSplitRows) return 1;       // short span: one wave per (b, g)
   const int64_t nblk = (span_rows + 31) / 32 + 1;   // a span may straddle one more block
   int64_t s = (kTargetWaves + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   if (s > nblk) s = nblk;
