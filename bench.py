@@ -4,9 +4,9 @@
 
 One step = the whole hot path over one batch of the GPT-OSS-Lite-shaped
 prefill (B=4, T=4096, n_q=8, n_kv=4, d_h=96, bf16, YaRN s=32 base 1.5e5):
-for each of its two layer kinds (128-token band, full causal) a fresh copy
-of the raw Q and K, RoPE on Q and K at offset 0, the cache rewound to 0 and
-K/V appended, and sink attention over the chunk.  Inputs are resident in HBM
+for each of its two layer kinds (128-token band, full causal) the cache
+rewound to 0, RoPE from the raw Q and K into working buffers, K/V appended,
+and sink attention over the chunk.  Inputs are resident in HBM
 before timing starts.  The value is algorithmic attention TFLOP/s of the
 step (4*d*n_q*B*sum_p|A(p)| flops: allowed query/key pairs only).
 
@@ -96,12 +96,10 @@ class Layer:
 
 
 def run_layer(L, w, sa, ev=None):
-    L.qw.copy_(L.q0)
-    L.kw.copy_(L.k0)
     L.cache.restore(L.snap)
     o = L.cache.offset
-    sa.yarn_rope_apply(L.qw, o, L.yarn)
-    sa.yarn_rope_apply(L.kw, o, L.yarn)
+    sa.yarn_rope_apply(L.q0, o, L.yarn, out=L.qw)      # raw -> rotated, out of place
+    sa.yarn_rope_apply(L.k0, o, L.yarn, out=L.kw)
     L.cache.append(L.kw, L.v)
     if ev is not None:
         ev[0].record()
@@ -169,11 +167,9 @@ def decode_extra(sa, torch, steps_warm=4):
         out = torch.empty_like(qbuf)
 
         def step(s, ev=None):
-            qbuf.copy_(toks[s]["q"])
-            kbuf.copy_(toks[s]["k"])
             o = cache.offset
-            sa.yarn_rope_apply(qbuf, o, y)
-            sa.yarn_rope_apply(kbuf, o, y)
+            sa.yarn_rope_apply(toks[s]["q"], o, y, out=qbuf)
+            sa.yarn_rope_apply(toks[s]["k"], o, y, out=kbuf)
             cache.append(kbuf, toks[s]["v"])
             if ev is not None:
                 ev[0].record()

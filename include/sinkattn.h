@@ -108,6 +108,12 @@ int64_t sa_kv_cache_bytes(int64_t L, int64_t B, int64_t T, int64_t H_kv,
 int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h,
                     int64_t offset, const sa_yarn* y, void* stream);
 
+/* The same rotation out of place: reads x, writes y (both device
+ * [B, T, n_heads, d_h] of `dtype`); y may be x itself but must not partly
+ * overlap it (SA_ERR_ARG).  x is not modified unless y == x. */
+int yarn_rope(const void* x, void* y, int dtype, int B, int T, int n_heads, int d_h,
+              int64_t offset, const sa_yarn* yarn, void* stream);
+
 /* Opaque host-side handle of one layer's cache.  K/V storage is the
  * caller's (layout above); the handle records the shape, the offset (rows
  * written: the next append goes to row `offset` of every sequence; one

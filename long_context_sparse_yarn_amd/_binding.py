@@ -23,7 +23,7 @@ STATUS = {0: "SA_OK", -1: "SA_ERR_ARG", -2: "SA_ERR_SHAPE", -3: "SA_ERR_DTYPE",
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libsinkattn.so is not built (%s); run `python -m long_context_sparse_yarn_amd.build` "
+        "libsinkattn.so is not built (%s); run `python long_context_sparse_yarn_amd/build.py` "
         "or __graft_entry__.build()" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -55,6 +55,8 @@ _sa_yarn_inv_freq = _sig("sa_yarn_inv_freq", _i32, ctypes.POINTER(SaYarn),
 _sa_kv_cache_bytes = _sig("sa_kv_cache_bytes", _i64, _i64, _i64, _i64, _i64, _i64, _i64)
 _yarn_rope_apply = _sig("yarn_rope_apply", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
                         ctypes.POINTER(SaYarn), _vp)
+_yarn_rope = _sig("yarn_rope", _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                  ctypes.POINTER(SaYarn), _vp)
 _kv_cache_create = _sig("kv_cache_create", _i32, ctypes.POINTER(_vp), _vp, _vp, _i32, _i32,
                         _i64, _i32, _i32, _i64)
 _kv_cache_destroy = _sig("kv_cache_destroy", _i32, _vp)
@@ -133,15 +135,23 @@ def kv_cache_bytes(L, B, T, H_kv, d, dtype_bytes) -> int:
     return int(_sa_kv_cache_bytes(L, B, T, H_kv, d, dtype_bytes))
 
 
-def yarn_rope_apply(x: torch.Tensor, offset: int, y: Yarn, stream=None) -> torch.Tensor:
-    """In place on x [B, T, H, d]; returns x."""
+def yarn_rope_apply(x: torch.Tensor, offset: int, y: Yarn, stream=None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rotate x [B, T, H, d] at positions offset + t: in place, or into `out`
+    (same shape and dtype) when given.  Returns the rotated tensor."""
     if x.dim() != 4:
         raise ValueError("x must be [B, T, H, d]")
     B, T, H, d = x.shape
     s = y.c_struct()
-    _check(_yarn_rope_apply(_dev(x, "x"), _dtype_code(x), B, T, H, d, int(offset),
-                            ctypes.byref(s), _stream(stream)))
-    return x
+    if out is None:
+        _check(_yarn_rope_apply(_dev(x, "x"), _dtype_code(x), B, T, H, d, int(offset),
+                                ctypes.byref(s), _stream(stream)))
+        return x
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _check(_yarn_rope(_dev(x, "x"), _dev(out, "out"), _dtype_code(x), B, T, H, d, int(offset),
+                      ctypes.byref(s), _stream(stream)))
+    return out
 
 
 def v_cache_shape(B: int, C: int, n_kv: int, d: int):

@@ -1,6 +1,9 @@
 """Build libsinkattn.so for gfx950 in-tree (hipcc, no JIT cache).
 
-    python -m long_context_sparse_yarn_amd.build [--verbose]
+    python long_context_sparse_yarn_amd/build.py [--verbose]
+
+(Run it as a script, not with -m: importing it through the package would
+first load the library it is about to build.)
 
 Every call compiles from scratch.  Flags: -O3, gfx950 only, and the packed
 fp32 instructions disabled on the device (-packed-fp32-ops).

@@ -1,4 +1,5 @@
-// yarn_rope_apply: rotate head rows in place at global positions.
+// yarn_rope / yarn_rope_apply: rotate head rows at global positions, from a
+// source buffer into a destination (the same buffer for the in-place form).
 //
 // "MoE-Xtend" README, ROPE + SCALING: cos/sin of (position * inv_freq_i),
 // both scaled by the YaRN concentration c; DESIGN CONTRACTS: the position is
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
   const int row0 = blockIdx.x * rows;
   const int nrows = min(rows, a.BT - row0);
   const int ntask = nrows * per_row;
+  const char* src = reinterpret_cast<const char*>(a.src);
   char* base = reinterpret_cast<char*>(a.x);
 
   Rot<ELT> x1[kTasks], x2[kTasks];
@@ -142,10 +144,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
       const int r = e / per_row;
       const int rem = e - r * per_row;
       const int h = rem / cpr, ch = rem - h * cpr;
-      ptr[k] = base + (((int64_t)(row0 + r) * a.H + h) * a.d + 8 * ch) * ELT;
+      const int64_t off = (((int64_t)(row0 + r) * a.H + h) * a.d + 8 * ch) * ELT;
+      ptr[k] = base + off;
       tab[k] = r * half + 8 * ch;
-      x1[k].load(ptr[k]);
-      x2[k].load(ptr[k] + half * ELT);
+      x1[k].load(src + off);
+      x2[k].load(src + off + half * ELT);
     }
   }
   for (int e = threadIdx.x; e < nrows * half; e += kThreads) {
@@ -175,15 +178,18 @@ __global__ __launch_bounds__(kThreads) void rope_pairs_kernel(RopeArgs a) {
     double sn, cn;
     sincos_reduced((double)(a.offset + t) * a.inv_freq[i], &sn, &cn);
     const double cc = cn * a.conc, ss = sn * a.conc;
-    char* p = reinterpret_cast<char*>(a.x) + (rh * a.d + i) * ELT;
+    const int64_t off = (rh * a.d + i) * ELT;
+    const char* sp = reinterpret_cast<const char*>(a.src) + off;
+    const char* sq = sp + half * ELT;
+    char* p = reinterpret_cast<char*>(a.x) + off;
     char* q = p + half * ELT;
     if (ELT == 2) {
-      const double u = bf16_to_f32(*reinterpret_cast<uint16_t*>(p));
-      const double v = bf16_to_f32(*reinterpret_cast<uint16_t*>(q));
+      const double u = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sp));
+      const double v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sq));
       *reinterpret_cast<uint16_t*>(p) = (uint16_t)f64_to_bf16_bits(u * cc - v * ss);
       *reinterpret_cast<uint16_t*>(q) = (uint16_t)f64_to_bf16_bits(v * cc + u * ss);
     } else {
-      const double u = *reinterpret_cast<float*>(p), v = *reinterpret_cast<float*>(q);
+      const double u = *reinterpret_cast<const float*>(sp), v = *reinterpret_cast<const float*>(sq);
       *reinterpret_cast<float*>(p) = (float)(u * cc - v * ss);
       *reinterpret_cast<float*>(q) = (float)(v * cc + u * ss);
     }

@@ -9,7 +9,8 @@
 #define SA_MAX_HALF 128   // d_h <= 256
 
 struct RopeArgs {
-  void* x;
+  const void* src;      // rows read from here ...
+  void* x;              // ... and written here (may be the same buffer)
   int64_t offset;
   int BT, T, H, d;
   double conc;

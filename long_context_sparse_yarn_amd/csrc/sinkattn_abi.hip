@@ -111,10 +111,10 @@ int64_t sa_kv_cache_bytes(int64_t L, int64_t B, int64_t T, int64_t H_kv, int64_t
   return r;
 }
 
-int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int64_t offset,
-                    const sa_yarn* y, void* stream) {
-  if (!x) return fail(SA_ERR_ARG, "x is null");
-  if (misaligned(x)) return fail(SA_ERR_ARG, "x must be 16-byte aligned");
+int yarn_rope(const void* x, void* y, int dtype, int B, int T, int n_heads, int d_h,
+              int64_t offset, const sa_yarn* yarn, void* stream) {
+  if (!x || !y) return fail(SA_ERR_ARG, "x or y is null");
+  if (misaligned(x) || misaligned(y)) return fail(SA_ERR_ARG, "x and y must be 16-byte aligned");
   const int eb = elt_bytes(dtype);
   if (!eb) return fail(SA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (B <= 0 || T < 0 || n_heads <= 0 || offset < 0)
@@ -122,12 +122,18 @@ int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int6
   if (d_h <= 0 || d_h % 8 || d_h > 2 * SA_MAX_HALF)
     return fail(SA_ERR_SHAPE, "d_h must be a positive multiple of 8 up to %d", 2 * SA_MAX_HALF);
   if ((int64_t)B * T > INT32_MAX) return fail(SA_ERR_ARG, "B*T too large");
+  const char* xb = static_cast<const char*>(x);
+  const char* yb = static_cast<const char*>(y);
+  const int64_t bytes = (int64_t)B * T * n_heads * d_h * eb;
+  if (xb != yb && xb < yb + bytes && yb < xb + bytes)
+    return fail(SA_ERR_ARG, "x and y overlap without being the same buffer");
   RopeArgs a;
   memset(&a, 0, sizeof a);
-  int st = yarn_table(y, d_h, a.inv_freq, &a.conc);
+  int st = yarn_table(yarn, d_h, a.inv_freq, &a.conc);
   if (st != SA_OK) return st;
   if (T == 0) return ok();
-  a.x = x;
+  a.src = x;
+  a.x = y;
   a.offset = offset;
   a.BT = B * T;
   a.T = T;
@@ -136,6 +142,11 @@ int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int6
   hipError_t e = launch_rope(a, eb, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "rope launch");
   return ok();
+}
+
+int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int64_t offset,
+                    const sa_yarn* y, void* stream) {
+  return yarn_rope(x, x, dtype, B, T, n_heads, d_h, offset, y, stream);
 }
 
 int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity,

@@ -129,6 +129,10 @@ def test_errors_are_reported_before_any_launch():
     assert R(q, 0, 1, 4, 8, 96, 0, ctypes.byref(y), None) == SA_ERR_SHAPE   # yarn d_h 64
     assert R(q, 0, 1, 4, 8, 64, -1, ctypes.byref(y), None) == SA_ERR_ARG
     assert R(q, 0, 1, 0, 8, 64, 0, ctypes.byref(y), None) == SA_OK          # T = 0
+    R2 = B._yarn_rope
+    # out of place: partial overlap refused, exact aliasing allowed (no launch at T = 0)
+    assert R2(q, ctypes.c_void_p(0x30000 + 64), 0, 1, 4, 8, 64, 0, ctypes.byref(y), None) == SA_ERR_ARG
+    assert R2(q, q, 0, 1, 0, 8, 64, 0, ctypes.byref(y), None) == SA_OK
 
 
 def test_snapshot_bookkeeping_without_appends():

@@ -50,6 +50,20 @@ def test_rope_matches_oracle(dtype, B, T, H, d, off, y):
     assert (ulp == 0).mean() >= 0.999
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_out_of_place_equals_in_place(dtype):
+    y = Yarn()
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, 50, 8, 96)).astype(np.float32)
+    a, src = dev(x, dtype), dev(x, dtype)
+    out = torch.empty_like(src)
+    sa.yarn_rope_apply(a, 777, lib_yarn(96, y))
+    sa.yarn_rope_apply(src, 777, lib_yarn(96, y), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a)
+    assert torch.equal(src, dev(x, dtype))          # the source is untouched
+
+
 def test_rope_position_past_table_length_uses_true_angle():
     # The same row rotated at p and at p + 131072 must differ (no wrap).
     y = Yarn()
