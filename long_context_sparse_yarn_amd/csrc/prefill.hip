@@ -21,10 +21,11 @@
 //    blocked V cache layout (32 keys contiguous per coordinate).
 //  * Online softmax in base 2 (log2 e folded into the scale and the sink),
 //    seeded with the sink: m = sigma*log2e, l = 1 (sigma = -inf: m = -inf,
-//    l = 0).  The running max is lazy: it moves (with a cross-lane max and a
-//    rescale of O and l) only when some score exceeds it by more than 2^8,
-//    so most tiles need no cross-lane traffic and no accumulator rescale;
-//    the exponentials stay below 2^8 either way.  Probabilities are rounded
+//    l = 0).  The reference is lazy: it moves to the running max (with a
+//    cross-lane max and a rescale of O and l) only when a lane's tile sum
+//    passes 2^64 or a query has no reference yet, in a slow path outside the
+//    steady-state loop; so most tiles need no max, no cross-lane traffic and
+//    no accumulator rescale, and nothing comes near overflow.  Probabilities are rounded
 //    to bf16 once (v_cvt_pk_bf16_f32) and the row sums accumulate those same
 //    rounded values (v_dot2c_f32_bf16), so numerator and denominator agree.
 //  * Masks are computed from positions, only on tiles that cross the
@@ -43,7 +44,7 @@
 namespace {
 
 constexpr int kTile = 64;  // keys per tile
-constexpr float kSlack = 8.0f;  // log2 headroom of the lazy running max
+constexpr float kHeadroom = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 
 // LDS placement of K row r, 16-byte chunk k (in elements).  The operand
 // reads take rows 32h + 8q + 4t + r' (q, r' < 4) across 16 lanes; a padded
@@ -197,28 +198,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   }
   const int va_off = j * VP + 8 * g4;
 
-  // One tile of keys: S^T = K Q^T, softmax update, O^T += V^T P^T.
-  auto tile = [&](int buf, int64_t k0, auto masked) {
-    f32x4 S[4][NT];
+  // ---- one tile of keys, in three parts: scores S^T = K Q^T (masked on
+  // tiles that cross the diagonal or the band edge), probabilities against
+  // the current reference m_run, and O^T += V^T P^T.
+  struct Scores { f32x4 v[4][NT]; };
+  auto scores = [&](int buf, int64_t k0, auto masked) {
+    Scores S;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) S[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NT; ++n) S.v[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const u32x4 A = ld16(&Ks[buf][ka_off[mt] + 32 * ks]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) S[mt][n] = mfma16x16x32(A, qop[n][ks], S[mt][n]);
+        for (int n = 0; n < NT; ++n) S.v[mt][n] = mfma16x16x32(A, qop[n][ks], S.v[mt][n]);
       }
     }
-    // lane (j, g4) now holds, for M tile mt and element r, the score of key
+    // lane (j, g4) holds, for M tile mt and element r, the score of key
     // k0 + 32*(mt>>1) + 8*g4 + 4*(mt&1) + r.
-    u32x4 Pk[2][NT];
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      if constexpr (decltype(masked)::value) {
+      for (int n = 0; n < NT; ++n) {
         const int rel0 = (int)(k0 - (a.q_offset + tpos[n]));   // key - p at (mt, r) = 0
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -226,44 +229,36 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
           for (int r = 0; r < 4; ++r) {
             const int rel = rel0 + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1) + r;
             const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
-            if (!ok) S[mt][n][r] = -INFINITY;
+            if (!ok) S.v[mt][n][r] = -INFINITY;
           }
       }
-      float mx = -INFINITY;
+    }
+    return S;
+  };
+  // p = 2^(s*scale - m_run), rounded to bf16 once; ls = this lane's sum of
+  // those rounded values (v_dot2 against 1).
+  auto probs = [&](const Scores& S, u32x4 (&Pk)[2][NT], float (&ls)[NT]) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[mt][n][r]);
-      // Lazy max: keep the running reference while no score passes it by
-      // more than 2^kSlack; only then (wave-uniform branch) take the column
-      // max across lanes and rescale the partial sums.
-      if (__builtin_amdgcn_ballot_w64(mx * scale > m_run[n] + kSlack) != 0) {
-        const float m_new = fmaxf(m_run[n], max_over_col(mx) * scale);
-        // m_run == -inf: nothing accumulated yet (and m_new may be -inf too)
-        const float alpha = (m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
-        l_run[n] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
-        m_run[n] = m_new;
-      }
+    for (int n = 0; n < NT; ++n) {
       const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
-      float ls = l_run[n];
+      float acc = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint32_t w[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 2 * e2;
-          const float p0 = fast_exp2(fmaf(S[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
-          const float p1 = fast_exp2(fmaf(S[2 * h + ((e + 1) >> 2)][n][(e + 1) & 3], scale, -m_use));
+          const float p0 = fast_exp2(fmaf(S.v[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
+          const float p1 = fast_exp2(fmaf(S.v[2 * h + ((e + 1) >> 2)][n][(e + 1) & 3], scale, -m_use));
           w[e2] = pack_bf16x2(p0, p1);
-          ls = sum_bf16x2(w[e2], ls);
+          acc = sum_bf16x2(w[e2], acc);
         }
         Pk[h][n] = u32x4{w[0], w[1], w[2], w[3]};
       }
-      l_run[n] = ls;
+      ls[n] = acc;
     }
-    // ---- O^T += V^T P^T, two 32-key halves
+  };
+  auto pv = [&](int buf, const u32x4 (&Pk)[2][NT]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -273,25 +268,78 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
         for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[h][n], O[dt][n]);
       }
   };
+  // Move the reference to the true running max (column max across the four
+  // lanes of a query) and rescale what has been accumulated.
+  auto rescale = [&](const Scores& S) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S.v[mt][n][r]);
+      const float m_new = fmaxf(m_run[n], max_over_col(mx) * scale);
+      // m_run == -inf: nothing accumulated yet (and m_new may be -inf too)
+      const float alpha = (m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
+      l_run[n] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
+      m_run[n] = m_new;
+    }
+  };
 
   load_tile(t_first);
   store_tile(0);
   __syncthreads();
 
+  // Steady state: the reference m_run stays put while every lane's tile sum
+  // stays below 2^64 (so no exponential, partial sum or accumulator can come
+  // near fp32/bf16 overflow); a tile that breaks that, or a query with no
+  // reference yet (no sink and nothing seen), leaves the loop for the slow
+  // path, which moves the reference, redoes that tile and comes back.  The
+  // fast loop never rewrites O outside the matrix cores.
   int buf = 0;
-  for (int64_t t = t_first; t <= t_last; ++t) {
-    const bool more = t < t_last;
-    if (more) load_tile(t + 1);
-    const int64_t k0 = t * kTile;
-    const bool need_mask = (k0 + kTile - 1 > P_min) ||
-                           (a.window > 0 && k0 < P_max - a.window + 1);
-    if (need_mask)
-      tile(buf, k0, std::true_type{});
-    else
-      tile(buf, k0, std::false_type{});
-    if (more) store_tile(buf ^ 1);
+  int64_t t = t_first;
+  for (;;) {
+    bool slow = false;
+    Scores S;
+    u32x4 Pk[2][NT];
+    float ls[NT];
+    for (; t <= t_last; ++t) {
+      const bool more = t < t_last;
+      if (more) load_tile(t + 1);
+      const int64_t k0 = t * kTile;
+      const bool need_mask = (k0 + kTile - 1 > P_min) ||
+                             (a.window > 0 && k0 < P_max - a.window + 1);
+      if (need_mask)
+        S = scores(buf, k0, std::true_type{});
+      else
+        S = scores(buf, k0, std::false_type{});
+      probs(S, Pk, ls);
+      bool bad = false;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || m_run[n] == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        slow = true;
+        break;
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
+      pv(buf, Pk);
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+    if (!slow) break;
+    rescale(S);
+    probs(S, Pk, ls);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
+    pv(buf, Pk);
+    if (t < t_last) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    ++t;
   }
 
   // ---- normalise and store: lane holds O^T[16*dt + 4*g4 + r][query]
@@ -325,7 +373,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 // Tile shape per head dimension: N tiles (16 queries each) per wave and
-// waves per workgroup.  Overridable at build time for tuning sweeps.
+// waves per workgroup, for full-causal layers and for band layers (whose
+// workgroups re-read a window of K/V per query block, so taller query blocks
+// cut traffic).  Overridable at build time for tuning sweeps.
 #ifndef SA_PF64
 #define SA_PF64 2, 4
 #endif
@@ -335,12 +385,23 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 #ifndef SA_PF128
 #define SA_PF128 2, 4
 #endif
+#ifndef SA_PFB64
+#define SA_PFB64 2, 4
+#endif
+#ifndef SA_PFB96
+#define SA_PFB96 2, 8
+#endif
+#ifndef SA_PFB128
+#define SA_PFB128 2, 4
+#endif
+constexpr int kBandWindowMax = 512;   // windows up to this use the band shape
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
+  const bool band = a.window > 0 && a.window <= kBandWindowMax;
   switch (a.d) {
-    case 64: return launch_d<64, SA_PF64>(a, s);
-    case 96: return launch_d<96, SA_PF96>(a, s);
-    case 128: return launch_d<128, SA_PF128>(a, s);
+    case 64: return band ? launch_d<64, SA_PFB64>(a, s) : launch_d<64, SA_PF64>(a, s);
+    case 96: return band ? launch_d<96, SA_PFB96>(a, s) : launch_d<96, SA_PF96>(a, s);
+    case 128: return band ? launch_d<128, SA_PFB128>(a, s) : launch_d<128, SA_PF128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -236,3 +236,29 @@ def test_prefill_is_deterministic():
     b = sa.sinkattn_prefill(q, cache, sinks, 0, 0.125, 0)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("scale_qk,growing", [(12.0, True), (12.0, False), (0.02, False)])
+@pytest.mark.parametrize("sink_inf", [False, True])
+def test_prefill_extreme_logits(scale_qk, growing, sink_inf):
+    """Scores far from the sink: large logits that grow along the sequence
+    (the reference must move several times mid-sequence), large logits from
+    the start, and near-zero logits; with and without a sink."""
+    B, T, n_q, n_kv, d = 1, 300, 8, 2, 64
+    rng = np.random.default_rng(21)
+    q = bf16_round((rng.standard_normal((B, T, n_q, d)) * scale_qk).astype(np.float32))
+    k = rng.standard_normal((B, T, n_kv, d)).astype(np.float32) * scale_qk
+    if growing:                       # key norms rise with position: later keys dominate
+        k *= np.linspace(0.2, 1.0, T, dtype=np.float32)[None, :, None, None]
+    k = bf16_round(k)
+    v = bf16_round(rng.standard_normal((B, T, n_kv, d)).astype(np.float32))
+    sinks = np.full(n_q, -np.inf, np.float32) if sink_inf else rng.standard_normal(n_q).astype(np.float32)
+    cache = sa.KVCache.empty(B, 320, n_kv, d, fill=float("nan"))
+    cache.append(dev(k, "bf16"), dev(v, "bf16"))          # K taken as already rotated
+    out = sa.sinkattn_prefill(dev(q, "bf16"), cache, torch.from_numpy(sinks).cuda(), 0, 0.125, 0)
+    torch.cuda.synchronize()
+    got = host(out)
+    want = sink_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                          sinks, 0, 0, 0.125)
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= 2e-2, max_abs(got, want)
