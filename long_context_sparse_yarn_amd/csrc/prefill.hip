@@ -46,31 +46,43 @@ namespace {
 constexpr int kTile = 64;  // keys per tile
 constexpr float kHeadroom = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 
-// LDS placement of K row r, 16-byte chunk k (in elements).  The operand
-// reads take rows 32h + 8q + 4t + r' (q, r' < 4) across 16 lanes; a padded
-// pitch (D + 8) and shifts of 4, 8 and 11 sixteen-byte slots for rows with
-// bit 3, 4 and 5 set put every such read on distinct banks, whether the LDS
-// serves 16-byte reads 8 lanes (128 B) or 16 lanes (256 B) at a time, and no
-// two rows overlap.
+// LDS placement of K row r, 16-byte chunk k (in elements).  Rows are not
+// padded (d = 96 rows take 256 bytes so that the swizzle below stays a
+// permutation of the row's slots); chunk k of row r sits in slot
+// k ^ f(r), f(r) = (r&3) | ((r>>1)&4) | ((r>>1)&8) (the top bit only where a
+// row has 16 slots).  The operand reads take rows 32h + 8q + 4t + r'
+// (q, r' < 4) across 16 lanes and a chunk per lane group; with this swizzle a
+// wave's 16-byte reads hit no bank twice (timed at the conflict-free rate of
+// a linear read, against twice that for a padded pitch).
+template <int D>
+constexpr int k_pitch() { return D == 96 ? 128 : D; }
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  constexpr int mask = k_pitch<D>() / 8 - 1;
+  return ((r & 3) | ((r >> 1) & 4) | ((r >> 1) & 8)) & mask;
+}
 template <int D>
 __device__ __forceinline__ int k_lds(int r, int k) {
-  return r * (D + 8) + 8 * k + 32 * ((r >> 3) & 1) + 64 * ((r >> 4) & 1) + 88 * (r >> 5);
+  return r * k_pitch<D>() + 8 * (k ^ k_swz<D>(r));
 }
+// V^T rows (one per coordinate and 32-key half, 64 bytes each) are not
+// padded either; chunk c of row r sits in slot c ^ ((r>>1)&3), which keeps
+// the 16-lane V^T operand reads conflict-free.
+__device__ __forceinline__ int v_lds(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
 
 template <int D, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
   constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
   constexpr int DT = D / 16;          // coordinate tiles of O^T
-  constexpr int VP = 32 + 8;          // LDS row pitch of V^T (elements)
   constexpr int KTOT = kTile * D / 8; // 16-byte K chunks per tile
   constexpr int VTOT = 2 * D * 4;     // 16-byte V chunks per tile
   constexpr int KCH = (KTOT + kThreads - 1) / kThreads;   // per thread
   constexpr int VCH = (VTOT + kThreads - 1) / kThreads;
-  constexpr int KBUF = kTile * (D + 8) + 184;   // last row's shift: 32 + 64 + 88
+  constexpr int KBUF = kTile * k_pitch<D>();
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * D * 32];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -145,7 +157,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     const int dd = rem >> 2, ch = rem & 3;
     v_key[i] = 32 * blk + 8 * ch;                                  // first key of the chunk
     v_off[i] = (int)(blk * vblk_stride) + dd * 32 + 8 * ch;
-    v_lds_off[i] = (blk * D + dd) * VP + 8 * ch;
+    v_lds_off[i] = v_lds(blk * D + dd, ch);
   }
 
   u32x4 kreg[KCH], vreg[VCH];
@@ -189,14 +201,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int i = 0; i < VCH; ++i) st16(&Vs[buf][v_lds_off[i]], vreg[i]);
   };
 
-  // LDS read offsets of this lane's operands
-  int ka_off[4];
+  // LDS read offsets of this lane's operands: K chunk g4 + 4*ks of row
+  // krow(mt) sits at ka_row[mt] + 32*(ks ^ ka_hi[mt]) (the swizzle's low two
+  // bits act on g4, its high bits on ks); V^T reads add uniform offsets.
+  int ka_row[4], ka_hi[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int krow = 32 * (mt >> 1) + 8 * (j >> 2) + 4 * (mt & 1) + (j & 3);
-    ka_off[mt] = k_lds<D>(krow, g4);     // chunk g4 of k-step 0; k-step ks adds 4 chunks
+    const int f = k_swz<D>(krow);
+    ka_row[mt] = krow * k_pitch<D>() + 8 * (g4 ^ (f & 3));
+    ka_hi[mt] = f >> 2;
   }
-  const int va_off = j * VP + 8 * g4;
+  const int va_off = v_lds(j, g4);
 
   // ---- one tile of keys, in three parts: scores S^T = K Q^T (masked on
   // tiles that cross the diagonal or the band edge), probabilities against
@@ -212,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 A = ld16(&Ks[buf][ka_off[mt] + 32 * ks]);
+        const u32x4 A = ld16(&Ks[buf][ka_row[mt] + 32 * (ks ^ ka_hi[mt])]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) S.v[mt][n] = mfma16x16x32(A, qop[n][ks], S.v[mt][n]);
       }
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * VP]);
+        const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * 32]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[h][n], O[dt][n]);
       }
