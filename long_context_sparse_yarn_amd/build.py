@@ -54,7 +54,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp], verbose)
+    # --no-undefined: a kernel whose host-side launch stub went missing fails here, not at load
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,--no-undefined", *objs, "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -39,31 +39,45 @@
 #include "sa_device.h"
 #include "sa_kernels.h"
 
-#include <type_traits>
+
+#ifndef SA_RD_AHEAD
+#define SA_RD_AHEAD 4
+#endif
+#ifndef SA_INTERLEAVE
+#define SA_INTERLEAVE 0
+#endif
 
 namespace {
 
 constexpr int kTile = 64;  // keys per tile
 constexpr float kHeadroom = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 
-// LDS placement of K row r, 16-byte chunk k (in elements).  Rows are not
-// padded (d = 96 rows take 256 bytes so that the swizzle below stays a
-// permutation of the row's slots); chunk k of row r sits in slot
-// k ^ f(r), f(r) = (r&3) | ((r>>1)&4) | ((r>>1)&8) (the top bit only where a
-// row has 16 slots).  The operand reads take rows 32h + 8q + 4t + r'
-// (q, r' < 4) across 16 lanes and a chunk per lane group; with this swizzle a
-// wave's 16-byte reads hit no bank twice (timed at the conflict-free rate of
-// a linear read, against twice that for a padded pitch).
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// LDS bytes [16 l, 16 l + 16) of the block at lds_block (uniform per wave).
+__device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(lds_block)), 16, 0, 0);
+}
+// Wait for this wave's global loads (including those into LDS).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+template <int Mask, int N>
+__device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(Mask, N, 0); }
+
+// LDS placement of K: rows are not padded (d/8 sixteen-byte slots each) and
+// chunk k of row r sits in slot k ^ f(r).  The operand reads take rows
+// 32h + 8q + 4t + r' (q, r' < 4) across 16 lanes and chunk g4 + 4*ks in lane
+// group g4; with f(r) = (r&3) | ((r>>1)&4) | ((r>>1)&8) (bits above the row's
+// slot count dropped) for d = 64 and 128, and f(r) = 2*(bit1(r) ^ bit4(r)) for
+// the 12-slot rows of d = 96, a wave's 16-byte reads time at the rate of a
+// linear read (a padded pitch measured twice that).  f uses row bits 0, 1, 3
+// and 4 only, so it is the same for the four M tiles a lane reads.
 template <int D>
-constexpr int k_pitch() { return D == 96 ? 128 : D; }
+constexpr int k_pitch() { return D; }
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-  constexpr int mask = k_pitch<D>() / 8 - 1;
+  if constexpr (D == 96) return (((r >> 1) ^ (r >> 4)) & 1) << 1;
+  constexpr int mask = D / 8 - 1;
   return ((r & 3) | ((r >> 1) & 4) | ((r >> 1) & 8)) & mask;
-}
-template <int D>
-__device__ __forceinline__ int k_lds(int r, int k) {
-  return r * k_pitch<D>() + 8 * (k ^ k_swz<D>(r));
 }
 // V^T rows (one per coordinate and 32-key half, 64 bytes each) are not
 // padded either; chunk c of row r sits in slot c ^ ((r>>1)&3), which keeps
@@ -75,14 +89,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
   constexpr int DT = D / 16;          // coordinate tiles of O^T
-  constexpr int KTOT = kTile * D / 8; // 16-byte K chunks per tile
-  constexpr int VTOT = 2 * D * 4;     // 16-byte V chunks per tile
-  constexpr int KCH = (KTOT + kThreads - 1) / kThreads;   // per thread
-  constexpr int VCH = (VTOT + kThreads - 1) / kThreads;
   constexpr int KBUF = kTile * k_pitch<D>();
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * D * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[3][KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[3][2 * D * 32];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -127,63 +137,89 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   }
 
   const float scale = a.sm_scale * SA_LOG2E;
-  const int64_t P_min = a.q_offset + p0;
-  const int64_t P_max = a.q_offset + t_end - 1;
-  const int64_t lo = a.window > 0 ? max((int64_t)0, P_min - a.window + 1) : 0;
-  const int64_t hi = P_max + 1;   // keys >= hi are masked for every row here
-  const int64_t t_first = lo / kTile, t_last = (hi - 1) / kTile;
+  // Positions fit in 32 bits (the launcher rejects caches of 2^31 rows or more).
+  const int P_min = (int)a.q_offset + p0;
+  const int P_max = (int)a.q_offset + t_end - 1;
+  const int lo = a.window > 0 ? max(0, P_min - a.window + 1) : 0;
+  const int hi = P_max + 1;   // keys >= hi are masked for every row here
+  const int t_first = lo / kTile, t_last = (hi - 1) / kTile;
 
-  // ---- per-thread load slots: K chunk (row, ch) and V chunk (blk, dd, ch)
-  const int64_t krow_stride = (int64_t)a.n_kv * D;                  // elements per cache row
-  const int64_t vblk_stride = (int64_t)a.n_kv * D * 32;             // elements per 32-key block
+  // ---- tile loads.  Full tiles go global -> LDS directly (16 bytes per
+  // lane, lane l of a wave writing LDS slot l of a 1 KB block), each lane
+  // fetching the chunk that the swizzled layout puts in its slot.  K rows
+  // at or past hi (keys after the last query, all masked) are fetched from
+  // row hi-1 so that unwritten cache rows are never read.  V of the one
+  // tile that straddles hi goes through registers instead, with the keys
+  // at or past hi zeroed (their probabilities are exactly 0, but 0 * NaN
+  // would not be).
+  const int krow_stride = a.n_kv * D;                  // elements per cache row
+  const int vblk_stride = a.n_kv * D * 32;             // elements per 32-key block
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.kc) + ((int64_t)b * C * a.n_kv + g) * D;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.vc) +
                           ((int64_t)b * (C / 32) * a.n_kv + g) * (int64_t)(D * 32);
-  int k_row[KCH], k_off[KCH], k_lds_off[KCH];
+  constexpr int NSK = k_pitch<D>() / 8;           // 16-byte slots per K row
+  constexpr int KBLK = NSK;                       // 1 KB blocks per K tile (64 rows)
+  constexpr int VBLK = D / 8;                     // 1 KB blocks per V tile (2D rows of 4 slots)
+  constexpr int KBW = (KBLK + NW - 1) / NW;       // blocks per wave
+  constexpr int VBW = (VBLK + NW - 1) / NW;
+  // K slot of block wave + i*NW: row k_r, chunk k_c, element offset k_goff
+  // within the tile.
+  int k_r[KBW], k_c[KBW];
+  uint32_t k_goff[KBW], v_goff[VBW];
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = min((int)threadIdx.x + i * kThreads, KTOT - 1);   // excess slots repeat the last
-    k_row[i] = c / (D / 8);
-    const int ch = c - k_row[i] * (D / 8);
-    k_off[i] = 8 * ch;
-    k_lds_off[i] = k_lds<D>(k_row[i], ch);
+  for (int i = 0; i < KBW; ++i) {
+    const int s = 64 * (wave + i * NW) + lane;
+    const int r = (s / NSK) & 63;
+    k_r[i] = r;
+    k_c[i] = (s % NSK) ^ k_swz<D>(r);
+    k_goff[i] = (uint32_t)(r * krow_stride + 8 * k_c[i]);
   }
-  int v_key[VCH], v_off[VCH], v_lds_off[VCH];
 #pragma unroll
-  for (int i = 0; i < VCH; ++i) {
-    const int c = min((int)threadIdx.x + i * kThreads, VTOT - 1);
-    const int blk = c / (D * 4);
-    const int rem = c - blk * (D * 4);
-    const int dd = rem >> 2, ch = rem & 3;
-    v_key[i] = 32 * blk + 8 * ch;                                  // first key of the chunk
-    v_off[i] = (int)(blk * vblk_stride) + dd * 32 + 8 * ch;
-    v_lds_off[i] = v_lds(blk * D + dd, ch);
+  for (int i = 0; i < VBW; ++i) {
+    const int s = 64 * (wave + i * NW) + lane;
+    const int r = (s >> 2) % (2 * D);
+    const int c = (s & 3) ^ ((r >> 1) & 3);
+    v_goff[i] = (uint32_t)((r >= D ? vblk_stride : 0) + (r % D) * 32 + 8 * c);
   }
-
-  u32x4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int64_t t) {
-    const int64_t k0 = t * kTile;
-    const uint16_t* kt = kbase + k0 * krow_stride;
-    const uint16_t* vt = vbase + (k0 / 32) * vblk_stride;
-    if (k0 + kTile <= hi) {                // whole tile below the last query
+  auto load_k = [&](int buf, int t) {
+    const int k0 = t * kTile;
+    const uint16_t* kt = kbase + (int64_t)k0 * krow_stride;     // uniform
+    const bool full = k0 + kTile <= hi;
+    const int last_row = hi - 1 - k0;
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) kreg[i] = ld16(kt + k_row[i] * krow_stride + k_off[i]);
-#pragma unroll
-      for (int i = 0; i < VCH; ++i) vreg[i] = ld16(vt + v_off[i]);
-      return;
+    for (int i = 0; i < KBW; ++i) {
+      const int blk = wave + i * NW;
+      if (KBLK % NW == 0 || blk < KBLK) {
+        const uint32_t off = full ? k_goff[i]
+                                  : (uint32_t)(min(k_r[i], last_row) * krow_stride + 8 * k_c[i]);
+        lds_direct16(kt + off, &Ks[buf][512 * blk]);
+      }
     }
+  };
+  auto load_v_full = [&](int buf, int t) {
+    const uint16_t* vt = vbase + (int64_t)(t * (kTile / 32)) * vblk_stride;   // uniform
 #pragma unroll
-    for (int i = 0; i < KCH; ++i)
-      kreg[i] = k0 + k_row[i] < hi ? ld16(kt + k_row[i] * krow_stride + k_off[i])
-                                   : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int64_t key0 = k0 + v_key[i];
+    for (int i = 0; i < VBW; ++i) {
+      const int blk = wave + i * NW;
+      if (VBLK % NW == 0 || blk < VBLK)
+        lds_direct16(vt + v_goff[i], &Vs[buf][512 * blk]);
+    }
+  };
+  // Register path: thread c of the workgroup moves chunks c, c + kThreads,
+  // ... of the V^T tile (row = 32-key half * D + coordinate, chunk of 8
+  // keys); zero = true writes zeros.
+  auto store_v_regs = [&](int buf, int t, bool zero) {
+    const int k0 = t * kTile;
+    const uint16_t* vt = vbase + (int64_t)(k0 / 32) * vblk_stride;
+    for (int cidx = threadIdx.x; cidx < 8 * D; cidx += kThreads) {
+      const int r = cidx >> 2, ch = cidx & 3;
+      const int half = r >= D ? 1 : 0, dd = r - half * D;
+      const int key0 = k0 + 32 * half + 8 * ch;
       u32x4 v = {0, 0, 0, 0};
-      if (key0 < hi) {
-        v = ld16(vt + v_off[i]);
-        if (key0 + 8 > hi) {       // zero the keys past the last query
-          const int valid = (int)(hi - key0);
+      if (!zero && key0 < hi) {
+        v = ld16(vt + half * vblk_stride + dd * 32 + 8 * ch);
+        if (key0 + 8 > hi) {
+          const int valid = hi - key0;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             uint32_t keep = (2 * w + 1 < valid) ? 0xFFFFFFFFu : (2 * w < valid ? 0x0000FFFFu : 0u);
@@ -191,98 +227,95 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
           }
         }
       }
-      vreg[i] = v;
+      st16(&Vs[buf][v_lds(r, ch)], v);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) st16(&Ks[buf][k_lds_off[i]], kreg[i]);
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) st16(&Vs[buf][v_lds_off[i]], vreg[i]);
+  auto load_v = [&](int buf, int t) {
+    if (t * kTile + kTile <= hi)
+      load_v_full(buf, t);
+    else
+      store_v_regs(buf, t, false);
   };
 
-  // LDS read offsets of this lane's operands: K chunk g4 + 4*ks of row
-  // krow(mt) sits at ka_row[mt] + 32*(ks ^ ka_hi[mt]) (the swizzle's low two
-  // bits act on g4, its high bits on ks); V^T reads add uniform offsets.
-  int ka_row[4], ka_hi[4];
+  // LDS read offsets of this lane's operands.  The K rows of M tile mt are
+  // krow0 + 4*(mt&1) + 32*(mt>>1) with krow0 = 8*(j>>2) + (j&3); the
+  // swizzle f depends only on row bits 0, 1, 3 and 4, i.e. on j alone, so
+  // chunk g4 + 4*ks of every M tile sits at ka[ks] plus a fixed offset
+  // (the swizzle's low two bits act on g4, its high bits on ks).  V^T reads
+  // add uniform offsets to va_off.
+  int ka[KS];
+  {
+    const int krow0 = 8 * (j >> 2) + (j & 3);
+    const int f = k_swz<D>(krow0);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int krow = 32 * (mt >> 1) + 8 * (j >> 2) + 4 * (mt & 1) + (j & 3);
-    const int f = k_swz<D>(krow);
-    ka_row[mt] = krow * k_pitch<D>() + 8 * (g4 ^ (f & 3));
-    ka_hi[mt] = f >> 2;
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = krow0 * k_pitch<D>() + 8 * (g4 ^ (f & 3)) + 32 * (ks ^ (f >> 2));
   }
   const int va_off = v_lds(j, g4);
 
-  // ---- one tile of keys, in three parts: scores S^T = K Q^T (masked on
-  // tiles that cross the diagonal or the band edge), probabilities against
-  // the current reference m_run, and O^T += V^T P^T.
-  struct Scores { f32x4 v[4][NT]; };
-  auto scores = [&](int buf, int64_t k0, auto masked) {
-    Scores S;
+  // ---- the parts of a unit of 32 keys (half a tile; key half h of tile t
+  // holds keys 64t + 32h + [0, 32)): scores S^T = K Q^T (masked on units
+  // that cross the diagonal or the band edge), probabilities against the
+  // current reference m_run, and O^T += V^T P^T.
+  struct Scores { f32x4 v[2][NT]; };
+  auto scores = [&](Scores& S, int buf, int h) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) S.v[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NT; ++n) S.v[mm][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 A = ld16(&Ks[buf][ka_row[mt] + 32 * (ks ^ ka_hi[mt])]);
+      for (int mm = 0; mm < 2; ++mm) {
+        const int mt = 2 * h + mm;
+        const u32x4 A = ld16(&Ks[buf][ka[ks] + k_pitch<D>() * (4 * (mt & 1) + 32 * (mt >> 1))]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) S.v[mt][n] = mfma16x16x32(A, qop[n][ks], S.v[mt][n]);
+        for (int n = 0; n < NT; ++n) S.v[mm][n] = mfma16x16x32(A, qop[n][ks], S.v[mm][n]);
       }
     }
-    // lane (j, g4) holds, for M tile mt and element r, the score of key
-    // k0 + 32*(mt>>1) + 8*g4 + 4*(mt&1) + r.
-    if constexpr (decltype(masked)::value) {
+  };
+  // Lane (j, g4) holds, for M tile mm and element r, the score of key
+  // k0h + 8*g4 + 4*mm + r; keys after the query or outside its band get -inf.
+  auto apply_mask = [&](Scores& S, int k0h) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int rel0 = (int)(k0 - (a.q_offset + tpos[n]));   // key - p at (mt, r) = 0
+    for (int n = 0; n < NT; ++n) {
+      const int rel0 = k0h + 8 * g4 - ((int)a.q_offset + tpos[n]);   // key - p at (mm, r) = 0
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int rel = rel0 + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1) + r;
-            const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
-            if (!ok) S.v[mt][n][r] = -INFINITY;
-          }
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int rel = rel0 + 4 * mm + r;
+          const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
+          S.v[mm][n][r] = ok ? S.v[mm][n][r] : -INFINITY;
+        }
     }
-    return S;
   };
   // p = 2^(s*scale - m_run), rounded to bf16 once; ls = this lane's sum of
   // those rounded values (v_dot2 against 1).
-  auto probs = [&](const Scores& S, u32x4 (&Pk)[2][NT], float (&ls)[NT]) {
+  auto probs = [&](const Scores& S, u32x4 (&Pk)[NT], float (&ls)[NT]) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
       float acc = 0.f;
+      uint32_t w[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e = 2 * e2;
-          const float p0 = fast_exp2(fmaf(S.v[2 * h + (e >> 2)][n][e & 3], scale, -m_use));
-          const float p1 = fast_exp2(fmaf(S.v[2 * h + ((e + 1) >> 2)][n][(e + 1) & 3], scale, -m_use));
-          w[e2] = pack_bf16x2(p0, p1);
-          acc = sum_bf16x2(w[e2], acc);
-        }
-        Pk[h][n] = u32x4{w[0], w[1], w[2], w[3]};
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float p0 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1)], scale, -m_use));
+        const float p1 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1) + 1], scale, -m_use));
+        w[e2] = pack_bf16x2(p0, p1);
+        acc = sum_bf16x2(w[e2], acc);
       }
+      Pk[n] = u32x4{w[0], w[1], w[2], w[3]};
       ls[n] = acc;
     }
   };
-  auto pv = [&](int buf, const u32x4 (&Pk)[2][NT]) {
+  auto pv = [&](int buf, int h, const u32x4 (&Pk)[NT]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * 32]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * 32]);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[h][n], O[dt][n]);
-      }
+      for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[n], O[dt][n]);
+    }
   };
   // Move the reference to the true running max (column max across the four
   // lanes of a query) and rescale what has been accumulated.
@@ -291,9 +324,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int n = 0; n < NT; ++n) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S.v[mt][n][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S.v[mm][n][r]);
       const float m_new = fmaxf(m_run[n], max_over_col(mx) * scale);
       // m_run == -inf: nothing accumulated yet (and m_new may be -inf too)
       const float alpha = (m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
@@ -303,60 +336,103 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       m_run[n] = m_new;
     }
   };
+  // Does the unit starting at key k0h need masking?
+  auto need_mask = [&](int k0h) {
+    return (k0h + 31 > P_min) || (a.window > 0 && k0h < P_max - a.window + 1);
+  };
 
-  load_tile(t_first);
-  store_tile(0);
+  // ---- software pipeline over units.  Unit u computes S(u+1) and
+  // O += V(u-1) P(u-1) on the matrix cores while the vector units turn S(u)
+  // into P(u), all in one stretch of straight-line code.  Tile t (units 2t
+  // and 2t+1) first starts the loads of K(t+2) and V(t+1) into LDS and ends
+  // with one barrier.  K and V have three LDS buffers each; with
+  // (b0, b1, b2) rotating one place per tile, K(t), K(t+1), K(t+2) sit in
+  // b0, b1, b2 and V(t-1), V(t), V(t+1) in b2, b0, b1.  After each unit,
+  // P(u) is checked: the reference m_run stays put while every lane's unit
+  // sum stays below 2^64 (so no exponential, partial sum or accumulator
+  // comes near fp32/bf16 overflow); a unit that breaks that, or a query with
+  // no reference yet (no sink and nothing seen), recomputes S(u) from K (still
+  // in LDS), moves the reference to the running max, rescales O (which then
+  // holds units up to u-1) and recomputes P(u).
+  const int t0 = t_first;
+  int b0 = 0, b1 = 1, b2 = 2;
+  load_k(0, t0);
+  if (t0 + 1 <= t_last) load_k(1, t0 + 1);
+  load_v(0, t0);
+  store_v_regs(2, t0, true);     // "V(t0-1)", multiplied by P = 0 in unit 2*t0
+  wait_vmem();
   __syncthreads();
+  Scores S0, S1;
+  u32x4 P0[NT], P1[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) P1[n] = u32x4{0, 0, 0, 0};
+  scores(S0, 0, 0);
+  if (need_mask(t0 * kTile)) apply_mask(S0, t0 * kTile);
 
-  // Steady state: the reference m_run stays put while every lane's tile sum
-  // stays below 2^64 (so no exponential, partial sum or accumulator can come
-  // near fp32/bf16 overflow); a tile that breaks that, or a query with no
-  // reference yet (no sink and nothing seen), leaves the loop for the slow
-  // path, which moves the reference, redoes that tile and comes back.  The
-  // fast loop never rewrites O outside the matrix cores.
-  int buf = 0;
-  int64_t t = t_first;
-  for (;;) {
-    bool slow = false;
-    Scores S;
-    u32x4 Pk[2][NT];
-    float ls[NT];
-    for (; t <= t_last; ++t) {
-      const bool more = t < t_last;
-      if (more) load_tile(t + 1);
-      const int64_t k0 = t * kTile;
-      const bool need_mask = (k0 + kTile - 1 > P_min) ||
-                             (a.window > 0 && k0 < P_max - a.window + 1);
-      if (need_mask)
-        S = scores(buf, k0, std::true_type{});
-      else
-        S = scores(buf, k0, std::false_type{});
-      probs(S, Pk, ls);
-      bool bad = false;
+  // Instruction order of a unit's main stretch: a few operand reads ahead,
+  // then each pair of MFMAs with one more operand read and its share of the
+  // softmax's vector work, so that the matrix cores and the vector units
+  // work side by side and only a few operands are in flight.
+  auto interleave = [&]() {
+    if constexpr (!SA_INTERLEAVE) return;
+    constexpr int kMf = 2 * KS * NT + DT * NT;            // MFMAs per unit
+    constexpr int kValu = (NT * 26 + kMf / 2 - 1) / (kMf / 2);
+    sched_group<0x100, SA_RD_AHEAD>();          // LDS reads
 #pragma unroll
-      for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || m_run[n] == -INFINITY;
-      if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-        slow = true;
-        break;
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
-      pv(buf, Pk);
-      if (more) store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+    for (int i = 0; i < kMf / 2; ++i) {
+      sched_group<0x100, 1>();
+      sched_group<0x008, 2>();                  // MFMA
+      sched_group<0x002, kValu>();              // VALU
     }
-    if (!slow) break;
-    rescale(S);
-    probs(S, Pk, ls);
+  };
+  // One unit: Sc = S(u) in, Sn = S(u+1) out (from K buffer kbn, half hn,
+  // first key k0n); Pp = P(u-1) in (V buffer vbp, half hp), Pc = P(u) out;
+  // S(u) can be recomputed from K buffer kbc, half hc, first key k0c.  The
+  // mask of S(u+1), where it needs one, is applied in place after the main
+  // stretch.
+  auto unit = [&](const Scores& Sc, Scores& Sn, const u32x4 (&Pp)[NT], u32x4 (&Pc)[NT],
+                  int kbn, int hn, int k0n, int vbp, int hp, int kbc, int hc, int k0c,
+                  bool mask_next) {
+    float ls[NT];
+    scores(Sn, kbn, hn);
+    pv(vbp, hp, Pp);
+    probs(Sc, Pc, ls);
+    interleave();
+    bool bad = false;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || m_run[n] == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      // The compiler may not hoist this recomputation onto the fast path
+      // (LDS reads can be speculated): the clobber pins it here.
+      asm volatile("" ::: "memory");
+      Scores Sr;
+      scores(Sr, kbc, hc);
+      if (need_mask(k0c)) apply_mask(Sr, k0c);
+      rescale(Sr);
+      probs(Sr, Pc, ls);
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
-    pv(buf, Pk);
-    if (t < t_last) store_tile(buf ^ 1);
+    if (mask_next) apply_mask(Sn, k0n);
+  };
+  for (int t = t0; t <= t_last; ++t) {
+    if (t + 2 <= t_last) load_k(b2, t + 2);
+    if (t + 1 <= t_last) load_v(b1, t + 1);
+    const int k0 = t * kTile;
+    // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1
+    unit(S0, S1, P1, P0, b0, 1, k0 + 32, b2, 1, b0, 0, k0, need_mask(k0 + 32));
+    // unit 2t+1: S(2t+2) from K(t+1) half 0 (a throw-away after the last
+    // tile); P(2t) with V(t) half 0
+    unit(S1, S0, P0, P1, b1, 0, k0 + kTile, b0, 0, b0, 1, k0 + 32,
+         t < t_last && need_mask(k0 + kTile));
+    wait_vmem();
     __syncthreads();
-    buf ^= 1;
-    ++t;
+    const int k = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = k;
   }
+  pv(b2, 1, P1);                 // P(2 t_last + 1) with V(t_last) half 1
 
   // ---- normalise and store: lane holds O^T[16*dt + 4*g4 + r][query]
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
@@ -396,19 +472,19 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 #define SA_PF64 2, 4
 #endif
 #ifndef SA_PF96
-#define SA_PF96 2, 8
+#define SA_PF96 2, 4
 #endif
 #ifndef SA_PF128
-#define SA_PF128 2, 4
+#define SA_PF128 2, 8
 #endif
 #ifndef SA_PFB64
 #define SA_PFB64 2, 4
 #endif
 #ifndef SA_PFB96
-#define SA_PFB96 2, 8
+#define SA_PFB96 2, 4
 #endif
 #ifndef SA_PFB128
-#define SA_PFB128 2, 4
+#define SA_PFB128 2, 8
 #endif
 constexpr int kBandWindowMax = 512;   // windows up to this use the band shape
 
