@@ -167,8 +167,9 @@ int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap);
  *   out = sum_{j in A} e^{l_j} V_j / (e^{sigma_h} + sum_{j in A} e^{l_j}).
  * Requires q_offset + T_q <= kv_cache_offset(c) (append first); n_kv and
  * d_h must equal the cache's.  bf16: d_h in {64, 96, 128},
- * n_q/n_kv <= 128, matrix-core kernel with fp32 accumulation; fp32: d_h % 8
- * == 0, d_h <= 256, vector kernel. */
+ * n_q/n_kv <= 128, cache capacity below 2^31 rows (SA_ERR_SHAPE otherwise),
+ * matrix-core kernel with fp32 accumulation; fp32: d_h % 8 == 0,
+ * d_h <= 256, vector kernel. */
 int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks,
                      void* out, int B, int T_q, int n_q, int n_kv, int d_h,
                      int window, float sm_scale, int64_t q_offset,

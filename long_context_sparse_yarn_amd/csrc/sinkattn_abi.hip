@@ -262,6 +262,8 @@ int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks, vo
     if (d_h != 64 && d_h != 96 && d_h != 128)
       return fail(SA_ERR_SHAPE, "bf16 attention supports d_h in {64, 96, 128}, got %d", d_h);
     if (q_mult > 128) return fail(SA_ERR_SHAPE, "n_q/n_kv must be <= 128");
+    if (c->capacity > INT32_MAX)   // the kernel keeps key positions in 32 bits
+      return fail(SA_ERR_SHAPE, "bf16 prefill needs a capacity below 2^31 rows");
   }
   if ((int64_t)B * T_q * n_q > INT32_MAX) return fail(SA_ERR_ARG, "B*T_q*n_q too large");
   if (T_q == 0) return ok();

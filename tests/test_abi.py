@@ -121,6 +121,12 @@ def test_errors_are_reported_before_any_launch():
     assert st == SA_OK
     assert P(q, h80, s, o, 2, 5, 8, 2, 80, 0, 0.125, 0, None) == SA_ERR_SHAPE
     B._kv_cache_destroy(h80)
+    # bf16 prefill keeps key positions in 32 bits: a 2^31-row cache is refused
+    st, hbig = create(Bn=1, C=(1 << 31), n_kv=2, d=64, offset=10)
+    assert st == SA_OK
+    assert P(q, hbig, s, o, 1, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE
+    assert "2^31" in sa.last_error()
+    B._kv_cache_destroy(hbig)
     # rope
     y = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
     R = B._yarn_rope_apply
