@@ -20,6 +20,7 @@ Extra objects on the same JSON line:
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,8 +35,16 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
 # valid only for the kernel sources it was measured on.
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "66b90877f1d3a2e4", "bytes": (33363 * 2 + 34701) * 1024}
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "d58f5a7774a44747", "bytes": (31426 * 2 + 24576) * 1024}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_kernels.h")
+
+
+def prefill_kernel_name(d, band):
+    """Template instance the library launches for head dim d (tile shape from
+    the SA_PF* / SA_PFB* defaults in prefill.hip)."""
+    src = open(os.path.join(ROOT, "long_context_sparse_yarn_amd", "csrc", "prefill.hip")).read()
+    m = re.search(r"#define SA_PF%s%d (\d+), (\d+)" % ("B" if band else "", d), src)
+    return "prefill_bf16_kernel<%d,%s,%s>" % (d, m.group(1), m.group(2)) if m else "prefill_bf16_kernel<%d>" % d
 
 
 def kernel_sources_hash():
@@ -290,7 +299,7 @@ def main():
                             if kernel_sources_hash() == TRAFFIC_FULL_PREFILL["sources_sha256_16"]
                             else None),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
-                "kernel": "prefill_bf16_kernel<96,2,8> (full causal)",
+                "kernel": prefill_kernel_name(w.d_h, False) + " (full causal)",
                 "kernel_ms": round(kern_ms[full_i], 4)}
     line = {
         "metric": "sink-GQA attention prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
