@@ -93,7 +93,7 @@ class Layer:
         self.host = x
         self.window = w.windows[layer]
         self.q0, self.k0, self.v = up(x["q"]), up(x["k"]), up(x["v"])
-        self.qw, self.kw = torch.empty_like(self.q0), torch.empty_like(self.k0)
+        self.qw = torch.empty_like(self.q0)
         self.sinks = torch.from_numpy(x["sinks"]).cuda()
         self.cache = sa.KVCache.empty(w.B, w.capacity, w.n_kv, w.d_h, dtype=dt)
         if w.prefix:
@@ -108,8 +108,7 @@ def run_layer(L, w, sa, ev=None):
     L.cache.restore(L.snap)
     o = L.cache.offset
     sa.yarn_rope_apply(L.q0, o, L.yarn, out=L.qw)      # raw -> rotated, out of place
-    sa.yarn_rope_apply(L.k0, o, L.yarn, out=L.kw)
-    L.cache.append(L.kw, L.v)
+    L.cache.append_rope(L.k0, L.v, L.yarn)               # K rotated at rows o.. as it is appended
     if ev is not None:
         ev[0].record()
     sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, o, out=L.out)
@@ -172,14 +171,12 @@ def decode_extra(sa, torch, steps_warm=4):
         ws = sa.decode_workspace(cache, w.n_q)
         snap = cache.snapshot()
         qbuf = torch.empty_like(toks[0]["q"])
-        kbuf = torch.empty_like(toks[0]["k"])
         out = torch.empty_like(qbuf)
 
         def step(s, ev=None):
             o = cache.offset
             sa.yarn_rope_apply(toks[s]["q"], o, y, out=qbuf)
-            sa.yarn_rope_apply(toks[s]["k"], o, y, out=kbuf)
-            cache.append(kbuf, toks[s]["v"])
+            cache.append_rope(toks[s]["k"], toks[s]["v"], y)
             if ev is not None:
                 ev[0].record()
             sa.sinkattn_decode(qbuf, cache, sinks, W, w.sm_scale, workspace=ws, out=out)

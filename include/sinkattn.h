@@ -146,6 +146,18 @@ int64_t kv_cache_offset(const sa_kv_cache* c);
 int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v,
                     int T_new, void* stream);
 
+/* Rotate and append in one pass ("MoE-Xtend" README, ROPE + SCALING and KV
+ * CACHE; DESIGN CONTRACTS: a row's position is its global index, so K row
+ * t goes to cache row offset + t rotated at that position).  k: device
+ * [B, T_new, n_kv, d_h], unrotated; v as for kv_cache_append; y: YaRN
+ * parameters with y->d_h == d_h.  The cache receives exactly the bits that
+ * yarn_rope(k, offset = kv_cache_offset(c)) followed by kv_cache_append
+ * would write, without the intermediate buffer.  bf16 needs d_h % 16 == 0
+ * (SA_ERR_SHAPE otherwise); other errors as for kv_cache_append and
+ * yarn_rope. */
+int kv_cache_append_rope(sa_kv_cache* c, const void* k, const void* v,
+                         int T_new, const sa_yarn* y, void* stream);
+
 /* O(1) host bookkeeping ("prefill once, decode many").  A snapshot records
  * the offset; restore rewinds the offset to it.  Restoring is refused with
  * SA_ERR_SNAPSHOT if the snapshot belongs to another cache or if any append

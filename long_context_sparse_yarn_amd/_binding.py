@@ -62,6 +62,8 @@ _kv_cache_create = _sig("kv_cache_create", _i32, ctypes.POINTER(_vp), _vp, _vp, 
 _kv_cache_destroy = _sig("kv_cache_destroy", _i32, _vp)
 _kv_cache_offset = _sig("kv_cache_offset", _i64, _vp)
 _kv_cache_append = _sig("kv_cache_append", _i32, _vp, _vp, _vp, _i32, _vp)
+_kv_cache_append_rope = _sig("kv_cache_append_rope", _i32, _vp, _vp, _vp, _i32,
+                             ctypes.POINTER(SaYarn), _vp)
 _kv_cache_snapshot = _sig("kv_cache_snapshot", _i32, _vp, ctypes.POINTER(SaSnapshot))
 _kv_cache_restore = _sig("kv_cache_restore", _i32, _vp, ctypes.POINTER(SaSnapshot))
 _sinkattn_prefill = _sig("sinkattn_prefill", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -215,6 +217,19 @@ class KVCache:
             raise ValueError("shape differs from the cache's")
         _check(_kv_cache_append(self._h, _dev(k_rot, "k_rot"), _dev(v, "v"),
                                 int(k_rot.shape[1]), _stream(stream)))
+
+    def append_rope(self, k: torch.Tensor, v: torch.Tensor, y: "Yarn", stream=None) -> None:
+        """kv_cache_append_rope: rotate the unrotated K rows at their cache
+        positions (offset + t) and append them with V in one pass."""
+        if k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k and v must both be [B, T_new, n_kv, d]")
+        if k.dtype != self.dtype or v.dtype != self.dtype:
+            raise TypeError("dtype differs from the cache's")
+        if (k.shape[0], k.shape[2], k.shape[3]) != (self.B, self.n_kv, self.d):
+            raise ValueError("shape differs from the cache's")
+        ys = y.c_struct()
+        _check(_kv_cache_append_rope(self._h, _dev(k, "k"), _dev(v, "v"), int(k.shape[1]),
+                                     ctypes.byref(ys), _stream(stream)))
 
     def snapshot(self) -> SaSnapshot:
         s = SaSnapshot()

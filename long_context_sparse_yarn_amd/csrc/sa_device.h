@@ -47,15 +47,16 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
 // when it lands on one (low 16 bits 0x8000) without being exact, the fp64
 // value says which side it came from and the bf16 rounding goes that way.
 // Otherwise rounding the fp32 value to bf16 to nearest even is exact.
+// Both candidates are computed and one is selected, so a wave takes no
+// branch per element.
 __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   const float t = (float)x;
-  uint32_t u = __float_as_uint(t);
-  if ((u & 0xFFFFu) == 0x8000u && (double)t != x) {
-    const bool away = fabs(x) > fabs((double)t);
-    return (away ? u + 0x8000u : u) >> 16;
-  }
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t nearest = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const double td = (double)t;
+  const uint32_t side = (fabs(x) > fabs(td) ? u + 0x8000u : u) >> 16;
+  const bool on_mid = ((u & 0xFFFFu) == 0x8000u) & (td != x);
+  return on_mid ? side : nearest;
 }
 
 // ---------------------------------------------------------------- loads

@@ -28,6 +28,13 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s);
 
+struct AppendRopeArgs {  // rotate K rows at their cache positions, then append
+  AppendArgs ap;         // k_src holds unrotated rows
+  double conc;
+  double inv_freq[SA_MAX_HALF];
+};
+hipError_t launch_append_rope(const AppendRopeArgs& a, int elt_bytes, hipStream_t s);
+
 struct AttnArgs {
   const void* q;        // [B, T_q, n_q, d]
   const void* kc;       // [B, C, n_kv, d]

@@ -187,30 +187,59 @@ int kv_cache_destroy(sa_kv_cache* c) {
 
 int64_t kv_cache_offset(const sa_kv_cache* c) { return c ? c->offset : -1; }
 
-int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v, int T_new, void* stream) {
-  if (!c || !k_rot || !v) return fail(SA_ERR_ARG, "null argument");
-  if (misaligned(k_rot) || misaligned(v)) return fail(SA_ERR_ARG, "k_rot and v must be 16-byte aligned");
+namespace {
+// Checks shared by the append entry points; fills the launch arguments.
+int append_args(sa_kv_cache* c, const void* k, const void* v, int T_new, AppendArgs* a) {
+  if (!c || !k || !v) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(k) || misaligned(v)) return fail(SA_ERR_ARG, "k and v must be 16-byte aligned");
   if (T_new <= 0) return fail(SA_ERR_ARG, "T_new must be positive");
   if (c->offset + T_new > c->capacity)
     return fail(SA_ERR_CAPACITY, "append of %d rows at offset %lld exceeds capacity %lld", T_new,
                 (long long)c->offset, (long long)c->capacity);
-  AppendArgs a;
-  a.k_src = k_rot;
-  a.v_src = v;
-  a.kc = c->k;
-  a.vc = c->v;
-  a.B = c->B;
-  a.T_new = T_new;
-  a.n_kv = c->n_kv;
-  a.d = c->d_h;
-  a.C = c->capacity;
-  a.o = c->offset;
-  hipError_t e = launch_append(a, elt_bytes(c->dtype), (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  a->k_src = k;
+  a->v_src = v;
+  a->kc = c->k;
+  a->vc = c->v;
+  a->B = c->B;
+  a->T_new = T_new;
+  a->n_kv = c->n_kv;
+  a->d = c->d_h;
+  a->C = c->capacity;
+  a->o = c->offset;
+  return SA_OK;
+}
+// Bookkeeping after an append of T_new rows was enqueued.
+void appended(sa_kv_cache* c, int T_new) {
   c->stamp += 1;
   if (c->offset < c->high_water) c->rewrites.emplace_back(c->stamp, c->offset);
   c->offset += T_new;
   if (c->offset > c->high_water) c->high_water = c->offset;
+}
+}  // namespace
+
+int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v, int T_new, void* stream) {
+  AppendArgs a;
+  int st = append_args(c, k_rot, v, T_new, &a);
+  if (st != SA_OK) return st;
+  hipError_t e = launch_append(a, elt_bytes(c->dtype), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  appended(c, T_new);
+  return ok();
+}
+
+int kv_cache_append_rope(sa_kv_cache* c, const void* k, const void* v, int T_new, const sa_yarn* y,
+                         void* stream) {
+  AppendRopeArgs a;
+  memset(&a, 0, sizeof a);
+  int st = append_args(c, k, v, T_new, &a.ap);
+  if (st != SA_OK) return st;
+  if (c->dtype == SA_BF16 && c->d_h % 16)
+    return fail(SA_ERR_SHAPE, "bf16 rotate-and-append needs d_h %% 16 == 0, got %d", c->d_h);
+  st = yarn_table(y, c->d_h, a.inv_freq, &a.conc);
+  if (st != SA_OK) return st;
+  hipError_t e = launch_append_rope(a, elt_bytes(c->dtype), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  appended(c, T_new);
   return ok();
 }
 

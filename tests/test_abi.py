@@ -127,6 +127,21 @@ def test_errors_are_reported_before_any_launch():
     assert P(q, hbig, s, o, 1, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE
     assert "2^31" in sa.last_error()
     B._kv_cache_destroy(hbig)
+    # rotate-and-append: yarn checks, bf16 head dim, capacity, nothing launched
+    AR = B._kv_cache_append_rope
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    y64 = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
+    y96 = B.SaYarn(96, 150000.0, 32.0, 4096, 1.0, 32.0)
+    assert AR(h, q, q, 4, None, None) == SA_ERR_ARG                         # no yarn
+    assert AR(h, q, q, 4, ctypes.byref(y96), None) == SA_ERR_SHAPE           # yarn d_h differs
+    assert AR(h, q, q, 247, ctypes.byref(y64), None) == SA_ERR_CAPACITY
+    assert AR(h, ctypes.c_void_p(0x30008), q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert B._kv_cache_offset(h) == 10
+    B._kv_cache_destroy(h)
+    st, h24 = create(d=24, offset=10)
+    y24 = B.SaYarn(24, 150000.0, 32.0, 4096, 1.0, 32.0)
+    assert AR(h24, q, q, 4, ctypes.byref(y24), None) == SA_ERR_SHAPE         # bf16 needs d % 16
+    B._kv_cache_destroy(h24)
     # rope
     y = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
     R = B._yarn_rope_apply

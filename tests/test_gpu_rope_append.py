@@ -24,6 +24,9 @@ ROPE_CASES = [
     (1, 128, 8, 64, 0, Yarn(base=10000.0, factor=1.0)),   # plain RoPE
     (2, 9, 64, 64, 131135, Yarn()),
     (1, 3, 3, 8, 7, Yarn()),
+    (1, 5, 64, 128, 5, Yarn(base=500000.0, factor=8.0, orig_ctx=8192)),   # 2 tasks per thread
+    (1, 3, 128, 128, 100, Yarn(base=500000.0, factor=8.0, orig_ctx=8192)),  # 4 tasks per thread
+    (1, 20000, 1, 64, 3, Yarn()),        # more row blocks than workgroups: each loops
 ]
 
 
@@ -143,3 +146,54 @@ def test_append_capacity_and_restore_on_device():
         cache.append(dev(np.zeros((1, 60, 1, 64), np.float32), "bf16"),
                      dev(np.zeros((1, 60, 1, 64), np.float32), "bf16"))
     assert e.value.status == -4 and cache.offset == 10
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,C,n_kv,d,o0,chunks", [
+    (2, 256, 2, 64, 0, [5, 1, 40, 1, 90]),
+    (1, 4096, 4, 96, 0, [4000]),               # GPT-OSS-Lite K shape, many full blocks
+    (3, 192, 1, 128, 7, [64, 33]),
+    (1, 160, 16, 64, 3, [1] * 9 + [100]),      # several head groups per block
+    (2, 128, 8, 96, 31, [2, 60]),
+])
+def test_append_rope_equals_rope_then_append(dtype, B, C, n_kv, d, o0, chunks):
+    """kv_cache_append_rope writes the bits of yarn_rope + kv_cache_append,
+    rows outside the appended range keep theirs, and K matches the oracle."""
+    y = Yarn()
+    ly = lib_yarn(d, y)
+    fused = _sentinel_cache(B, C, n_kv, d, dtype)
+    ref = _sentinel_cache(B, C, n_kv, d, dtype)
+    rng = np.random.default_rng(C * 7 + d + n_kv)
+    pre = rng.standard_normal((B, o0, n_kv, d)).astype(np.float32) if o0 else None
+    if o0:
+        fused.append(dev(pre, dtype), dev(pre, dtype))
+        ref.append(dev(pre, dtype), dev(pre, dtype))
+    ks = []
+    for T in chunks:
+        k = rng.standard_normal((B, T, n_kv, d)).astype(np.float32)
+        v = rng.standard_normal((B, T, n_kv, d)).astype(np.float32)
+        if dtype == "bf16":
+            k = (k.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+            v = (v.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+        o = ref.offset
+        kd, vd = dev(k, dtype), dev(v, dtype)
+        kr = torch.empty_like(kd)
+        sa.yarn_rope_apply(kd, o, ly, out=kr)
+        ref.append(kr, vd)
+        fused.append_rope(kd, vd, ly)
+        assert fused.offset == ref.offset == o + T
+        ks.append((o, k))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits_t(fused.k), _bits_t(ref.k))
+    assert torch.equal(_bits_t(fused.v), _bits_t(ref.v))
+    # K against the oracle rotation (one ulp where the two fp64 evaluations straddle a tie)
+    kb = _bits(fused.k)
+    for o, k in ks:
+        want = oracle_rot(k, o, d, y, dtype)
+        got = kb[:, o:o + k.shape[1]]
+        ulp = np.abs(got - _bits(torch.from_numpy(want).to(TORCH_DT[dtype])))
+        assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+
+
+def _bits_t(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
