@@ -40,11 +40,13 @@ KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_kernels.h")
 
 
 def prefill_kernel_name(d, band):
-    """Template instance the library launches for head dim d (tile shape from
-    the SA_PF* / SA_PFB* defaults in prefill.hip)."""
+    """Template instance sinkattn_prefill launches for head dim d (tile shape
+    from the SA_PF* / SA_PFB* defaults in prefill.hip; `false`: Q arrives
+    rotated)."""
     src = open(os.path.join(ROOT, "long_context_sparse_yarn_amd", "csrc", "prefill.hip")).read()
     m = re.search(r"#define SA_PF%s%d (\d+), (\d+)" % ("B" if band else "", d), src)
-    return "prefill_bf16_kernel<%d,%s,%s>" % (d, m.group(1), m.group(2)) if m else "prefill_bf16_kernel<%d>" % d
+    return ("prefill_bf16_kernel<%d,%s,%s,false>" % (d, m.group(1), m.group(2)) if m
+            else "prefill_bf16_kernel<%d>" % d)
 
 
 def kernel_sources_hash():
@@ -107,8 +109,8 @@ class Layer:
 def run_layer(L, w, sa, ev=None):
     L.cache.restore(L.snap)
     o = L.cache.offset
-    sa.yarn_rope_apply(L.q0, o, L.yarn, out=L.qw)      # raw -> rotated, out of place
-    L.cache.append_rope(L.k0, L.v, L.yarn)               # K rotated at rows o.. as it is appended
+    # Q rotated into qw and K into the cache at positions o.., V appended: one pass
+    L.cache.append_rope_qk(L.q0, L.k0, L.v, L.yarn, q_out=L.qw)
     if ev is not None:
         ev[0].record()
     sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, o, out=L.out)
@@ -174,9 +176,7 @@ def decode_extra(sa, torch, steps_warm=4):
         out = torch.empty_like(qbuf)
 
         def step(s, ev=None):
-            o = cache.offset
-            sa.yarn_rope_apply(toks[s]["q"], o, y, out=qbuf)
-            cache.append_rope(toks[s]["k"], toks[s]["v"], y)
+            cache.append_rope_qk(toks[s]["q"], toks[s]["k"], toks[s]["v"], y, q_out=qbuf)
             if ev is not None:
                 ev[0].record()
             sa.sinkattn_decode(qbuf, cache, sinks, W, w.sm_scale, workspace=ws, out=out)

@@ -158,6 +158,16 @@ int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v,
 int kv_cache_append_rope(sa_kv_cache* c, const void* k, const void* v,
                          int T_new, const sa_yarn* y, void* stream);
 
+/* kv_cache_append_rope that also rotates the layer's queries, which sit at
+ * the same positions: q (device [B, T_new, n_q, d_h], unrotated) is written
+ * rotated to q_rot (same shape; q_rot == q rotates in place, any other
+ * overlap is SA_ERR_ARG), exactly as yarn_rope(q, q_rot, offset =
+ * kv_cache_offset(c)) would, sharing the angle tables with K.  q and q_rot
+ * both null: same as kv_cache_append_rope. */
+int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q,
+                            const void* k, const void* v, int T_new,
+                            const sa_yarn* y, void* stream);
+
 /* O(1) host bookkeeping ("prefill once, decode many").  A snapshot records
  * the offset; restore rewinds the offset to it.  Restoring is refused with
  * SA_ERR_SNAPSHOT if the snapshot belongs to another cache or if any append
@@ -186,6 +196,17 @@ int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks,
                      void* out, int B, int T_q, int n_q, int n_kv, int d_h,
                      int window, float sm_scale, int64_t q_offset,
                      void* stream);
+
+/* sinkattn_prefill with unrotated queries: q holds raw rows and the kernel
+ * rotates each one at its position q_offset + t ("MoE-Xtend" README, ROPE +
+ * SCALING) before attending, with yarn_rope's arithmetic, so the result is
+ * exactly that of yarn_rope(q, q_offset) followed by sinkattn_prefill, without
+ * the rotated copy of Q.  y: YaRN parameters with y->d_h == d_h.  bf16
+ * caches only (SA_ERR_DTYPE otherwise); other errors as sinkattn_prefill. */
+int sinkattn_prefill_rope(const void* q, const sa_kv_cache* c, const float* sinks,
+                          void* out, int B, int T_q, int n_q, int n_kv, int d_h,
+                          int window, float sm_scale, int64_t q_offset,
+                          const sa_yarn* y, void* stream);
 
 /* Bytes of fp32 workspace that sinkattn_decode needs for any cache offset up
  * to `capacity` with these shapes (0 on invalid arguments). */

@@ -64,10 +64,14 @@ _kv_cache_offset = _sig("kv_cache_offset", _i64, _vp)
 _kv_cache_append = _sig("kv_cache_append", _i32, _vp, _vp, _vp, _i32, _vp)
 _kv_cache_append_rope = _sig("kv_cache_append_rope", _i32, _vp, _vp, _vp, _i32,
                              ctypes.POINTER(SaYarn), _vp)
+_kv_cache_append_rope_qk = _sig("kv_cache_append_rope_qk", _i32, _vp, _vp, _vp, _i32, _vp, _vp,
+                                _i32, ctypes.POINTER(SaYarn), _vp)
 _kv_cache_snapshot = _sig("kv_cache_snapshot", _i32, _vp, ctypes.POINTER(SaSnapshot))
 _kv_cache_restore = _sig("kv_cache_restore", _i32, _vp, ctypes.POINTER(SaSnapshot))
 _sinkattn_prefill = _sig("sinkattn_prefill", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                          _i32, _i32, _f32, _i64, _vp)
+_sinkattn_prefill_rope = _sig("sinkattn_prefill_rope", _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                              _i32, _i32, _i32, _i32, _f32, _i64, ctypes.POINTER(SaYarn), _vp)
 _sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
 _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                         _i32, _f32, _vp, _sz, _vp)
@@ -231,6 +235,29 @@ class KVCache:
         _check(_kv_cache_append_rope(self._h, _dev(k, "k"), _dev(v, "v"), int(k.shape[1]),
                                      ctypes.byref(ys), _stream(stream)))
 
+    def append_rope_qk(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, y: "Yarn",
+                       q_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """kv_cache_append_rope_qk: append_rope that also rotates q [B, T_new,
+        n_q, d] at the same positions into q_out (default: a new tensor;
+        q_out is q rotates in place); returns q_out."""
+        if k.shape != v.shape or k.dim() != 4 or q.dim() != 4:
+            raise ValueError("q, k and v must be [B, T_new, heads, d] with k and v alike")
+        if q.dtype != self.dtype or k.dtype != self.dtype or v.dtype != self.dtype:
+            raise TypeError("dtype differs from the cache's")
+        if (k.shape[0], k.shape[2], k.shape[3]) != (self.B, self.n_kv, self.d):
+            raise ValueError("shape differs from the cache's")
+        if (q.shape[0], q.shape[1], q.shape[3]) != (k.shape[0], k.shape[1], k.shape[3]):
+            raise ValueError("q must be [B, T_new, n_q, d] like k")
+        if q_out is None:
+            q_out = torch.empty_like(q)
+        elif q_out.shape != q.shape or q_out.dtype != q.dtype:
+            raise ValueError("q_out must match q")
+        ys = y.c_struct()
+        _check(_kv_cache_append_rope_qk(self._h, _dev(q, "q"), _dev(q_out, "q_out"),
+                                        int(q.shape[2]), _dev(k, "k"), _dev(v, "v"),
+                                        int(k.shape[1]), ctypes.byref(ys), _stream(stream)))
+        return q_out
+
     def snapshot(self) -> SaSnapshot:
         s = SaSnapshot()
         _check(_kv_cache_snapshot(self._h, ctypes.byref(s)))
@@ -268,6 +295,27 @@ def sinkattn_prefill(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, windo
     _check(_sinkattn_prefill(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"), _dev(out, "out"),
                              B, T_q, n_q, cache.n_kv, d, int(window), float(sm_scale),
                              int(q_offset), _stream(stream)))
+    return out
+
+
+def sinkattn_prefill_rope(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window: int,
+                          sm_scale: float, q_offset: int, y: Yarn,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sinkattn_prefill with unrotated q: each query row is rotated at its
+    position q_offset + t inside the kernel (same bits as yarn_rope_apply
+    followed by sinkattn_prefill)."""
+    B, T_q, n_q, d = q.shape
+    if sinks.dtype != torch.float32 or sinks.numel() != n_q:
+        raise ValueError("sinks must be float32 [n_q]")
+    if q.dtype != cache.dtype:
+        raise TypeError("q dtype differs from the cache's")
+    if out is None:
+        out = torch.empty_like(q)
+    ys = y.c_struct()
+    _check(_sinkattn_prefill_rope(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"),
+                                  _dev(out, "out"), B, T_q, n_q, cache.n_kv, d, int(window),
+                                  float(sm_scale), int(q_offset), ctypes.byref(ys),
+                                  _stream(stream)))
     return out
 
 

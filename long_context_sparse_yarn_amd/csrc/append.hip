@@ -17,7 +17,9 @@
 // owns one (b, 32-key block, group of heads): it stages V through LDS as
 // above and builds the block's (c*cos, c*sin) table once in LDS for all its
 // heads; each thread then takes a (row, head, 8-pair chunk), loads both
-// halves of the chunk, and writes both rotated halves.
+// halves of the chunk, and writes both rotated halves.  Optionally the same
+// workgroups rotate the layer's Q rows, which sit at the same positions, out
+// of place with the same table (kv_cache_append_rope_qk).
 #include "sa_device.h"
 #include "sa_kernels.h"
 #include "sa_rope.h"
@@ -146,49 +148,71 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
       }
   }
   __syncthreads();
-  // K: thread -> (head, 8-pair chunk) of a row: both halves of the chunk in,
-  // both rotated halves out
-  {
+  // Rotation of nheads heads of each of the nk rows: thread -> (head,
+  // 8-pair chunk) column; both halves of the chunk in, both rotated halves
+  // out (reads finish before writes, so src may equal dst).
+  auto rotate_rows = [&](const E* src, int src_rstride, E* dst, int dst_rstride, int nheads) {
     const int cpr = half / VEC;                 // chunks per head
-    const int per_row = nh * cpr;
-    const int rstep = kThreads / per_row;
-    const int q = threadIdx.x % per_row, r0 = threadIdx.x / per_row;
-    const int hh = q / cpr, c = (q - hh * cpr) * VEC;
-    if (r0 < rstep)
-      for (int r = r0; r < nk; r += rstep) {
-        const E* row = src0 + r * rstride + hh * d;
-        const u32x4 uv = ld16(row + c), vv = ld16(row + c + half);
-        const E* ue = reinterpret_cast<const E*>(&uv);
-        const E* ve = reinterpret_cast<const E*>(&vv);
-        const double2* t = &tab[r * half + c];
-        u32x4 w1, w2;
-        E* o1 = reinterpret_cast<E*>(&w1);
-        E* o2 = reinterpret_cast<E*>(&w2);
+    const int per_row = nheads * cpr;
+    auto one = [&](int r, int hh, int c) {
+      const E* row = src + r * src_rstride + hh * d;
+      const u32x4 uv = ld16(row + c), vv = ld16(row + c + half);
+      const E* ue = reinterpret_cast<const E*>(&uv);
+      const E* ve = reinterpret_cast<const E*>(&vv);
+      const double2* t = &tab[r * half + c];
+      u32x4 w1, w2;
+      E* o1 = reinterpret_cast<E*>(&w1);
+      E* o2 = reinterpret_cast<E*>(&w2);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          double u, v;
-          if constexpr (ELT == 2) {
-            u = (double)bf16_to_f32(ue[i]);
-            v = (double)bf16_to_f32(ve[i]);
-          } else {
-            u = (double)__uint_as_float(ue[i]);
-            v = (double)__uint_as_float(ve[i]);
-          }
-          const double2 cs = t[i];
-          const double y1 = sa_rope::rot_first(u, v, cs.x, cs.y);
-          const double y2 = sa_rope::rot_second(u, v, cs.x, cs.y);
-          if constexpr (ELT == 2) {
-            o1[i] = (E)f64_to_bf16_bits(y1);
-            o2[i] = (E)f64_to_bf16_bits(y2);
-          } else {
-            o1[i] = __float_as_uint((float)y1);
-            o2[i] = __float_as_uint((float)y2);
-          }
+      for (int i = 0; i < VEC; ++i) {
+        double u, v;
+        if constexpr (ELT == 2) {
+          u = (double)bf16_to_f32(ue[i]);
+          v = (double)bf16_to_f32(ve[i]);
+        } else {
+          u = (double)__uint_as_float(ue[i]);
+          v = (double)__uint_as_float(ve[i]);
         }
-        E* out = dst0 + r * rstride + hh * d;
-        st16(out + c, w1);
-        st16(out + c + half, w2);
+        const double2 cs = t[i];
+        const double y1 = sa_rope::rot_first(u, v, cs.x, cs.y);
+        const double y2 = sa_rope::rot_second(u, v, cs.x, cs.y);
+        if constexpr (ELT == 2) {
+          o1[i] = (E)f64_to_bf16_bits(y1);
+          o2[i] = (E)f64_to_bf16_bits(y2);
+        } else {
+          o1[i] = __float_as_uint((float)y1);
+          o2[i] = __float_as_uint((float)y2);
+        }
       }
+      E* out = dst + r * dst_rstride + hh * d;
+      st16(out + c, w1);
+      st16(out + c + half, w2);
+    };
+    if (per_row <= kThreads) {                  // fixed column, rows stepping
+      const int rstep = kThreads / per_row;
+      const int q = threadIdx.x % per_row, r0 = threadIdx.x / per_row;
+      const int hh = q / cpr, c = (q - hh * cpr) * VEC;
+      if (r0 < rstep)
+        for (int r = r0; r < nk; r += rstep) one(r, hh, c);
+    } else {
+      for (int e = threadIdx.x; e < nk * per_row; e += kThreads) {
+        const int r = e / per_row, q = e - r * per_row;
+        const int hh = q / cpr;
+        one(r, hh, (q - hh * cpr) * VEC);
+      }
+    }
+  };
+  rotate_rows(src0, rstride, dst0, rstride, nh);
+  if (ar.q_src) {
+    // this head group's share of the Q heads, rotated at the same rows
+    const int qpg = (ar.n_q + nhc - 1) / nhc;
+    const int qh0 = (rest % nhc) * qpg;
+    const int nq = min(qpg, ar.n_q - qh0);
+    if (nq > 0) {
+      const int64_t qoff = (((int64_t)b * a.T_new + (key_lo - a.o)) * ar.n_q + qh0) * d;
+      rotate_rows(reinterpret_cast<const E*>(ar.q_src) + qoff, ar.n_q * d,
+                  reinterpret_cast<E*>(ar.q_dst) + qoff, ar.n_q * d, nq);
+    }
   }
   // V: transposed into the blocked layout, one head after another
   for (int hh = 0; hh < nh; ++hh) {

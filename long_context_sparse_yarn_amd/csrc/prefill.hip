@@ -38,6 +38,7 @@
 //    that XCD's L2; the longest (latest) query blocks start first.
 #include "sa_device.h"
 #include "sa_kernels.h"
+#include "sa_rope.h"
 
 
 #ifndef SA_RD_AHEAD
@@ -84,15 +85,20 @@ __device__ __forceinline__ int k_swz(int r) {
 // the 16-lane V^T operand reads conflict-free.
 __device__ __forceinline__ int v_lds(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
 
-template <int D, int NT, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb) {
+template <int D, int NT, int NW, bool ROPE>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb,
+                                                               RopeTab rt) {
   constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
   constexpr int DT = D / 16;          // coordinate tiles of O^T
   constexpr int KBUF = kTile * k_pitch<D>();
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[3][KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[3][2 * D * 32];
+  constexpr int VBUF = 2 * D * 32;
+  // one LDS arena: three K tiles, three V^T tiles (and, before the first
+  // tile arrives, the Q rotation table)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * KBUF + 3 * VBUF];
+  auto Kb = [&](int buf) { return lds + buf * KBUF; };
+  auto Vb = [&](int buf) { return lds + 3 * KBUF + buf * VBUF; };
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -134,6 +140,60 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     l_run[n] = (g4 == 0 && sg != -INFINITY) ? 1.0f : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if constexpr (ROPE) {
+    // Rotate this lane's Q operands at their positions with yarn_rope's
+    // arithmetic (so they carry exactly the bits yarn_rope would write): the
+    // workgroup builds the (c*cos, c*sin) table of its positions in LDS, in
+    // chunks of positions if it does not fit, and each lane rotates its
+    // 8-coordinate chunks against their partner halves (loaded again; the
+    // rows are in cache).
+    constexpr int HALF = D / 2;
+    constexpr int kTabRows = (int)(sizeof(lds) / (HALF * sizeof(double2)));
+    double2* tab = reinterpret_cast<double2*>(lds);
+    const int npos = t_end - p0;
+    for (int c0 = 0; c0 < npos; c0 += kTabRows) {
+      const int nc = min(kTabRows, npos - c0);
+      if (c0 > 0) __syncthreads();              // readers of the previous chunk are done
+      for (int e = threadIdx.x; e < nc * HALF; e += kThreads) {
+        const int r = e / HALF, i = e - r * HALF;
+        double sn, cn;
+        sa_rope::sincos_reduced((double)(a.q_offset + p0 + c0 + r) * rt.inv_freq[i], &sn, &cn);
+        tab[e] = make_double2(cn * rt.conc, sn * rt.conc);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int row = tpos[n] - p0 - c0;
+        if (!rvalid[n] || row < 0 || row >= nc) continue;
+        const uint16_t* qrow = q + (((int64_t)b * a.T_q + tpos[n]) * a.n_q + head[n]) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = 32 * ks + 8 * g4;       // the chunk's 8 coordinates lie in one half
+          const bool first = c < HALF;
+          const u32x4 pv = ld16(qrow + (first ? c + HALF : c - HALF));
+          const double2* t = &tab[row * HALF + (first ? c : c - HALF)];
+          uint32_t w[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t out[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const double x = (double)(h ? bf16_hi(qop[n][ks][e2]) : bf16_lo(qop[n][ks][e2]));
+              const double y = (double)(h ? bf16_hi(pv[e2]) : bf16_lo(pv[e2]));
+              const double2 cs = t[2 * e2 + h];
+              const double o = first ? sa_rope::rot_first(x, y, cs.x, cs.y)
+                                     : sa_rope::rot_second(y, x, cs.x, cs.y);
+              out[h] = f64_to_bf16_bits(o);
+            }
+            w[e2] = out[0] | (out[1] << 16);
+          }
+          qop[n][ks] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+    __syncthreads();                            // the table area becomes tile buffers
   }
 
   const float scale = a.sm_scale * SA_LOG2E;
@@ -192,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       if (KBLK % NW == 0 || blk < KBLK) {
         const uint32_t off = full ? k_goff[i]
                                   : (uint32_t)(min(k_r[i], last_row) * krow_stride + 8 * k_c[i]);
-        lds_direct16(kt + off, &Ks[buf][512 * blk]);
+        lds_direct16(kt + off, &Kb(buf)[512 * blk]);
       }
     }
   };
@@ -202,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int i = 0; i < VBW; ++i) {
       const int blk = wave + i * NW;
       if (VBLK % NW == 0 || blk < VBLK)
-        lds_direct16(vt + v_goff[i], &Vs[buf][512 * blk]);
+        lds_direct16(vt + v_goff[i], &Vb(buf)[512 * blk]);
     }
   };
   // Register path: thread c of the workgroup moves chunks c, c + kThreads,
@@ -227,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
           }
         }
       }
-      st16(&Vs[buf][v_lds(r, ch)], v);
+      st16(&Vb(buf)[v_lds(r, ch)], v);
     }
   };
   auto load_v = [&](int buf, int t) {
@@ -268,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const int mt = 2 * h + mm;
-        const u32x4 A = ld16(&Ks[buf][ka[ks] + k_pitch<D>() * (4 * (mt & 1) + 32 * (mt >> 1))]);
+        const u32x4 A = ld16(&Kb(buf)[ka[ks] + k_pitch<D>() * (4 * (mt & 1) + 32 * (mt >> 1))]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) S.v[mm][n] = mfma16x16x32(A, qop[n][ks], S.v[mm][n]);
       }
@@ -312,7 +372,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   auto pv = [&](int buf, int h, const u32x4 (&Pk)[NT]) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const u32x4 A = ld16(&Vs[buf][va_off + (h * D + 16 * dt) * 32]);
+      const u32x4 A = ld16(&Vb(buf)[va_off + (h * D + 16 * dt) * 32]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[n], O[dt][n]);
     }
@@ -451,14 +511,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 }
 
 template <int D, int NT, int NW>
-hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_d(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
   const int rows = NW * NT * 16;
   if (a.q_mult > rows) return hipErrorInvalidValue;
   const int BQ = rows / a.q_mult;
   const int n_qb = (a.T_q + BQ - 1) / BQ;
   const int64_t grid = (int64_t)n_qb * a.B * a.n_kv;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s,
-                     a, BQ, n_qb);
+  RopeTab rt;
+  if (rope) {
+    rt = *rope;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, true>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
+  } else {
+    rt.conc = 0.0;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, false>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
+  }
   return hipGetLastError();
 }
 
@@ -488,12 +556,12 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 #endif
 constexpr int kBandWindowMax = 512;   // windows up to this use the band shape
 
-hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_prefill_bf16(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
   const bool band = a.window > 0 && a.window <= kBandWindowMax;
   switch (a.d) {
-    case 64: return band ? launch_d<64, SA_PFB64>(a, s) : launch_d<64, SA_PF64>(a, s);
-    case 96: return band ? launch_d<96, SA_PFB96>(a, s) : launch_d<96, SA_PF96>(a, s);
-    case 128: return band ? launch_d<128, SA_PFB128>(a, s) : launch_d<128, SA_PF128>(a, s);
+    case 64: return band ? launch_d<64, SA_PFB64>(a, rope, s) : launch_d<64, SA_PF64>(a, rope, s);
+    case 96: return band ? launch_d<96, SA_PFB96>(a, rope, s) : launch_d<96, SA_PF96>(a, rope, s);
+    case 128: return band ? launch_d<128, SA_PFB128>(a, rope, s) : launch_d<128, SA_PF128>(a, rope, s);
     default: return hipErrorInvalidValue;
   }
 }

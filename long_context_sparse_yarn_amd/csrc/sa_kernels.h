@@ -30,6 +30,9 @@ hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s);
 
 struct AppendRopeArgs {  // rotate K rows at their cache positions, then append
   AppendArgs ap;         // k_src holds unrotated rows
+  const void* q_src;     // optional [B, T_new, n_q, d]: rotated at the same
+  void* q_dst;           //   positions into q_dst (may be q_src); null: none
+  int n_q;
   double conc;
   double inv_freq[SA_MAX_HALF];
 };
@@ -46,7 +49,13 @@ struct AttnArgs {
   int64_t q_offset;     // global position of query 0
   float sm_scale;
 };
-hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
+struct RopeTab {         // YaRN tables for rotating Q inside the prefill kernel
+  double conc;
+  double inv_freq[SA_MAX_HALF];
+};
+// rope == nullptr: q is already rotated; otherwise q holds unrotated rows and
+// the kernel rotates them at their positions first (yarn_rope's arithmetic).
+hipError_t launch_prefill_bf16(const AttnArgs& a, const RopeTab* rope, hipStream_t s);
 hipError_t launch_attn_rows_f32(const AttnArgs& a, hipStream_t s);
 
 struct DecodeArgs {

@@ -229,10 +229,28 @@ int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v, int T_new,
 
 int kv_cache_append_rope(sa_kv_cache* c, const void* k, const void* v, int T_new, const sa_yarn* y,
                          void* stream) {
+  return kv_cache_append_rope_qk(c, nullptr, nullptr, 0, k, v, T_new, y, stream);
+}
+
+int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q, const void* k,
+                            const void* v, int T_new, const sa_yarn* y, void* stream) {
   AppendRopeArgs a;
   memset(&a, 0, sizeof a);
   int st = append_args(c, k, v, T_new, &a.ap);
   if (st != SA_OK) return st;
+  if (q || q_rot) {
+    if (!q || !q_rot) return fail(SA_ERR_ARG, "q and q_rot must both be given");
+    if (misaligned(q) || misaligned(q_rot)) return fail(SA_ERR_ARG, "q and q_rot must be 16-byte aligned");
+    if (n_q <= 0) return fail(SA_ERR_ARG, "n_q must be positive");
+    const char* qb = static_cast<const char*>(q);
+    const char* rb = static_cast<const char*>(q_rot);
+    const int64_t bytes = (int64_t)c->B * T_new * n_q * c->d_h * elt_bytes(c->dtype);
+    if (qb != rb && qb < rb + bytes && rb < qb + bytes)
+      return fail(SA_ERR_ARG, "q and q_rot overlap without being the same buffer");
+    a.q_src = q;
+    a.q_dst = q_rot;
+    a.n_q = n_q;
+  }
   if (c->dtype == SA_BF16 && c->d_h % 16)
     return fail(SA_ERR_SHAPE, "bf16 rotate-and-append needs d_h %% 16 == 0, got %d", c->d_h);
   st = yarn_table(y, c->d_h, a.inv_freq, &a.conc);
@@ -277,9 +295,12 @@ static int check_attn(const void* q, const sa_kv_cache* c, const float* sinks, c
   return SA_OK;
 }
 
-int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
-                     int T_q, int n_q, int n_kv, int d_h, int window, float sm_scale,
-                     int64_t q_offset, void* stream) {
+namespace {
+// Shared by the prefill entry points; yarn != nullptr: q is unrotated and the
+// bf16 kernel rotates it first.
+int prefill_common(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
+                   int T_q, int n_q, int n_kv, int d_h, int window, float sm_scale,
+                   int64_t q_offset, const sa_yarn* yarn, void* stream) {
   int st = check_attn(q, c, sinks, out, B, T_q, n_q, n_kv, d_h);
   if (st != SA_OK) return st;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SA_ERR_ARG, "sm_scale must be finite and > 0");
@@ -293,6 +314,12 @@ int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks, vo
     if (q_mult > 128) return fail(SA_ERR_SHAPE, "n_q/n_kv must be <= 128");
     if (c->capacity > INT32_MAX)   // the kernel keeps key positions in 32 bits
       return fail(SA_ERR_SHAPE, "bf16 prefill needs a capacity below 2^31 rows");
+  }
+  RopeTab rt;
+  if (yarn) {
+    if (c->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "in-kernel Q rotation needs a bf16 cache");
+    st = yarn_table(yarn, d_h, rt.inv_freq, &rt.conc);
+    if (st != SA_OK) return st;
   }
   if ((int64_t)B * T_q * n_q > INT32_MAX) return fail(SA_ERR_ARG, "B*T_q*n_q too large");
   if (T_q == 0) return ok();
@@ -312,10 +339,27 @@ int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks, vo
   a.C = c->capacity;
   a.q_offset = q_offset;
   a.sm_scale = sm_scale;
-  hipError_t e = c->dtype == SA_BF16 ? launch_prefill_bf16(a, (hipStream_t)stream)
-                                     : launch_attn_rows_f32(a, (hipStream_t)stream);
+  hipError_t e = c->dtype == SA_BF16
+                     ? launch_prefill_bf16(a, yarn ? &rt : nullptr, (hipStream_t)stream)
+                     : launch_attn_rows_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
+}
+}  // namespace
+
+int sinkattn_prefill(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
+                     int T_q, int n_q, int n_kv, int d_h, int window, float sm_scale,
+                     int64_t q_offset, void* stream) {
+  return prefill_common(q, c, sinks, out, B, T_q, n_q, n_kv, d_h, window, sm_scale, q_offset,
+                        nullptr, stream);
+}
+
+int sinkattn_prefill_rope(const void* q, const sa_kv_cache* c, const float* sinks, void* out,
+                          int B, int T_q, int n_q, int n_kv, int d_h, int window, float sm_scale,
+                          int64_t q_offset, const sa_yarn* y, void* stream) {
+  if (!y) return fail(SA_ERR_ARG, "yarn parameters are null");
+  return prefill_common(q, c, sinks, out, B, T_q, n_q, n_kv, d_h, window, sm_scale, q_offset, y,
+                        stream);
 }
 
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h, int64_t capacity) {

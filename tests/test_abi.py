@@ -127,6 +127,19 @@ def test_errors_are_reported_before_any_launch():
     assert P(q, hbig, s, o, 1, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE
     assert "2^31" in sa.last_error()
     B._kv_cache_destroy(hbig)
+    # prefill with in-kernel rotation: yarn checks and bf16 only, nothing launched
+    PR = B._sinkattn_prefill_rope
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    yq = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
+    yq96 = B.SaYarn(96, 150000.0, 32.0, 4096, 1.0, 32.0)
+    assert PR(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, None, None) == SA_ERR_ARG
+    assert PR(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, ctypes.byref(yq96), None) == SA_ERR_SHAPE
+    assert PR(q, h, s, o, 2, 5, 8, 2, 64, 0, 0.125, 6, ctypes.byref(yq), None) == SA_ERR_CAPACITY
+    assert PR(q, h, s, o, 2, 0, 8, 2, 64, 0, 0.125, 0, ctypes.byref(yq), None) == SA_OK
+    B._kv_cache_destroy(h)
+    st, hf = create(dtype=1, Bn=2, C=256, n_kv=2, d=64, offset=10)
+    assert PR(q, hf, s, o, 2, 5, 8, 2, 64, 0, 0.125, 0, ctypes.byref(yq), None) == SA_ERR_DTYPE
+    B._kv_cache_destroy(hf)
     # rotate-and-append: yarn checks, bf16 head dim, capacity, nothing launched
     AR = B._kv_cache_append_rope
     st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
@@ -136,6 +149,17 @@ def test_errors_are_reported_before_any_launch():
     assert AR(h, q, q, 4, ctypes.byref(y96), None) == SA_ERR_SHAPE           # yarn d_h differs
     assert AR(h, q, q, 247, ctypes.byref(y64), None) == SA_ERR_CAPACITY
     assert AR(h, ctypes.c_void_p(0x30008), q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert B._kv_cache_offset(h) == 10
+    B._kv_cache_destroy(h)
+    # with queries: both or neither, aligned, n_q > 0, no partial overlap
+    QK = B._kv_cache_append_rope_qk
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    qr = ctypes.c_void_p(0x60000)
+    assert QK(h, q, None, 8, q, q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert QK(h, q, ctypes.c_void_p(0x60008), 8, q, q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert QK(h, q, qr, 0, q, q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert QK(h, q, ctypes.c_void_p(0x30000 + 128), 8, q, q, 4, ctypes.byref(y64), None) == SA_ERR_ARG
+    assert QK(h, q, qr, 8, q, q, 4, ctypes.byref(y96), None) == SA_ERR_SHAPE
     assert B._kv_cache_offset(h) == 10
     B._kv_cache_destroy(h)
     st, h24 = create(d=24, offset=10)

@@ -262,3 +262,59 @@ def test_prefill_extreme_logits(scale_qk, growing, sink_inf):
                           sinks, 0, 0, 0.125)
     assert np.all(np.isfinite(got))
     assert max_abs(got, want) <= 2e-2, max_abs(got, want)
+
+
+ROPE_PREFILL_CASES = [
+    # B, prefix, T, n_q, n_kv, d, window
+    (2, 0, 333, 8, 2, 64, 0),
+    (1, 37, 200, 8, 4, 96, 128),
+    (1, 100, 150, 16, 2, 128, 17),
+    (1, 64, 129, 64, 8, 64, 0),
+    (1, 5, 300, 4, 4, 128, 0),        # q_mult 1 at d = 128: the rotation table takes chunks
+    (2, 7, 65, 8, 8, 96, 0),          # q_mult 1 at d = 96
+    (1, 1000, 31, 16, 1, 64, 0),
+]
+
+
+@pytest.mark.parametrize("B,prefix,T,n_q,n_kv,d,W", ROPE_PREFILL_CASES)
+def test_prefill_rope_equals_rope_then_prefill(B, prefix, T, n_q, n_kv, d, W):
+    """sinkattn_prefill_rope on raw queries gives the bits of yarn_rope_apply
+    followed by sinkattn_prefill."""
+    rng = np.random.default_rng(T * 5 + d + prefix)
+    ly = lib_yarn(d, Yarn())
+    C = ((prefix + T + 31) // 32) * 32 + 32
+    k = _draw((B, prefix + T, n_kv, d), rng, "bf16")
+    v = _draw((B, prefix + T, n_kv, d), rng, "bf16")
+    q = _draw((B, T, n_q, d), rng, "bf16")
+    sinks = torch.from_numpy(rng.standard_normal(n_q).astype(np.float32)).cuda()
+    cache = sa.KVCache.empty(B, C, n_kv, d, fill=float("nan"))
+    cache.append_rope(dev(k, "bf16"), dev(v, "bf16"), ly)
+    q_raw = dev(q, "bf16")
+    q_rot = torch.empty_like(q_raw)
+    sa.yarn_rope_apply(q_raw, prefix, ly, out=q_rot)
+    want = sa.sinkattn_prefill(q_rot, cache, sinks, W, 1.0 / np.sqrt(d), prefix)
+    got = sa.sinkattn_prefill_rope(q_raw, cache, sinks, W, 1.0 / np.sqrt(d), prefix, ly)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert torch.equal(q_raw.view(torch.int16), dev(q, "bf16").view(torch.int16))  # q untouched
+
+
+def test_prefill_rope_matches_oracle():
+    """The fused path against the fp64 oracle layer (rotation included)."""
+    B, T, n_q, n_kv, d, W = 1, 200, 8, 4, 96, 128
+    rng = np.random.default_rng(11)
+    y = Yarn()
+    ly = lib_yarn(d, y)
+    q = _draw((B, T, n_q, d), rng, "bf16")
+    k = _draw((B, T, n_kv, d), rng, "bf16")
+    v = _draw((B, T, n_kv, d), rng, "bf16")
+    sinks = rng.standard_normal(n_q).astype(np.float32)
+    sm = 1.0 / np.sqrt(d)
+    cache = sa.KVCache.empty(B, 256, n_kv, d, fill=float("nan"))
+    cache.append_rope(dev(k, "bf16"), dev(v, "bf16"), ly)
+    got = sa.sinkattn_prefill_rope(dev(q, "bf16"), cache, torch.from_numpy(sinks).cuda(), W, sm,
+                                   0, ly)
+    inv, conc = oracle_tables(d, y)
+    want, _, _ = prefill_layer(OracleKVCache(B, 256, n_kv, d), q, k, v, sinks, W, sm, inv, conc,
+                               "bf16")
+    assert max_abs(host(got), want) <= TOL["bf16"]

@@ -197,3 +197,43 @@ def test_append_rope_equals_rope_then_append(dtype, B, C, n_kv, d, o0, chunks):
 
 def _bits_t(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,C,n_q,n_kv,d,o0,T,inplace", [
+    (2, 256, 8, 2, 64, 0, 90, False),
+    (1, 4096, 8, 4, 96, 0, 4000, False),      # GPT-OSS-Lite shapes
+    (1, 256, 64, 8, 64, 5, 100, True),        # gpt-oss heads, rotated in place
+    (1, 192, 64, 4, 128, 7, 97, False),       # 512 Q columns per row: the general loop
+    (1, 160, 32, 16, 64, 3, 70, False),       # Q heads spread over several head groups
+])
+def test_append_rope_qk_equals_separate_rotations(dtype, B, C, n_q, n_kv, d, o0, T, inplace):
+    """kv_cache_append_rope_qk writes the cache bits of kv_cache_append_rope
+    and the Q bits of yarn_rope at the same positions."""
+    ly = lib_yarn(d, Yarn())
+    rng = np.random.default_rng(C + n_q + d)
+    def draw(*shape):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32) if dtype == "bf16" else x
+    fused = _sentinel_cache(B, C, n_kv, d, dtype)
+    ref = _sentinel_cache(B, C, n_kv, d, dtype)
+    if o0:
+        pk, pv = draw(B, o0, n_kv, d), draw(B, o0, n_kv, d)
+        fused.append(dev(pk, dtype), dev(pv, dtype))
+        ref.append(dev(pk, dtype), dev(pv, dtype))
+    q, k, v = draw(B, T, n_q, d), draw(B, T, n_kv, d), draw(B, T, n_kv, d)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    want_q = torch.empty_like(qd)
+    sa.yarn_rope_apply(qd, o0, ly, out=want_q)
+    ref.append_rope(kd, vd, ly)
+    if inplace:
+        got_q = qd.clone()
+        out = fused.append_rope_qk(got_q, kd, vd, ly, q_out=got_q)
+        assert out is got_q
+    else:
+        got_q = fused.append_rope_qk(qd, kd, vd, ly)
+    torch.cuda.synchronize()
+    assert fused.offset == ref.offset == o0 + T
+    assert torch.equal(_bits_t(got_q), _bits_t(want_q))
+    assert torch.equal(_bits_t(fused.k), _bits_t(ref.k))
+    assert torch.equal(_bits_t(fused.v), _bits_t(ref.v))
