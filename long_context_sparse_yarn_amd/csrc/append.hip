@@ -6,18 +6,19 @@
 // [B, C/32, n_kv, d, 32] (keys contiguous per coordinate).  One workgroup
 // owns one (b, g, 32-key block) and copies only the rows of that block that
 // fall in [o, o + T_new), so rows outside the range keep their bits.
-// K rows move as 16-byte vectors.  V rows are staged through LDS and written
-// transposed: a full block as 16-byte vectors of 8 keys of one coordinate, a
-// partial block (at either end of the range) element by element.
+// K rows move as 16-byte vectors.  V goes through registers: for a full
+// block a thread transposes an 8-key x 8-coordinate tile (bf16) and writes
+// 16-byte vectors of 8 keys of one coordinate; a partial block (at either
+// end of the range) moves element by element.
 //
 // kv_cache_append_rope does the same with unrotated K: each K row is rotated
 // at its cache row index, which is its global position (DESIGN CONTRACTS),
 // with the arithmetic of yarn_rope (sa_rope.h), so the cache receives the
 // bits that yarn_rope followed by kv_cache_append would write.  A workgroup
-// owns one (b, 32-key block, group of heads): it stages V through LDS as
-// above and builds the block's (c*cos, c*sin) table once in LDS for all its
-// heads; each thread then takes a (row, head, 8-pair chunk), loads both
-// halves of the chunk, and writes both rotated halves.  Optionally the same
+// owns one (b, 32-key block, group of heads): it moves V as above and builds
+// the block's (c*cos, c*sin) table once in LDS for all its heads; each
+// thread then takes a (row, head, 8-pair chunk), loads both halves of the
+// chunk, and writes both rotated halves.  Optionally the same
 // workgroups rotate the layer's Q rows, which sit at the same positions, out
 // of place with the same table (kv_cache_append_rope_qk).
 #include "sa_device.h"
@@ -30,13 +31,58 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Rows [key_lo, key_lo + nk) of nheads V heads, all in one 32-key block, into
+// the blocked layout [.., d, 32].  src: row key_lo of the first head (rows
+// rstride elements apart, heads d apart); dst: the block of the first head
+// (heads d*32 apart); kk0: slot of key_lo in the block.  A full block moves
+// as register-transposed tiles: a thread loads 8 keys x 8 coordinates
+// (bf16; 4 x 4 for fp32) as 16-byte row vectors and stores the 8 (4)
+// coordinate vectors of 8 (4) keys; partial blocks go element by element.
+template <int ELT>
+__device__ __forceinline__ void v_to_blocked(
+    const typename std::conditional<ELT == 2, uint16_t, uint32_t>::type* src, int rstride,
+    typename std::conditional<ELT == 2, uint16_t, uint32_t>::type* dst, int nheads, int d, int nk,
+    int kk0) {
+  constexpr int VEC = 16 / ELT;                 // keys (= coordinates) per tile side
+  if (nk == 32) {
+    const int cgs = d / VEC;                    // coordinate groups per head
+    const int ntask = nheads * cgs * (32 / VEC);
+    for (int tk = threadIdx.x; tk < ntask; tk += kThreads) {
+      const int kg = tk % (32 / VEC), rest = tk / (32 / VEC);
+      const int hh = rest / cgs, cg = rest - hh * cgs;
+      u32x4 R[VEC];
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) R[k] = ld16(src + (kg * VEC + k) * rstride + hh * d + cg * VEC);
+      auto* out = dst + (int64_t)hh * d * 32 + (cg * VEC) * 32 + kg * VEC;
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        u32x4 w;
+        if constexpr (ELT == 2) {
+          // keys 2m, 2m+1 of coordinate c: halves c&1 of word c/2 of rows 2m, 2m+1
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w[m] = __builtin_amdgcn_perm(R[2 * m + 1][c >> 1], R[2 * m][c >> 1], sel);
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w[m] = R[m][c];
+        }
+        st16(out + c * 32, w);
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < nheads * d * nk; e += kThreads) {
+      const int r = e % nk, hc = e / nk;        // hc = head * d + coordinate
+      const int hh = hc / d, c = hc - hh * d;
+      dst[(int64_t)hh * d * 32 + c * 32 + kk0 + r] = src[r * rstride + hc];
+    }
+  }
+}
+
 template <int ELT>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int64_t kb0, int nblk) {
   typedef typename std::conditional<ELT == 2, uint16_t, uint32_t>::type E;
   constexpr int VEC = 16 / ELT;                 // elements per 16-byte vector
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int d = a.d;
-  const int pitch = d + 1;                      // odd pitch: transposed reads spread banks
   const int blk = blockIdx.x % nblk;
   const int rest = blockIdx.x / nblk;
   const int g = rest % a.n_kv;
@@ -47,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int64_t 
   const int nk = (int)(key_hi - key_lo);
   const int kk0 = (int)(key_lo - kb * 32);      // first slot in the block
 
-  E* tile = reinterpret_cast<E*>(smem);
   const E* ksrc = reinterpret_cast<const E*>(a.k_src);
   const E* vsrc = reinterpret_cast<const E*>(a.v_src);
   E* kc = reinterpret_cast<E*>(a.kc);
@@ -55,52 +100,33 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int64_t 
   const int64_t src_row0 = ((int64_t)b * a.T_new + (key_lo - a.o)) * a.n_kv + g;   // in rows of d
   const int64_t dst_row0 = ((int64_t)b * a.C + key_lo) * a.n_kv + g;
   const int vpr = d / VEC;                      // vectors per row
+  const int rstride = a.n_kv * d;
 
-  // K rows and V rows (into LDS), 16 bytes at a time
+  // K rows, 16 bytes at a time
   for (int e = threadIdx.x; e < nk * vpr; e += kThreads) {
     const int r = e / vpr, c = (e - r * vpr) * VEC;
-    const int64_t so = (src_row0 + (int64_t)r * a.n_kv) * d + c;
-    st16(kc + (dst_row0 + (int64_t)r * a.n_kv) * d + c, ld16(ksrc + so));
-    const u32x4 v = ld16(vsrc + so);
-    const E* ve = reinterpret_cast<const E*>(&v);
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) tile[r * pitch + c + i] = ve[i];
+    st16(kc + dst_row0 * d + (int64_t)r * rstride + c, ld16(ksrc + src_row0 * d + (int64_t)r * rstride + c));
   }
-  __syncthreads();
-  E* vblk = vc + (((int64_t)b * (a.C / 32) + kb) * a.n_kv + g) * (int64_t)d * 32;
-  if (nk == 32) {
-    // full block: coordinate c, keys 8k .. 8k+7 (bf16) / 4k .. 4k+3 (fp32)
-    constexpr int KV = VEC;
-    for (int e = threadIdx.x; e < d * (32 / KV); e += kThreads) {
-      const int c = e / (32 / KV), k = (e - c * (32 / KV)) * KV;
-      u32x4 w;
-      E* we = reinterpret_cast<E*>(&w);
-#pragma unroll
-      for (int i = 0; i < KV; ++i) we[i] = tile[(k + i) * pitch + c];
-      st16(vblk + c * 32 + k, w);
-    }
-  } else {
-    for (int e = threadIdx.x; e < nk * d; e += kThreads) {
-      const int c = e / nk, r = e - c * nk;
-      vblk[c * 32 + kk0 + r] = tile[r * pitch + c];
-    }
-  }
+  v_to_blocked<ELT>(vsrc + src_row0 * d, rstride,
+                    vc + (((int64_t)b * (a.C / 32) + kb) * a.n_kv + g) * (int64_t)d * 32, 1, d, nk,
+                    kk0);
 }
 
 template <int ELT>
 __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar, int64_t kb0,
-                                                               int nblk, int hc) {
+                                                               int nblk, int hc, int ngr, int qpg) {
   typedef typename std::conditional<ELT == 2, uint16_t, uint32_t>::type E;
   constexpr int VEC = 16 / ELT;                 // elements per 16-byte vector
   const AppendArgs& a = ar.ap;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int d = a.d, half = d / 2;
-  const int pitch = d + 1;
-  const int nhc = (a.n_kv + hc - 1) / hc;
+  // head group grp of ngr: K heads [h0, h0 + nh) (possibly none) and Q heads
+  // [grp * qpg, ...)
   const int blk = blockIdx.x % nblk;
   const int rest = blockIdx.x / nblk;
-  const int h0 = (rest % nhc) * hc;
-  const int b = rest / nhc;
+  const int grp = rest % ngr;
+  const int b = rest / ngr;
+  const int h0 = min(grp * hc, a.n_kv);
   const int nh = min(hc, a.n_kv - h0);
   const int64_t kb = kb0 + blk;
   const int64_t key_lo = max(kb * 32, a.o);
@@ -109,7 +135,6 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   const int kk0 = (int)(key_lo - kb * 32);
 
   double2* tab = reinterpret_cast<double2*>(smem);                      // [32][half]
-  E* vtile = reinterpret_cast<E*>(smem + (size_t)32 * half * sizeof(double2));   // [nh][32][d+1]
   const E* ksrc = reinterpret_cast<const E*>(a.k_src);
   const E* vsrc = reinterpret_cast<const E*>(a.v_src);
   E* kc = reinterpret_cast<E*>(a.kc);
@@ -121,21 +146,11 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   E* dst0 = kc + (((int64_t)b * a.C + key_lo) * a.n_kv + h0) * d;
   const int rstride = a.n_kv * d;
 
-  // V rows into LDS: thread -> vector column q of a row (nh*d/VEC per row),
-  // rows stepping by the threads per row
-  {
-    const int per_row = nh * (d / VEC);
-    const int rstep = kThreads / per_row;
-    const int q = threadIdx.x % per_row, r0 = threadIdx.x / per_row;
-    const int hh = q / (d / VEC), c = (q - hh * (d / VEC)) * VEC;
-    if (r0 < rstep)
-      for (int r = r0; r < nk; r += rstep) {
-        const u32x4 v = ld16(vsrc0 + r * rstride + hh * d + c);
-        const E* ve = reinterpret_cast<const E*>(&v);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) vtile[(hh * 32 + r) * pitch + c + i] = ve[i];
-      }
-  }
+  // V: straight into the blocked layout (no LDS)
+  if (nh > 0)
+    v_to_blocked<ELT>(vsrc0, rstride,
+                      vc + (((int64_t)b * (a.C / 32) + kb) * a.n_kv + h0) * (int64_t)d * 32, nh, d,
+                      nk, kk0);
   // (c*cos, c*sin) of the block's rows: thread -> pair i, rows stepping
   {
     const int rstep = kThreads / half;
@@ -193,7 +208,10 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
       const int q = threadIdx.x % per_row, r0 = threadIdx.x / per_row;
       const int hh = q / cpr, c = (q - hh * cpr) * VEC;
       if (r0 < rstep)
-        for (int r = r0; r < nk; r += rstep) one(r, hh, c);
+        for (int r = r0; r < nk; r += 2 * rstep) {
+          one(r, hh, c);
+          if (r + rstep < nk) one(r + rstep, hh, c);
+        }
     } else {
       for (int e = threadIdx.x; e < nk * per_row; e += kThreads) {
         const int r = e / per_row, q = e - r * per_row;
@@ -202,36 +220,15 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
       }
     }
   };
-  rotate_rows(src0, rstride, dst0, rstride, nh);
+  if (nh > 0) rotate_rows(src0, rstride, dst0, rstride, nh);
   if (ar.q_src) {
     // this head group's share of the Q heads, rotated at the same rows
-    const int qpg = (ar.n_q + nhc - 1) / nhc;
-    const int qh0 = (rest % nhc) * qpg;
+    const int qh0 = grp * qpg;
     const int nq = min(qpg, ar.n_q - qh0);
     if (nq > 0) {
       const int64_t qoff = (((int64_t)b * a.T_new + (key_lo - a.o)) * ar.n_q + qh0) * d;
       rotate_rows(reinterpret_cast<const E*>(ar.q_src) + qoff, ar.n_q * d,
                   reinterpret_cast<E*>(ar.q_dst) + qoff, ar.n_q * d, nq);
-    }
-  }
-  // V: transposed into the blocked layout, one head after another
-  for (int hh = 0; hh < nh; ++hh) {
-    E* vblk = vc + (((int64_t)b * (a.C / 32) + kb) * a.n_kv + h0 + hh) * (int64_t)d * 32;
-    const E* vt = vtile + hh * 32 * pitch;
-    if (nk == 32) {
-      for (int e = threadIdx.x; e < d * (32 / VEC); e += kThreads) {
-        const int c = e / (32 / VEC), k = (e - c * (32 / VEC)) * VEC;
-        u32x4 w;
-        E* we = reinterpret_cast<E*>(&w);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) we[i] = vt[(k + i) * pitch + c];
-        st16(vblk + c * 32 + k, w);
-      }
-    } else {
-      for (int e = threadIdx.x; e < nk * d; e += kThreads) {
-        const int c = e / nk, r = e - c * nk;
-        vblk[c * 32 + kk0 + r] = vt[r * pitch + c];
-      }
     }
   }
 }
@@ -243,17 +240,20 @@ hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s) {
   const int64_t kb1 = (a.o + a.T_new - 1) / 32;
   const int nblk = (int)(kb1 - kb0 + 1);
   const int64_t grid = (int64_t)nblk * a.n_kv * a.B;
-  const size_t lds = (size_t)32 * (a.d + 1) * elt_bytes;
   if (elt_bytes == 2)
-    hipLaunchKernelGGL(append_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds, s, a, kb0, nblk);
+    hipLaunchKernelGGL(append_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, kb0, nblk);
   else
-    hipLaunchKernelGGL(append_kernel<4>, dim3((unsigned)grid), dim3(kThreads), lds, s, a, kb0, nblk);
+    hipLaunchKernelGGL(append_kernel<4>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, kb0, nblk);
   return hipGetLastError();
 }
 
-// Heads per workgroup: as many as keep its LDS (table + V tiles) within
-// kAppendRopeLds, so that at least two workgroups share a CU.
-constexpr size_t kAppendRopeLds = 64 * 1024;
+// Head groups: a workgroup rotates at most about kGroupCols (head, chunk)
+// columns per row, so that many workgroups share the work (each builds the
+// block's angle table, its only LDS).
+#ifndef SA_GROUP_COLS
+#define SA_GROUP_COLS 64
+#endif
+constexpr int kGroupCols = SA_GROUP_COLS;
 
 hipError_t launch_append_rope(const AppendRopeArgs& ar, int elt_bytes, hipStream_t s) {
   const AppendArgs& a = ar.ap;
@@ -261,15 +261,18 @@ hipError_t launch_append_rope(const AppendRopeArgs& ar, int elt_bytes, hipStream
   const int64_t kb1 = (a.o + a.T_new - 1) / 32;
   const int nblk = (int)(kb1 - kb0 + 1);
   const size_t tab = (size_t)32 * (a.d / 2) * sizeof(double2);
-  const size_t per_head = (size_t)32 * (a.d + 1) * elt_bytes;
-  int hc = tab + per_head >= kAppendRopeLds ? 1 : (int)((kAppendRopeLds - tab) / per_head);
-  if (hc > a.n_kv) hc = a.n_kv;
-  const int nhc = (a.n_kv + hc - 1) / hc;
-  const int64_t grid = (int64_t)nblk * nhc * a.B;
-  const size_t lds = tab + (size_t)hc * per_head;
+  const int cpr = a.d / 2 / (16 / elt_bytes);
+  const int n_q = ar.q_src ? ar.n_q : 0;
+  const int cols = (a.n_kv + n_q) * cpr;
+  int ngr = (cols + kGroupCols - 1) / kGroupCols;
+  if (ngr > a.n_kv + n_q) ngr = a.n_kv + n_q;
+  const int hc = (a.n_kv + ngr - 1) / ngr;                  // K heads per group
+  const int qpg = n_q ? (n_q + ngr - 1) / ngr : 0;
+  const int64_t grid = (int64_t)nblk * ngr * a.B;
+  const size_t lds = tab;
   if (elt_bytes == 2)
-    hipLaunchKernelGGL(append_rope_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc);
+    hipLaunchKernelGGL(append_rope_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc, ngr, qpg);
   else
-    hipLaunchKernelGGL(append_rope_kernel<4>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc);
+    hipLaunchKernelGGL(append_rope_kernel<4>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc, ngr, qpg);
   return hipGetLastError();
 }

@@ -47,6 +47,9 @@
 #ifndef SA_INTERLEAVE
 #define SA_INTERLEAVE 0
 #endif
+#ifndef SA_VALU_LEAD
+#define SA_VALU_LEAD 0
+#endif
 
 namespace {
 
@@ -435,16 +438,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // work side by side and only a few operands are in flight.
   auto interleave = [&]() {
     if constexpr (!SA_INTERLEAVE) return;
+    constexpr int kRd = 2 * KS + DT;                      // LDS operand reads per unit
+    constexpr int kAhead = SA_RD_AHEAD < kRd ? SA_RD_AHEAD : kRd;
     constexpr int kMf = 2 * KS * NT + DT * NT;            // MFMAs per unit
-    constexpr int kValu = (NT * 26 + kMf / 2 - 1) / (kMf / 2);
-    sched_group<0x100, SA_RD_AHEAD>();          // LDS reads
+    constexpr int kValu = (NT * 27 - SA_VALU_LEAD + kMf / 2 - 1) / (kMf / 2);
+    sched_group<0x100, kAhead>();               // LDS reads
+    if constexpr (SA_VALU_LEAD > 0) sched_group<0x002, SA_VALU_LEAD>();
 #pragma unroll
     for (int i = 0; i < kMf / 2; ++i) {
-      sched_group<0x100, 1>();
+      if (i < kRd - kAhead) sched_group<0x100, 1>();
       sched_group<0x008, 2>();                  // MFMA
       sched_group<0x002, kValu>();              // VALU
     }
   };
+
   // One unit: Sc = S(u) in, Sn = S(u+1) out (from K buffer kbn, half hn,
   // first key k0n); Pp = P(u-1) in (V buffer vbp, half hp), Pc = P(u) out;
   // S(u) can be recomputed from K buffer kbc, half hc, first key k0c.  The
