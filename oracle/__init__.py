@@ -14,6 +14,8 @@ Modules
   attention  masks, sink-augmented softmax, GQA; a per-query form and a
              dense mask-matrix form
   kvcache    append-only cache with snapshot/restore; KV byte count
+  ring       sliding-window ring cache of band layers (W rows, slot p mod W),
+             its band mask in ring coordinates, KV entry counts
 
 Sources are cited as page title + section.  The pages:
   "MoE-Xtend" README (sections DESIGN CONTRACTS, ARCHITECTURE,
@@ -21,7 +23,8 @@ Sources are cited as page title + section.  The pages:
       NOTATION)
   "GQA Attention" study note on gpt-oss (section "How it works")
   "MoE-Xtend" project summary page
-  "GPT-OSS-Lite" README and visual guide (shapes only)
+  "GPT-OSS-Lite" README (shapes; the KV-cache reduction figures) and visual
+      guide (shapes; the KV-cache calculator)
 
 Every function here is pinned by the ``-m "not gpu"`` tests against closed
 forms, special cases that reduce to library routines, brute force on tiny
