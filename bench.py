@@ -155,6 +155,93 @@ def time_prefill_step(w, sa, torch, steps, warmup):
     return layers, ms_step, b2b, in_step
 
 
+def abi_call_figures(w, L, sa, torch):
+    """Each data-moving ABI call of a prefill layer timed on its own (events
+    around KERNEL_REPEAT back-to-back calls on the layer's buffers), in
+    algorithmic GB/s: RoPE of Q out of place, the plain append, and the fused
+    rotate-Q-and-K-and-append pass the step uses."""
+    elt = 2
+    qb = w.B * w.T * w.n_q * w.d_h * elt
+    kvb = 2 * w.B * w.T * w.n_kv * w.d_h * elt
+    kr = torch.empty_like(L.k0)
+    sa.yarn_rope_apply(L.k0, L.q_offset, L.yarn, out=kr)
+    calls = {
+        "yarn_rope(q)": (lambda: sa.yarn_rope_apply(L.q0, L.q_offset, L.yarn, out=L.qw), 2 * qb),
+        "kv_cache_append": (lambda: (L.cache.restore(L.snap), L.cache.append(kr, L.v)), 2 * kvb),
+        "kv_cache_append_rope_qk": (lambda: (L.cache.restore(L.snap),
+                                             L.cache.append_rope_qk(L.q0, L.k0, L.v, L.yarn,
+                                                                    q_out=L.qw)),
+                                    2 * qb + 2 * kvb),
+    }
+    out = {}
+    for name, (fn, by) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(KERNEL_REPEAT):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / KERNEL_REPEAT * 1e3
+        out[name] = {"us": round(us, 2), "alg_mb": round(by / 1e6, 2),
+                     "gbs": round(by / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    # leave the layer as the step left it (rotated Q, appended cache)
+    run_layer(L, w, sa)
+    torch.cuda.synchronize()
+    return out
+
+
+def ring_prefill_figures(w, L, sa, torch):
+    """The band layer through a W-row ring instead of a T-row cache: stage
+    (nothing to copy at offset 0), fused RoPE + append into the stage,
+    prefill over the stage, commit of the last W rows into the ring; timed
+    over KERNEL_REPEAT back-to-back layer passes against the same passes on
+    the linear cache.  KV bytes are the caches' logical bf16 entries."""
+    W, dt = L.window, torch.bfloat16
+    kbuf = torch.empty((w.B, W, w.n_kv, w.d_h), dtype=dt, device="cuda")
+    vbuf = torch.empty(sa.v_cache_shape(w.B, W, w.n_kv, w.d_h), dtype=dt, device="cuda")
+    stage_rows = ((W - 1 + w.T + 31) // 32) * 32
+    stage = sa.KVCache.empty(w.B, stage_rows, w.n_kv, w.d_h, dtype=dt)
+    out = torch.empty_like(L.out)
+
+    def ring_pass():
+        ring = sa.KVRing(kbuf, vbuf)          # an empty ring over the same buffers (host only)
+        ring.stage(stage)
+        stage.append_rope_qk(L.q0, L.k0, L.v, L.yarn, q_out=L.qw)
+        sa.sinkattn_prefill(L.qw, stage, L.sinks, W, w.sm_scale, 0, out=out)
+        ring.commit(stage)
+        return ring
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(KERNEL_REPEAT):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / KERNEL_REPEAT
+
+    ring_ms = timed(ring_pass)
+    lin_ms = timed(lambda: run_layer(L, w, sa))
+    same = bool(torch.equal(out.view(torch.int16), L.out.view(torch.int16)))
+    row = w.n_kv * w.d_h * 2 * 2                     # K + V bytes of one position
+    n_layers = 12
+    full_b = w.B * w.capacity * row
+    return {"window": W, "layer_ms_ring": round(ring_ms, 4), "layer_ms_linear": round(lin_ms, 4),
+            "out_bitequal_linear": same,
+            "kv_bytes": {"band_layer_linear": w.B * w.capacity * row,
+                         "band_layer_ring": w.B * W * row,
+                         "stage_scratch_shared": w.B * stage_rows * row,
+                         "full_layer": full_b,
+                         "reduction_%d_alternating_layers" % n_layers:
+                             round((n_layers * full_b) /
+                                   (n_layers // 2 * full_b + n_layers // 2 * w.B * W * row), 4)}}
+
+
 def prefill_figures(w, L, ms, ms_in_step=None):
     fl = attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window)
     elt = 2
@@ -170,6 +257,43 @@ def prefill_figures(w, L, ms, ms_in_step=None):
             "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
             "alg_mb": round(by / 1e6, 2), "gbs": round(gbs, 1),
             "frac_bound": round(tf / min(PEAK_BF16_TFLOPS, fl / by * PEAK_HBM_GBS / 1e3), 4)}
+
+
+def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
+    """The band layer's decode steps on a W-row ring holding the prefix's last
+    W rows (appending the whole prefix keeps only those), restored by
+    kv_ring_load between the warmup and the timed steps."""
+    ring = sa.KVRing.empty(w.B, W, w.n_kv, w.d_h, dtype=torch.bfloat16)
+    ring.append(pk, pv)
+    saved = ring.save()
+    ws = sa.decode_workspace(ring, w.n_q)
+    qbuf = torch.empty_like(toks[0]["q"])
+    out = torch.empty_like(qbuf)
+
+    def step(s, ev=None):
+        ring.append_rope_qk(toks[s]["q"], toks[s]["k"], toks[s]["v"], y, q_out=qbuf)
+        if ev is not None:
+            ev[0].record()
+        sa.sinkattn_decode(qbuf, ring, sinks, W, w.sm_scale, workspace=ws, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for s in range(4):
+        step(s)
+    ring.load(saved)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.decode_steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(w.decode_steps):
+        step(s, evs[s])
+    t1.record()
+    torch.cuda.synchronize()
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    step_ms = t0.elapsed_time(t1) / w.decode_steps
+    return {"attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+            "kv_bytes": w.B * W * w.n_kv * w.d_h * 2 * 2}
 
 
 def decode_extra(sa, torch, steps_warm=4):
@@ -222,7 +346,10 @@ def decode_extra(sa, torch, steps_warm=4):
         res["full" if W == 0 else "band%d" % W] = {
             "attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
             "alg_mb_per_step": round(by / 1e6, 3), "gbs": round(gbs, 1),
-            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "kv_bytes": w.B * w.capacity * w.n_kv * w.d_h * 2 * 2}
+        if W > 0:
+            res["band%d_ring" % W] = ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch)
         del cache, ws, toks
         torch.cuda.empty_cache()
     return {"workload": w.name, **res}
@@ -327,6 +454,8 @@ def main():
                             "orig_ctx": w.yarn.orig_ctx}, "parallelism": "single GPU"},
         "roofline": roofline,
         "layers": per_layer,
+        "abi_calls": abi_call_figures(w, layers[full_i], sa, torch),
+        "ring": ring_prefill_figures(w, [L for L in layers if L.window > 0][0], sa, torch),
     }
     if not args.no_extra:
         g = wl.GPTOSS_PREFILL

@@ -59,10 +59,12 @@ typedef enum {
   SA_ERR_SHAPE = -2,     /* n_q % n_kv != 0, unsupported d_h, shape differs
                             from the cache's, capacity not a multiple of 32  */
   SA_ERR_DTYPE = -3,     /* unknown dtype, or dtype differs from the cache's */
-  SA_ERR_CAPACITY = -4,  /* append past capacity, or queries past the rows
-                            already in the cache                             */
-  SA_ERR_SNAPSHOT = -5,  /* snapshot of another cache, or rows below it were
-                            rewritten since it was taken                     */
+  SA_ERR_CAPACITY = -4,  /* append past capacity, queries past the rows
+                            already in the cache, or keys the queries need
+                            below the cache's first position                 */
+  SA_ERR_SNAPSHOT = -5,  /* snapshot of another cache, rows below it were
+                            rewritten since it was taken, or a ring and its
+                            stage out of step                                */
   SA_ERR_HIP = -6        /* a HIP launch error                               */
 } sa_status;
 
@@ -115,10 +117,12 @@ int yarn_rope(const void* x, void* y, int dtype, int B, int T, int n_heads, int 
               int64_t offset, const sa_yarn* yarn, void* stream);
 
 /* Opaque host-side handle of one layer's cache.  K/V storage is the
- * caller's (layout above); the handle records the shape, the offset (rows
- * written: the next append goes to row `offset` of every sequence; one
- * offset is shared by the batch), and the write log used to validate
- * snapshots. */
+ * caller's (layout above); the handle records the shape, the offset (the
+ * global position the next append writes; one offset is shared by the
+ * batch), and the write log used to validate snapshots.  A linear cache
+ * holds position p in row p - base, where base is 0 except for a stage
+ * cache filled by kv_ring_stage; a ring cache (kv_ring_create) holds p in
+ * row p mod W. */
 typedef struct sa_kv_cache sa_kv_cache;
 
 typedef struct {
@@ -134,15 +138,22 @@ typedef struct {
 int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B,
                     int64_t capacity, int n_kv, int d_h, int64_t offset);
 int kv_cache_destroy(sa_kv_cache* c);
-/* Rows written so far; -1 for a null handle. */
+/* Positions written so far (the next append's position); -1 for a null
+ * handle. */
 int64_t kv_cache_offset(const sa_kv_cache* c);
+/* Oldest position the cache holds: base for a linear cache, max(0, offset -
+ * W) for a ring; -1 for a null handle. */
+int64_t kv_cache_base(const sa_kv_cache* c);
 
 /* Append T_new rows to every sequence ("MoE-Xtend" README, KV CACHE: extend
- * writes [offset, offset+T_new) then advances offset).  k_rot: device
+ * writes [offset, offset+T_new) then advances offset; on a ring, row t goes
+ * to its slot and only the last W rows of a longer append are written).
+ * k_rot: device
  * [B, T_new, n_kv, d_h], already rotated; v: device [B, T_new, n_kv, d_h],
  * unrotated.  Rows are copied bit for bit (V into its blocked layout).  The
  * offset advances at enqueue time.  A decode step appends T_new = 1.
- * SA_ERR_CAPACITY if offset + T_new > capacity. */
+ * SA_ERR_CAPACITY if a linear cache would pass its capacity (a ring never
+ * fills). */
 int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v,
                     int T_new, void* stream);
 
@@ -162,8 +173,9 @@ int kv_cache_append_rope(sa_kv_cache* c, const void* k, const void* v,
  * the same positions: q (device [B, T_new, n_q, d_h], unrotated) is written
  * rotated to q_rot (same shape; q_rot == q rotates in place, any other
  * overlap is SA_ERR_ARG), exactly as yarn_rope(q, q_rot, offset =
- * kv_cache_offset(c)) would, sharing the angle tables with K.  q and q_rot
- * both null: same as kv_cache_append_rope. */
+ * kv_cache_offset(c)) would, sharing the angle tables with K (on a ring,
+ * every query row is rotated even where only the last W key rows are kept).
+ * q and q_rot both null: same as kv_cache_append_rope. */
 int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q,
                             const void* k, const void* v, int T_new,
                             const sa_yarn* y, void* stream);
@@ -171,9 +183,71 @@ int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q,
 /* O(1) host bookkeeping ("prefill once, decode many").  A snapshot records
  * the offset; restore rewinds the offset to it.  Restoring is refused with
  * SA_ERR_SNAPSHOT if the snapshot belongs to another cache or if any append
- * made after it started below its offset (its rows were overwritten). */
+ * made after it started below its offset (its rows were overwritten); on a
+ * ring, if anything was appended after it (use kv_ring_save/kv_ring_load).
+ * kv_ring_stage starts a stage cache's history afresh: snapshots of the
+ * stage taken before are refused. */
 int kv_cache_snapshot(const sa_kv_cache* c, sa_kv_snapshot* out);
 int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap);
+
+/* ---- Ring caches for band layers ----
+ * "GPT-OSS-Lite" README, "Why these metrics matter" and "Results": the
+ * windowed layers cache only the last W tokens while full layers keep the
+ * sequence, which is the architecture's KV-cache reduction (2T/(T+W) for
+ * alternating layers); "MoE-Xtend" README, ARCHITECTURE: with a sliding
+ * window a decode step's attention is O(W).
+ *
+ * A ring holds W rows per sequence, W = the layer's window, a positive
+ * multiple of 32 (SA_ERR_SHAPE otherwise): position p lives in row p mod W,
+ * so appending p overwrites p - W, the key that has just left the band.
+ * Buffers (caller-owned, device): K [B, W, n_kv, d_h], V [B, W/32, n_kv,
+ * d_h, 32], the cache layout above with C = W.  The ring starts empty.
+ *   - The append entry points write each row at its slot.
+ *   - sinkattn_decode needs window == W (SA_ERR_ARG otherwise): every slot
+ *     the ring holds is in the decode query's band, so min(offset, W) rows
+ *     are attended without a mask (in slot order).
+ *   - sinkattn_prefill and sinkattn_prefill_rope refuse a ring (SA_ERR_ARG):
+ *     a chunk's queries need more than W keys between them.  A chunk goes
+ *     through a linear stage cache of the same B, n_kv, d_h and dtype and a
+ *     capacity of at least W - 1 + T_q rows:
+ *        kv_ring_stage(stage, ring)                    the ring's rows
+ *        kv_cache_append_rope_qk(stage, q, q_rot, ..)  the chunk
+ *        sinkattn_prefill(q_rot, stage, .., window = W,
+ *                         q_offset = kv_cache_offset(ring))
+ *        kv_ring_commit(ring, stage)                   the last W rows back
+ *     The stage is scratch, not layer state: one stage serves every band
+ *     layer in turn, and several chunks may be appended and attended
+ *     between a stage and its commit. */
+int kv_ring_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int window,
+                   int n_kv, int d_h);
+
+/* Make `stage` (a linear cache) hold the ring's last min(offset, W - 1)
+ * positions -- all its keys that a query at position offset can see -- at
+ * rows 0.., with base = offset - that count and offset = the ring's offset.
+ * Enqueues one small copy.  SA_ERR_ARG if `ring` is not a ring or `stage`
+ * is; SA_ERR_SHAPE / SA_ERR_DTYPE if they differ in B, n_kv, d_h or dtype;
+ * SA_ERR_CAPACITY if the stage is too small. */
+int kv_ring_stage(sa_kv_cache* stage, const sa_kv_cache* ring, void* stream);
+
+/* Copy the stage's positions at or above the ring's offset (at most its
+ * last W) into the ring's slots and advance the ring's offset to the
+ * stage's.  SA_ERR_SNAPSHOT unless the stage was staged (or last committed)
+ * from this ring and the ring has not changed since, or if the stage's
+ * offset is below the ring's. */
+int kv_ring_commit(sa_kv_cache* ring, sa_kv_cache* stage, void* stream);
+
+/* Snapshot and restore of a ring by copy ("prefill once, decode many" when
+ * decode sweeps overwrite slots).  k_save, v_save: caller-owned device
+ * buffers of B*W*n_kv*d_h elements each (the ring's buffer sizes), 16-byte
+ * aligned.  kv_ring_save enqueues a copy of the ring into them and records
+ * the offset in *out; kv_ring_load enqueues the copy back and sets the
+ * offset.  The caller keeps the buffers unchanged between the two.
+ * SA_ERR_ARG for a non-ring cache; SA_ERR_SNAPSHOT for a snapshot of
+ * another cache. */
+int kv_ring_save(const sa_kv_cache* ring, void* k_save, void* v_save, sa_kv_snapshot* out,
+                 void* stream);
+int kv_ring_load(sa_kv_cache* ring, const void* k_save, const void* v_save,
+                 const sa_kv_snapshot* snap, void* stream);
 
 /* Sink attention of T_q new queries against the cache ("MoE-Xtend" README,
  * ATTENTION STACK; "GQA Attention" study note, How it works).
@@ -187,8 +261,10 @@ int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap);
  *   `window` keys including the diagonal) or { j : 0 <= j <= p } (window
  *   <= 0: full causal), and l_j = sm_scale * <q, K_j>:
  *   out = sum_{j in A} e^{l_j} V_j / (e^{sigma_h} + sum_{j in A} e^{l_j}).
- * Requires q_offset + T_q <= kv_cache_offset(c) (append first); n_kv and
- * d_h must equal the cache's.  bf16: d_h in {64, 96, 128},
+ * Requires q_offset + T_q <= kv_cache_offset(c) (append first) and every
+ * allowed key at or above kv_cache_base(c) (SA_ERR_CAPACITY); a ring is
+ * refused (SA_ERR_ARG, see kv_ring_stage); n_kv and d_h must equal the
+ * cache's.  bf16: d_h in {64, 96, 128},
  * n_q/n_kv <= 128, cache capacity below 2^31 rows (SA_ERR_SHAPE otherwise),
  * matrix-core kernel with fp32 accumulation; fp32: d_h % 8 == 0,
  * d_h <= 256, vector kernel. */

@@ -61,6 +61,13 @@ _kv_cache_create = _sig("kv_cache_create", _i32, ctypes.POINTER(_vp), _vp, _vp, 
                         _i64, _i32, _i32, _i64)
 _kv_cache_destroy = _sig("kv_cache_destroy", _i32, _vp)
 _kv_cache_offset = _sig("kv_cache_offset", _i64, _vp)
+_kv_cache_base = _sig("kv_cache_base", _i64, _vp)
+_kv_ring_create = _sig("kv_ring_create", _i32, ctypes.POINTER(_vp), _vp, _vp, _i32, _i32, _i32,
+                       _i32, _i32)
+_kv_ring_stage = _sig("kv_ring_stage", _i32, _vp, _vp, _vp)
+_kv_ring_commit = _sig("kv_ring_commit", _i32, _vp, _vp, _vp)
+_kv_ring_save = _sig("kv_ring_save", _i32, _vp, _vp, _vp, ctypes.POINTER(SaSnapshot), _vp)
+_kv_ring_load = _sig("kv_ring_load", _i32, _vp, _vp, _vp, ctypes.POINTER(SaSnapshot), _vp)
 _kv_cache_append = _sig("kv_cache_append", _i32, _vp, _vp, _vp, _i32, _vp)
 _kv_cache_append_rope = _sig("kv_cache_append_rope", _i32, _vp, _vp, _vp, _i32,
                              ctypes.POINTER(SaYarn), _vp)
@@ -210,7 +217,13 @@ class KVCache:
 
     @property
     def offset(self) -> int:
+        """Positions appended so far (the next append's position)."""
         return int(_kv_cache_offset(self._h))
+
+    @property
+    def base(self) -> int:
+        """Oldest position the cache holds (kv_cache_base)."""
+        return int(_kv_cache_base(self._h))
 
     def append(self, k_rot: torch.Tensor, v: torch.Tensor, stream=None) -> None:
         if k_rot.shape != v.shape or k_rot.dim() != 4:
@@ -279,6 +292,67 @@ class KVCache:
             self.close()
         except Exception:
             pass
+
+
+class KVRing(KVCache):
+    """A band layer's ring cache over caller-owned buffers k [B,W,n_kv,d] and
+    v [B,W/32,n_kv,d,32]: position p in row p mod W (kv_ring_create).  The
+    append methods and sinkattn_decode (window == W) take it directly; a
+    prefill chunk goes through a linear stage cache: ``ring.stage(st)``,
+    ``st.append_rope_qk(..)``, ``sinkattn_prefill(.., st, .., q_offset=
+    ring.offset)``, ``ring.commit(st)``."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor):
+        if k.dim() != 4 or v.dim() != 5:
+            raise ValueError("k must be [B,W,n_kv,d], v [B,W/32,n_kv,d,32]")
+        B, W, n_kv, d = k.shape
+        if tuple(v.shape) != v_cache_shape(B, W, n_kv, d) or v.dtype != k.dtype:
+            raise ValueError("v buffer shape/dtype does not match k")
+        self.k, self.v = k, v
+        self.B, self.capacity, self.n_kv, self.d = B, W, n_kv, d
+        self.window = W
+        self.dtype = k.dtype
+        h = _vp()
+        _check(_kv_ring_create(ctypes.byref(h), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
+                               B, W, n_kv, d))
+        self._h = h
+
+    @classmethod
+    def empty(cls, B, W, n_kv, d, dtype=torch.bfloat16, device="cuda", fill=None):
+        return super().empty(B, W, n_kv, d, dtype=dtype, device=device, fill=fill)
+
+    def stage(self, stage: KVCache, stream=None) -> KVCache:
+        """kv_ring_stage: the stage now holds the ring's rows a query at
+        position ``offset`` can see; returns the stage."""
+        _check(_kv_ring_stage(stage.handle, self._h, _stream(stream)))
+        return stage
+
+    def commit(self, stage: KVCache, stream=None) -> None:
+        """kv_ring_commit: the stage's new rows (at most the last W) into the ring."""
+        _check(_kv_ring_commit(self._h, stage.handle, _stream(stream)))
+
+    def save(self, k_save: Optional[torch.Tensor] = None, v_save: Optional[torch.Tensor] = None,
+             stream=None):
+        """kv_ring_save into (new, unless given) buffers shaped like the ring's;
+        returns (snapshot, k_save, v_save) for load()."""
+        if k_save is None:
+            k_save = torch.empty_like(self.k)
+        if v_save is None:
+            v_save = torch.empty_like(self.v)
+        if k_save.shape != self.k.shape or v_save.shape != self.v.shape:
+            raise ValueError("save buffers must be shaped like the ring's")
+        if k_save.dtype != self.dtype or v_save.dtype != self.dtype:
+            raise TypeError("save buffers must have the ring's dtype")
+        snap = SaSnapshot()
+        _check(_kv_ring_save(self._h, _dev(k_save, "k_save"), _dev(v_save, "v_save"),
+                             ctypes.byref(snap), _stream(stream)))
+        return snap, k_save, v_save
+
+    def load(self, saved, stream=None) -> None:
+        """kv_ring_load of what save() returned."""
+        snap, k_save, v_save = saved
+        _check(_kv_ring_load(self._h, _dev(k_save, "k_save"), _dev(v_save, "v_save"),
+                             ctypes.byref(snap), _stream(stream)))
 
 
 def sinkattn_prefill(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window: int,

@@ -11,8 +11,13 @@
 // 16-byte vectors of 8 keys of one coordinate; a partial block (at either
 // end of the range) moves element by element.
 //
+// A launch writes one contiguous run of cache rows; a ring cache (a band
+// layer's W rows, position p in row p mod W) is written in at most two runs
+// by the caller.
+//
 // kv_cache_append_rope does the same with unrotated K: each K row is rotated
-// at its cache row index, which is its global position (DESIGN CONTRACTS),
+// at its global position (DESIGN CONTRACTS; pos0 is the position of the
+// launch's first cache row),
 // with the arithmetic of yarn_rope (sa_rope.h), so the cache receives the
 // bits that yarn_rope followed by kv_cache_append would write.  A workgroup
 // owns one (b, 32-key block, group of heads): it moves V as above and builds
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int64_t 
   const E* vsrc = reinterpret_cast<const E*>(a.v_src);
   E* kc = reinterpret_cast<E*>(a.kc);
   E* vc = reinterpret_cast<E*>(a.vc);
-  const int64_t src_row0 = ((int64_t)b * a.T_new + (key_lo - a.o)) * a.n_kv + g;   // in rows of d
+  const int64_t src_row0 = ((int64_t)b * a.src_T + a.src_t0 + (key_lo - a.o)) * a.n_kv + g;   // in rows of d
   const int64_t dst_row0 = ((int64_t)b * a.C + key_lo) * a.n_kv + g;
   const int vpr = d / VEC;                      // vectors per row
   const int rstride = a.n_kv * d;
@@ -141,8 +146,9 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   E* vc = reinterpret_cast<E*>(a.vc);
   // element offsets of row 0, head h0 in the source and in the cache; rows
   // step by n_kv heads in both
-  const E* src0 = ksrc + (((int64_t)b * a.T_new + (key_lo - a.o)) * a.n_kv + h0) * d;
-  const E* vsrc0 = vsrc + (((int64_t)b * a.T_new + (key_lo - a.o)) * a.n_kv + h0) * d;
+  const int64_t srow = (int64_t)b * a.src_T + a.src_t0 + (key_lo - a.o);   // source row of key_lo
+  const E* src0 = ksrc + (srow * a.n_kv + h0) * d;
+  const E* vsrc0 = vsrc + (srow * a.n_kv + h0) * d;
   E* dst0 = kc + (((int64_t)b * a.C + key_lo) * a.n_kv + h0) * d;
   const int rstride = a.n_kv * d;
 
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
     if (r0 < rstep)
       for (int r = r0; r < nk; r += rstep) {
         double sn, cn;
-        sa_rope::sincos_reduced((double)(key_lo + r) * ar.inv_freq[i], &sn, &cn);
+        sa_rope::sincos_reduced((double)(a.pos0 + (key_lo - a.o) + r) * ar.inv_freq[i], &sn, &cn);
         tab[r * half + i] = make_double2(cn * ar.conc, sn * ar.conc);
       }
   }
@@ -226,14 +232,62 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
     const int qh0 = grp * qpg;
     const int nq = min(qpg, ar.n_q - qh0);
     if (nq > 0) {
-      const int64_t qoff = (((int64_t)b * a.T_new + (key_lo - a.o)) * ar.n_q + qh0) * d;
+      const int64_t qoff = (srow * ar.n_q + qh0) * d;
       rotate_rows(reinterpret_cast<const E*>(ar.q_src) + qoff, ar.n_q * d,
                   reinterpret_cast<E*>(ar.q_dst) + qoff, ar.n_q * d, nq);
     }
   }
 }
 
+// Rows of positions [p0, p0 + n) from one cache to another; a workgroup owns
+// one (b, g, run of up to 32 positions).  Source and destination rows come
+// from each side's own mapping (ring: p mod C; linear: p - base), so a run
+// may cross a 32-row V block or the ring's end on either side: K moves as
+// 16-byte row vectors, V element by element with consecutive threads on
+// consecutive keys of one coordinate (runs of 2-byte accesses).
+template <int ELT>
+__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int nrun) {
+  typedef typename std::conditional<ELT == 2, uint16_t, uint32_t>::type E;
+  constexpr int VEC = 16 / ELT;
+  const int d = a.d;
+  const int run = blockIdx.x % nrun;
+  const int rest = blockIdx.x / nrun;
+  const int g = rest % a.n_kv;
+  const int b = rest / a.n_kv;
+  const int64_t p_lo = a.p0 + (int64_t)run * 32;
+  const int nk = (int)min((int64_t)32, a.p0 + a.n - p_lo);
+  auto row_s = [&](int64_t p) { return a.ring_s ? p % a.Cs : p - a.base_s; };
+  auto row_d = [&](int64_t p) { return a.ring_d ? p % a.Cd : p - a.base_d; };
+  const E* ks = reinterpret_cast<const E*>(a.ks);
+  const E* vs = reinterpret_cast<const E*>(a.vs);
+  E* kd = reinterpret_cast<E*>(a.kd);
+  E* vd = reinterpret_cast<E*>(a.vd);
+  const int vpr = d / VEC;
+  for (int e = threadIdx.x; e < nk * vpr; e += kThreads) {
+    const int r = e / vpr, c = (e - r * vpr) * VEC;
+    const int64_t rs = row_s(p_lo + r), rd = row_d(p_lo + r);
+    st16(kd + (((int64_t)b * a.Cd + rd) * a.n_kv + g) * d + c,
+         ld16(ks + (((int64_t)b * a.Cs + rs) * a.n_kv + g) * d + c));
+  }
+  for (int e = threadIdx.x; e < nk * d; e += kThreads) {
+    const int r = e % nk, c = e / nk;
+    const int64_t rs = row_s(p_lo + r), rd = row_d(p_lo + r);
+    vd[((((int64_t)b * (a.Cd / 32) + rd / 32) * a.n_kv + g) * d + c) * 32 + rd % 32] =
+        vs[((((int64_t)b * (a.Cs / 32) + rs / 32) * a.n_kv + g) * d + c) * 32 + rs % 32];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_rows(const CopyRowsArgs& a, int elt_bytes, hipStream_t s) {
+  const int nrun = (a.n + 31) / 32;
+  const int64_t grid = (int64_t)nrun * a.n_kv * a.B;
+  if (elt_bytes == 2)
+    hipLaunchKernelGGL(copy_rows_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nrun);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel<4>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nrun);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s) {
   const int64_t kb0 = a.o / 32;

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       for (int e = threadIdx.x; e < nc * HALF; e += kThreads) {
         const int r = e / HALF, i = e - r * HALF;
         double sn, cn;
-        sa_rope::sincos_reduced((double)(a.q_offset + p0 + c0 + r) * rt.inv_freq[i], &sn, &cn);
+        sa_rope::sincos_reduced((double)(rt.pos_base + a.q_offset + p0 + c0 + r) * rt.inv_freq[i], &sn, &cn);
         tab[e] = make_double2(cn * rt.conc, sn * rt.conc);
       }
       __syncthreads();
@@ -540,6 +540,7 @@ hipError_t launch_d(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
                        dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
   } else {
     rt.conc = 0.0;
+    rt.pos_base = 0;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, false>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
   }

@@ -19,18 +19,37 @@ struct RopeArgs {
 hipError_t launch_rope(const RopeArgs& a, int elt_bytes, hipStream_t s);
 
 struct AppendArgs {
-  const void* k_src;
+  const void* k_src;    // [B, src_T, n_kv, d]
   const void* v_src;
   void* kc;
   void* vc;
   int B, T_new, n_kv, d;
-  int64_t C, o;
+  int64_t C, o;         // cache rows [o, o + T_new) receive source rows
+  int src_T, src_t0;    //   [src_t0, src_t0 + T_new) of each sequence
+  int64_t pos0;         // global position of cache row o (for the rotation)
 };
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, hipStream_t s);
 
+// Copy the rows of positions [p0, p0 + n) from one cache to another (K rows
+// and blocked V).  Each side maps a position to a row: a ring holds p at
+// row p mod C, a linear cache at row p - base.
+struct CopyRowsArgs {
+  const void* ks;
+  const void* vs;
+  void* kd;
+  void* vd;
+  int64_t Cs, Cd;       // capacities (rows, multiples of 32)
+  int64_t base_s, base_d;
+  int ring_s, ring_d;
+  int64_t p0;
+  int n;
+  int B, n_kv, d;
+};
+hipError_t launch_copy_rows(const CopyRowsArgs& a, int elt_bytes, hipStream_t s);
+
 struct AppendRopeArgs {  // rotate K rows at their cache positions, then append
   AppendArgs ap;         // k_src holds unrotated rows
-  const void* q_src;     // optional [B, T_new, n_q, d]: rotated at the same
+  const void* q_src;     // optional [B, src_T, n_q, d]: rotated at the same
   void* q_dst;           //   positions into q_dst (may be q_src); null: none
   int n_q;
   double conc;
@@ -46,10 +65,12 @@ struct AttnArgs {
   void* out;            // [B, T_q, n_q, d]
   int B, T_q, n_q, n_kv, d, q_mult, window;
   int64_t C;            // capacity (rows)
-  int64_t q_offset;     // global position of query 0
+  int64_t q_offset;     // cache row of query 0 (its global position minus
+                        //   the cache's base; masks use row differences)
   float sm_scale;
 };
 struct RopeTab {         // YaRN tables for rotating Q inside the prefill kernel
+  int64_t pos_base;     // global position of cache row 0 (q_offset is a row)
   double conc;
   double inv_freq[SA_MAX_HALF];
 };

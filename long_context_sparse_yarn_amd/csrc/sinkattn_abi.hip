@@ -10,6 +10,7 @@
 #include <new>
 #include <string>
 #include <vector>
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/sinkattn.h"
@@ -73,6 +74,9 @@ std::atomic<uint64_t> g_next_id{1};
 
 }  // namespace
 
+// Offsets, high-water marks and rewrite records are global positions.  A
+// linear cache holds position p in row p - base (base is 0 unless the cache
+// was filled by kv_ring_stage); a ring holds p in row p mod capacity.
 struct sa_kv_cache {
   void* k;
   void* v;
@@ -80,12 +84,17 @@ struct sa_kv_cache {
   int B, n_kv, d_h;
   int64_t capacity;
   int64_t offset;
+  int64_t base;
+  bool ring;
   uint64_t id;
   uint64_t stamp;
-  // (stamp, first row) of appends that began below the high-water mark,
-  // i.e. that may have overwritten rows some snapshot relies on.
+  // (stamp, first position) of appends that began below the high-water
+  // mark, i.e. that may have overwritten rows some snapshot relies on.
   std::vector<std::pair<uint64_t, int64_t>> rewrites;
   int64_t high_water;
+  // a stage cache: the ring it was staged from and that ring's stamp then
+  uint64_t staged_from;
+  uint64_t staged_stamp;
 };
 
 extern "C" {
@@ -149,8 +158,9 @@ int yarn_rope_apply(void* x, int dtype, int B, int T, int n_heads, int d_h, int6
   return yarn_rope(x, x, dtype, B, T, n_heads, d_h, offset, y, stream);
 }
 
-int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity,
-                    int n_kv, int d_h, int64_t offset) {
+namespace {
+static int cache_new(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity, int n_kv,
+              int d_h, int64_t offset, bool ring) {
   if (!out || !k || !v) return fail(SA_ERR_ARG, "null argument");
   if (misaligned(k) || misaligned(v)) return fail(SA_ERR_ARG, "k and v must be 16-byte aligned");
   if (!elt_bytes(dtype)) return fail(SA_ERR_DTYPE, "unknown dtype %d", dtype);
@@ -172,11 +182,28 @@ int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64
   c->d_h = d_h;
   c->capacity = capacity;
   c->offset = offset;
+  c->base = 0;
+  c->ring = ring;
   c->high_water = offset;
   c->id = g_next_id.fetch_add(1);
   c->stamp = 0;
+  c->staged_from = 0;
+  c->staged_stamp = 0;
   *out = c;
   return ok();
+}
+}  // namespace
+
+int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity,
+                    int n_kv, int d_h, int64_t offset) {
+  return cache_new(out, k, v, dtype, B, capacity, n_kv, d_h, offset, false);
+}
+
+int kv_ring_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int window, int n_kv,
+                   int d_h) {
+  if (window <= 0 || window % 32)
+    return fail(SA_ERR_SHAPE, "a ring's window must be a positive multiple of 32 (got %d)", window);
+  return cache_new(out, k, v, dtype, B, window, n_kv, d_h, 0, true);
 }
 
 int kv_cache_destroy(sa_kv_cache* c) {
@@ -187,42 +214,91 @@ int kv_cache_destroy(sa_kv_cache* c) {
 
 int64_t kv_cache_offset(const sa_kv_cache* c) { return c ? c->offset : -1; }
 
+int64_t kv_cache_base(const sa_kv_cache* c) {
+  if (!c) return -1;
+  if (c->ring) return c->offset > c->capacity ? c->offset - c->capacity : 0;
+  return c->base;
+}
+
 namespace {
-// Checks shared by the append entry points; fills the launch arguments.
-int append_args(sa_kv_cache* c, const void* k, const void* v, int T_new, AppendArgs* a) {
+// Launch plan of an append: one run of cache rows, or two for a ring whose
+// rows wrap past its end.  Source rows [0, t0) are not written: a ring of W
+// rows keeps only the last W rows of a longer append.
+struct AppendPlan {
+  AppendArgs seg[2];
+  int nseg;
+  int t0;
+};
+// Checks shared by the append entry points; fills the plan.
+static int append_plan(sa_kv_cache* c, const void* k, const void* v, int T_new, AppendPlan* pl) {
   if (!c || !k || !v) return fail(SA_ERR_ARG, "null argument");
   if (misaligned(k) || misaligned(v)) return fail(SA_ERR_ARG, "k and v must be 16-byte aligned");
   if (T_new <= 0) return fail(SA_ERR_ARG, "T_new must be positive");
-  if (c->offset + T_new > c->capacity)
-    return fail(SA_ERR_CAPACITY, "append of %d rows at offset %lld exceeds capacity %lld", T_new,
-                (long long)c->offset, (long long)c->capacity);
-  a->k_src = k;
-  a->v_src = v;
-  a->kc = c->k;
-  a->vc = c->v;
-  a->B = c->B;
-  a->T_new = T_new;
-  a->n_kv = c->n_kv;
-  a->d = c->d_h;
-  a->C = c->capacity;
-  a->o = c->offset;
+  AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.k_src = k;
+  a.v_src = v;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.B = c->B;
+  a.n_kv = c->n_kv;
+  a.d = c->d_h;
+  a.C = c->capacity;
+  a.src_T = T_new;
+  if (!c->ring) {
+    const int64_t row = c->offset - c->base;
+    if (row + T_new > c->capacity)
+      return fail(SA_ERR_CAPACITY, "append of %d rows at row %lld exceeds capacity %lld", T_new,
+                  (long long)row, (long long)c->capacity);
+    a.T_new = T_new;
+    a.o = row;
+    a.src_t0 = 0;
+    a.pos0 = c->offset;
+    pl->seg[0] = a;
+    pl->nseg = 1;
+    pl->t0 = 0;
+    return SA_OK;
+  }
+  const int64_t W = c->capacity;
+  const int t0 = T_new > W ? (int)(T_new - W) : 0;
+  const int n = T_new - t0;
+  const int64_t p = c->offset + t0;                  // position of the first kept row
+  const int64_t s0 = p % W;
+  const int n1 = (int)std::min<int64_t>(n, W - s0);
+  a.T_new = n1;
+  a.o = s0;
+  a.src_t0 = t0;
+  a.pos0 = p;
+  pl->seg[0] = a;
+  pl->nseg = 1;
+  if (n1 < n) {                                      // wraps to row 0
+    a.T_new = n - n1;
+    a.o = 0;
+    a.src_t0 = t0 + n1;
+    a.pos0 = p + n1;
+    pl->seg[1] = a;
+    pl->nseg = 2;
+  }
+  pl->t0 = t0;
   return SA_OK;
 }
 // Bookkeeping after an append of T_new rows was enqueued.
-void appended(sa_kv_cache* c, int T_new) {
+static void appended(sa_kv_cache* c, int T_new) {
   c->stamp += 1;
-  if (c->offset < c->high_water) c->rewrites.emplace_back(c->stamp, c->offset);
+  if (!c->ring && c->offset < c->high_water) c->rewrites.emplace_back(c->stamp, c->offset);
   c->offset += T_new;
   if (c->offset > c->high_water) c->high_water = c->offset;
 }
 }  // namespace
 
 int kv_cache_append(sa_kv_cache* c, const void* k_rot, const void* v, int T_new, void* stream) {
-  AppendArgs a;
-  int st = append_args(c, k_rot, v, T_new, &a);
+  AppendPlan pl;
+  int st = append_plan(c, k_rot, v, T_new, &pl);
   if (st != SA_OK) return st;
-  hipError_t e = launch_append(a, elt_bytes(c->dtype), (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  for (int i = 0; i < pl.nseg; ++i) {
+    hipError_t e = launch_append(pl.seg[i], elt_bytes(c->dtype), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
   appended(c, T_new);
   return ok();
 }
@@ -236,7 +312,8 @@ int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q,
                             const void* v, int T_new, const sa_yarn* y, void* stream) {
   AppendRopeArgs a;
   memset(&a, 0, sizeof a);
-  int st = append_args(c, k, v, T_new, &a.ap);
+  AppendPlan pl;
+  int st = append_plan(c, k, v, T_new, &pl);
   if (st != SA_OK) return st;
   if (q || q_rot) {
     if (!q || !q_rot) return fail(SA_ERR_ARG, "q and q_rot must both be given");
@@ -255,8 +332,32 @@ int kv_cache_append_rope_qk(sa_kv_cache* c, const void* q, void* q_rot, int n_q,
     return fail(SA_ERR_SHAPE, "bf16 rotate-and-append needs d_h %% 16 == 0, got %d", c->d_h);
   st = yarn_table(y, c->d_h, a.inv_freq, &a.conc);
   if (st != SA_OK) return st;
-  hipError_t e = launch_append_rope(a, elt_bytes(c->dtype), (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  const int eb = elt_bytes(c->dtype);
+  if (a.q_src && pl.t0 > 0) {
+    // a ring keeps only the last rows of this append, but every query row is
+    // rotated: Q goes through yarn_rope's kernel (same bits) on its own
+    RopeArgs r;
+    memset(&r, 0, sizeof r);
+    r.src = a.q_src;
+    r.x = a.q_dst;
+    r.offset = c->offset;
+    r.BT = c->B * T_new;
+    r.T = T_new;
+    r.H = a.n_q;
+    r.d = c->d_h;
+    r.conc = a.conc;
+    memcpy(r.inv_freq, a.inv_freq, sizeof r.inv_freq);
+    if ((int64_t)c->B * T_new > INT32_MAX) return fail(SA_ERR_ARG, "B*T_new too large");
+    hipError_t e = launch_rope(r, eb, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
+    a.q_src = nullptr;
+    a.q_dst = nullptr;
+  }
+  for (int i = 0; i < pl.nseg; ++i) {
+    a.ap = pl.seg[i];
+    hipError_t e = launch_append_rope(a, eb, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
   appended(c, T_new);
   return ok();
 }
@@ -274,11 +375,131 @@ int kv_cache_restore(sa_kv_cache* c, const sa_kv_snapshot* snap) {
   if (snap->cache_id != c->id) return fail(SA_ERR_SNAPSHOT, "snapshot belongs to another cache");
   if (snap->stamp > c->stamp || snap->offset < 0 || snap->offset > c->high_water)
     return fail(SA_ERR_SNAPSHOT, "snapshot is not from this cache's history");
+  if (c->ring && snap->stamp != c->stamp)
+    return fail(SA_ERR_SNAPSHOT, "a ring overwrites its rows as it goes: rows were appended since "
+                                 "the snapshot (restore a ring with kv_ring_load)");
   for (const auto& w : c->rewrites)
     if (w.first > snap->stamp && w.second < snap->offset)
       return fail(SA_ERR_SNAPSHOT, "row %lld below the snapshot offset %lld was rewritten",
                   (long long)w.second, (long long)snap->offset);
   c->offset = snap->offset;
+  return ok();
+}
+
+namespace {
+static bool same_layout(const sa_kv_cache* a, const sa_kv_cache* b) {
+  return a->B == b->B && a->n_kv == b->n_kv && a->d_h == b->d_h;
+}
+static CopyRowsArgs copy_args(const sa_kv_cache* src, sa_kv_cache* dst, int64_t p0, int n) {
+  CopyRowsArgs a;
+  a.ks = src->k;
+  a.vs = src->v;
+  a.kd = dst->k;
+  a.vd = dst->v;
+  a.Cs = src->capacity;
+  a.Cd = dst->capacity;
+  a.base_s = src->base;
+  a.base_d = dst->base;
+  a.ring_s = src->ring;
+  a.ring_d = dst->ring;
+  a.p0 = p0;
+  a.n = n;
+  a.B = src->B;
+  a.n_kv = src->n_kv;
+  a.d = src->d_h;
+  return a;
+}
+}  // namespace
+
+int kv_ring_stage(sa_kv_cache* stage, const sa_kv_cache* ring, void* stream) {
+  if (!stage || !ring) return fail(SA_ERR_ARG, "null argument");
+  if (!ring->ring || stage->ring)
+    return fail(SA_ERR_ARG, "kv_ring_stage copies a ring cache into a linear one");
+  if (!same_layout(stage, ring)) return fail(SA_ERR_SHAPE, "stage and ring differ in B/n_kv/d_h");
+  if (stage->dtype != ring->dtype) return fail(SA_ERR_DTYPE, "stage and ring differ in dtype");
+  const int64_t n_prev = std::min<int64_t>(ring->offset, ring->capacity - 1);
+  if (n_prev > stage->capacity)
+    return fail(SA_ERR_CAPACITY, "stage of %lld rows cannot hold the ring's %lld rows",
+                (long long)stage->capacity, (long long)n_prev);
+  if (n_prev > 0) {
+    sa_kv_cache tmp = *stage;          // the destination mapping after staging
+    tmp.base = ring->offset - n_prev;
+    hipError_t e = launch_copy_rows(copy_args(ring, &tmp, ring->offset - n_prev, (int)n_prev),
+                                    elt_bytes(ring->dtype), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ring copy launch");
+  }
+  stage->base = ring->offset - n_prev;
+  stage->offset = ring->offset;
+  stage->high_water = ring->offset;
+  stage->rewrites.clear();
+  stage->id = g_next_id.fetch_add(1);   // a new history: older snapshots are refused
+  stage->stamp = 0;
+  stage->staged_from = ring->id;
+  stage->staged_stamp = ring->stamp;
+  return ok();
+}
+
+int kv_ring_commit(sa_kv_cache* ring, sa_kv_cache* stage, void* stream) {
+  if (!stage || !ring) return fail(SA_ERR_ARG, "null argument");
+  if (!ring->ring || stage->ring)
+    return fail(SA_ERR_ARG, "kv_ring_commit copies a linear stage cache into a ring");
+  if (stage->staged_from != ring->id || stage->staged_stamp != ring->stamp)
+    return fail(SA_ERR_SNAPSHOT, "the stage was not staged from this ring, or the ring changed since");
+  if (stage->offset < ring->offset)
+    return fail(SA_ERR_SNAPSHOT, "the stage (offset %lld) is behind the ring (offset %lld)",
+                (long long)stage->offset, (long long)ring->offset);
+  const int64_t p0 = std::max(ring->offset, stage->offset - ring->capacity);
+  const int n = (int)(stage->offset - p0);
+  if (n > 0) {
+    hipError_t e = launch_copy_rows(copy_args(stage, ring, p0, n), elt_bytes(ring->dtype),
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ring copy launch");
+  }
+  ring->stamp += 1;
+  ring->offset = stage->offset;
+  if (ring->offset > ring->high_water) ring->high_water = ring->offset;
+  stage->staged_stamp = ring->stamp;
+  return ok();
+}
+
+namespace {
+static int ring_copy(const sa_kv_cache* ring, void* kd, const void* ks, void* vd, const void* vs,
+              void* stream) {
+  const size_t bytes = (size_t)ring->B * ring->capacity * ring->n_kv * ring->d_h * elt_bytes(ring->dtype);
+  hipError_t e = hipMemcpyAsync(kd, ks, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(vd, vs, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ring copy");
+  return SA_OK;
+}
+}  // namespace
+
+int kv_ring_save(const sa_kv_cache* ring, void* k_save, void* v_save, sa_kv_snapshot* out,
+                 void* stream) {
+  if (!ring || !k_save || !v_save || !out) return fail(SA_ERR_ARG, "null argument");
+  if (!ring->ring) return fail(SA_ERR_ARG, "kv_ring_save takes a ring cache");
+  if (misaligned(k_save) || misaligned(v_save))
+    return fail(SA_ERR_ARG, "save buffers must be 16-byte aligned");
+  int st = ring_copy(ring, k_save, ring->k, v_save, ring->v, stream);
+  if (st != SA_OK) return st;
+  out->offset = ring->offset;
+  out->cache_id = ring->id;
+  out->stamp = ring->stamp;
+  return ok();
+}
+
+int kv_ring_load(sa_kv_cache* ring, const void* k_save, const void* v_save,
+                 const sa_kv_snapshot* snap, void* stream) {
+  if (!ring || !k_save || !v_save || !snap) return fail(SA_ERR_ARG, "null argument");
+  if (!ring->ring) return fail(SA_ERR_ARG, "kv_ring_load takes a ring cache");
+  if (snap->cache_id != ring->id) return fail(SA_ERR_SNAPSHOT, "snapshot belongs to another cache");
+  if (snap->offset < 0 || snap->stamp > ring->stamp)
+    return fail(SA_ERR_SNAPSHOT, "snapshot is not from this cache's history");
+  if (misaligned(k_save) || misaligned(v_save))
+    return fail(SA_ERR_ARG, "save buffers must be 16-byte aligned");
+  int st = ring_copy(ring, ring->k, k_save, ring->v, v_save, stream);
+  if (st != SA_OK) return st;
+  ring->stamp += 1;
+  ring->offset = snap->offset;
   return ok();
 }
 
@@ -298,15 +519,24 @@ static int check_attn(const void* q, const sa_kv_cache* c, const float* sinks, c
 namespace {
 // Shared by the prefill entry points; yarn != nullptr: q is unrotated and the
 // bf16 kernel rotates it first.
-int prefill_common(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
+static int prefill_common(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
                    int T_q, int n_q, int n_kv, int d_h, int window, float sm_scale,
                    int64_t q_offset, const sa_yarn* yarn, void* stream) {
   int st = check_attn(q, c, sinks, out, B, T_q, n_q, n_kv, d_h);
   if (st != SA_OK) return st;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SA_ERR_ARG, "sm_scale must be finite and > 0");
+  if (c->ring)
+    return fail(SA_ERR_ARG, "a ring cache serves decode; attend a chunk through a stage cache "
+                            "(kv_ring_stage)");
   if (q_offset < 0 || q_offset + T_q > c->offset)
     return fail(SA_ERR_CAPACITY, "queries [%lld, %lld) reach past the %lld rows in the cache",
                 (long long)q_offset, (long long)(q_offset + T_q), (long long)c->offset);
+  {
+    const int64_t lowest = window > 0 ? std::max<int64_t>(0, q_offset - window + 1) : 0;
+    if (lowest < c->base)
+      return fail(SA_ERR_CAPACITY, "keys from position %lld are needed but the cache starts at %lld",
+                  (long long)lowest, (long long)c->base);
+  }
   const int q_mult = n_q / n_kv;
   if (c->dtype == SA_BF16) {
     if (d_h != 64 && d_h != 96 && d_h != 128)
@@ -316,6 +546,7 @@ int prefill_common(const void* q, const sa_kv_cache* c, const float* sinks, void
       return fail(SA_ERR_SHAPE, "bf16 prefill needs a capacity below 2^31 rows");
   }
   RopeTab rt;
+  rt.pos_base = c->base;
   if (yarn) {
     if (c->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "in-kernel Q rotation needs a bf16 cache");
     st = yarn_table(yarn, d_h, rt.inv_freq, &rt.conc);
@@ -337,7 +568,7 @@ int prefill_common(const void* q, const sa_kv_cache* c, const float* sinks, void
   a.q_mult = q_mult;
   a.window = window > 0 ? window : 0;
   a.C = c->capacity;
-  a.q_offset = q_offset;
+  a.q_offset = q_offset - c->base;
   a.sm_scale = sm_scale;
   hipError_t e = c->dtype == SA_BF16
                      ? launch_prefill_bf16(a, yarn ? &rt : nullptr, (hipStream_t)stream)
@@ -375,6 +606,24 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
   if (st != SA_OK) return st;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SA_ERR_ARG, "sm_scale must be finite and > 0");
   if (c->offset < 1) return fail(SA_ERR_CAPACITY, "decode needs the step's row appended first");
+  // rows handed to the kernel: a ring holds exactly the band (every live
+  // slot is allowed, so it is attended as min(offset, W) unmasked rows); a
+  // linear cache holds position p at row p - base
+  int64_t q_row, win;
+  if (c->ring) {
+    if (window != c->capacity)
+      return fail(SA_ERR_ARG, "a ring of %lld rows serves a band of exactly that width (window %d)",
+                  (long long)c->capacity, window);
+    q_row = std::min(c->offset, c->capacity) - 1;
+    win = 0;
+  } else {
+    const int64_t lowest = window > 0 ? std::max<int64_t>(0, c->offset - window) : 0;
+    if (lowest < c->base)
+      return fail(SA_ERR_CAPACITY, "keys from position %lld are needed but the cache starts at %lld",
+                  (long long)lowest, (long long)c->base);
+    q_row = c->offset - 1 - c->base;
+    win = window > 0 ? window : 0;
+  }
   const int q_mult = n_q / n_kv;
   AttnArgs a;
   a.q = q;
@@ -388,9 +637,9 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
   a.n_kv = n_kv;
   a.d = d_h;
   a.q_mult = q_mult;
-  a.window = window > 0 ? window : 0;
+  a.window = (int)win;
   a.C = c->capacity;
-  a.q_offset = c->offset - 1;
+  a.q_offset = q_row;
   a.sm_scale = sm_scale;
   hipError_t e;
   if (c->dtype == SA_BF16) {
@@ -400,7 +649,8 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
     const size_t need = sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, c->capacity);
     if (!workspace || ws_bytes < need || misaligned(workspace))
       return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    const int64_t span = a.window > 0 ? (a.window < c->offset ? a.window : c->offset) : c->offset;
+    const int64_t rows = q_row + 1;
+    const int64_t span = a.window > 0 ? std::min<int64_t>(a.window, rows) : rows;
     DecodeArgs da;
     da.at = a;
     da.ws = reinterpret_cast<float*>(workspace);

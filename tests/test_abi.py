@@ -200,3 +200,54 @@ def test_decode_workspace_size_bound():
     b = B._sinkattn_decode_ws(8, 64, 8, 64, 256)
     assert a >= b > 0
     assert B._sinkattn_decode_ws(8, 63, 8, 64, 256) == 0
+
+
+def ring(dtype=0, Bn=2, W=128, n_kv=2, d=64):
+    h = ctypes.c_void_p()
+    st = B._kv_ring_create(ctypes.byref(h), FAKE_K, FAKE_V, dtype, Bn, W, n_kv, d)
+    return st, h
+
+
+def test_ring_create_and_host_bookkeeping():
+    assert ring(W=100)[0] == SA_ERR_SHAPE                 # window not a multiple of 32
+    assert ring(W=0)[0] == SA_ERR_SHAPE
+    assert ring(dtype=5)[0] == SA_ERR_DTYPE
+    st, r = ring()
+    assert st == SA_OK
+    assert B._kv_cache_offset(r) == 0 and B._kv_cache_base(r) == 0
+    st, lin = create(Bn=2, C=256, n_kv=2, d=64, offset=0)
+    q, o, s = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000)
+    # a ring is never attended by prefill; decode needs the step's row first
+    P = B._sinkattn_prefill
+    assert P(q, r, s, o, 2, 1, 8, 2, 64, 128, 0.125, 0, None) == SA_ERR_ARG
+    assert "stage" in sa.last_error()
+    assert B._sinkattn_decode(q, r, s, o, 2, 8, 2, 64, 128, 0.125, o, 1 << 20, None) == SA_ERR_CAPACITY
+    # staging: direction, shapes and dtype checked; an empty ring stages nothing
+    ST, CM = B._kv_ring_stage, B._kv_ring_commit
+    assert ST(r, lin, None) == SA_ERR_ARG                 # arguments swapped
+    st, r2 = ring()
+    assert ST(r2, r, None) == SA_ERR_ARG                  # stage must be linear
+    st, lin3 = create(Bn=2, C=256, n_kv=2, d=96)
+    assert ST(lin3, r, None) == SA_ERR_SHAPE
+    st, linf = create(dtype=1, Bn=2, C=256, n_kv=2, d=64)
+    assert ST(linf, r, None) == SA_ERR_DTYPE
+    assert CM(r, lin, None) == SA_ERR_SNAPSHOT            # never staged from r
+    assert ST(lin, r, None) == SA_OK                      # nothing to copy: no launch
+    assert B._kv_cache_offset(lin) == 0 and B._kv_cache_base(lin) == 0
+    assert CM(r2, lin, None) == SA_ERR_SNAPSHOT           # staged from another ring
+    assert CM(r, lin, None) == SA_OK                      # nothing new: no launch
+    assert CM(r, lin, None) == SA_OK                      # re-commit after commit is fine
+    # save/load: argument checks before any copy
+    snap = B.SaSnapshot()
+    ks, vs = ctypes.c_void_p(0x70000), ctypes.c_void_p(0x80000)
+    assert B._kv_ring_save(lin, ks, vs, ctypes.byref(snap), None) == SA_ERR_ARG   # not a ring
+    assert B._kv_ring_save(r, None, vs, ctypes.byref(snap), None) == SA_ERR_ARG
+    assert B._kv_ring_save(r, ctypes.c_void_p(0x70008), vs, ctypes.byref(snap), None) == SA_ERR_ARG
+    assert B._kv_cache_snapshot(r2, ctypes.byref(snap)) == SA_OK
+    assert B._kv_ring_load(r, ks, vs, ctypes.byref(snap), None) == SA_ERR_SNAPSHOT  # foreign
+    assert B._kv_ring_load(lin, ks, vs, ctypes.byref(snap), None) == SA_ERR_ARG
+    # O(1) restore of a ring with nothing appended since the snapshot is allowed
+    assert B._kv_cache_snapshot(r, ctypes.byref(snap)) == SA_OK
+    assert B._kv_cache_restore(r, ctypes.byref(snap)) == SA_OK
+    for h in (r, r2, lin, lin3, linf):
+        B._kv_cache_destroy(h)
