@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   const int nk = (int)(key_hi - key_lo);
   const int kk0 = (int)(key_lo - kb * 32);
 
-  double2* tab = reinterpret_cast<double2*>(smem);                      // [32][half]
+  double2* tab = reinterpret_cast<double2*>(smem);                      // [32][half] fp64
+  float2* tab32 = reinterpret_cast<float2*>(tab + 32 * half);           // [32][half] fp32 (bf16)
   const E* ksrc = reinterpret_cast<const E*>(a.k_src);
   const E* vsrc = reinterpret_cast<const E*>(a.v_src);
   E* kc = reinterpret_cast<E*>(a.kc);
@@ -165,49 +166,42 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
       for (int r = r0; r < nk; r += rstep) {
         double sn, cn;
         sa_rope::sincos_reduced((double)(a.pos0 + (key_lo - a.o) + r) * ar.inv_freq[i], &sn, &cn);
-        tab[r * half + i] = make_double2(cn * ar.conc, sn * ar.conc);
+        const double cc = cn * ar.conc, ss = sn * ar.conc;
+        tab[r * half + i] = make_double2(cc, ss);
+        if constexpr (ELT == 2) tab32[r * half + i] = make_float2((float)cc, (float)ss);
       }
   }
   __syncthreads();
   // Rotation of nheads heads of each of the nk rows: thread -> (head,
   // 8-pair chunk) column; both halves of the chunk in, both rotated halves
   // out (reads finish before writes, so src may equal dst).
+  const float k2 = sa_rope::bf16_rot_k2(ar.conc);
   auto rotate_rows = [&](const E* src, int src_rstride, E* dst, int dst_rstride, int nheads) {
     const int cpr = half / VEC;                 // chunks per head
     const int per_row = nheads * cpr;
     auto one = [&](int r, int hh, int c) {
       const E* row = src + r * src_rstride + hh * d;
       const u32x4 uv = ld16(row + c), vv = ld16(row + c + half);
-      const E* ue = reinterpret_cast<const E*>(&uv);
-      const E* ve = reinterpret_cast<const E*>(&vv);
-      const double2* t = &tab[r * half + c];
-      u32x4 w1, w2;
-      E* o1 = reinterpret_cast<E*>(&w1);
-      E* o2 = reinterpret_cast<E*>(&w2);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        double u, v;
-        if constexpr (ELT == 2) {
-          u = (double)bf16_to_f32(ue[i]);
-          v = (double)bf16_to_f32(ve[i]);
-        } else {
-          u = (double)__uint_as_float(ue[i]);
-          v = (double)__uint_as_float(ve[i]);
-        }
-        const double2 cs = t[i];
-        const double y1 = sa_rope::rot_first(u, v, cs.x, cs.y);
-        const double y2 = sa_rope::rot_second(u, v, cs.x, cs.y);
-        if constexpr (ELT == 2) {
-          o1[i] = (E)f64_to_bf16_bits(y1);
-          o2[i] = (E)f64_to_bf16_bits(y2);
-        } else {
-          o1[i] = __float_as_uint((float)y1);
-          o2[i] = __float_as_uint((float)y2);
-        }
-      }
       E* out = dst + r * dst_rstride + hh * d;
-      st16(out + c, w1);
-      st16(out + c + half, w2);
+      if constexpr (ELT == 2) {   // fp32 where it rounds like fp64 (sa_rope.h)
+        u32x4 w1, w2;
+        sa_rope::rot8_bf16(uv, vv, &tab32[r * half + c], &tab[r * half + c], k2, &w1, &w2);
+        st16(out + c, w1);
+        st16(out + c + half, w2);
+      } else {                    // fp32 rows: the fp64 rotation rounded to fp32
+        const double2* t = &tab[r * half + c];
+        f32x4 o1, o2;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const double u = (double)__uint_as_float(uv[i]);
+          const double v = (double)__uint_as_float(vv[i]);
+          const double2 cs = t[i];
+          o1[i] = (float)sa_rope::rot_first(u, v, cs.x, cs.y);
+          o2[i] = (float)sa_rope::rot_second(u, v, cs.x, cs.y);
+        }
+        *reinterpret_cast<f32x4*>(out + c) = o1;
+        *reinterpret_cast<f32x4*>(out + c + half) = o2;
+      }
     };
     if (per_row <= kThreads) {                  // fixed column, rows stepping
       const int rstep = kThreads / per_row;
@@ -256,8 +250,12 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int
   const int b = rest / a.n_kv;
   const int64_t p_lo = a.p0 + (int64_t)run * 32;
   const int nk = (int)min((int64_t)32, a.p0 + a.n - p_lo);
-  auto row_s = [&](int64_t p) { return a.ring_s ? p % a.Cs : p - a.base_s; };
-  auto row_d = [&](int64_t p) { return a.ring_d ? p % a.Cd : p - a.base_d; };
+  // rows of p_lo on both sides (one modulo per workgroup); row p_lo + r is
+  // then a step with at most one wrap
+  const int64_t rs0 = a.ring_s ? p_lo % a.Cs : p_lo - a.base_s;
+  const int64_t rd0 = a.ring_d ? p_lo % a.Cd : p_lo - a.base_d;
+  auto row_s = [&](int r) { const int64_t x = rs0 + r; return (a.ring_s && x >= a.Cs) ? x - a.Cs : x; };
+  auto row_d = [&](int r) { const int64_t x = rd0 + r; return (a.ring_d && x >= a.Cd) ? x - a.Cd : x; };
   const E* ks = reinterpret_cast<const E*>(a.ks);
   const E* vs = reinterpret_cast<const E*>(a.vs);
   E* kd = reinterpret_cast<E*>(a.kd);
@@ -265,15 +263,18 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyRowsArgs a, int
   const int vpr = d / VEC;
   for (int e = threadIdx.x; e < nk * vpr; e += kThreads) {
     const int r = e / vpr, c = (e - r * vpr) * VEC;
-    const int64_t rs = row_s(p_lo + r), rd = row_d(p_lo + r);
-    st16(kd + (((int64_t)b * a.Cd + rd) * a.n_kv + g) * d + c,
-         ld16(ks + (((int64_t)b * a.Cs + rs) * a.n_kv + g) * d + c));
+    st16(kd + (((int64_t)b * a.Cd + row_d(r)) * a.n_kv + g) * d + c,
+         ld16(ks + (((int64_t)b * a.Cs + row_s(r)) * a.n_kv + g) * d + c));
   }
-  for (int e = threadIdx.x; e < nk * d; e += kThreads) {
-    const int r = e % nk, c = e / nk;
-    const int64_t rs = row_s(p_lo + r), rd = row_d(p_lo + r);
-    vd[((((int64_t)b * (a.Cd / 32) + rd / 32) * a.n_kv + g) * d + c) * 32 + rd % 32] =
-        vs[((((int64_t)b * (a.Cs / 32) + rs / 32) * a.n_kv + g) * d + c) * 32 + rs % 32];
+  // V: consecutive threads on consecutive keys of one coordinate
+  const E* vsb = vs + (((int64_t)b * (a.Cs / 32)) * a.n_kv + g) * (int64_t)d * 32;
+  E* vdb = vd + (((int64_t)b * (a.Cd / 32)) * a.n_kv + g) * (int64_t)d * 32;
+  const int64_t blk_s = (int64_t)a.n_kv * d * 32, blk_d = blk_s;   // elements per 32-row block
+  for (int e = threadIdx.x; e < 32 * d; e += kThreads) {
+    const int r = e & 31, c = e >> 5;
+    if (r >= nk) continue;
+    const int64_t rs = row_s(r), rd = row_d(r);
+    vdb[(rd >> 5) * blk_d + c * 32 + (rd & 31)] = vsb[(rs >> 5) * blk_s + c * 32 + (rs & 31)];
   }
 }
 
@@ -314,7 +315,7 @@ hipError_t launch_append_rope(const AppendRopeArgs& ar, int elt_bytes, hipStream
   const int64_t kb0 = a.o / 32;
   const int64_t kb1 = (a.o + a.T_new - 1) / 32;
   const int nblk = (int)(kb1 - kb0 + 1);
-  const size_t tab = (size_t)32 * (a.d / 2) * sizeof(double2);
+  const size_t tab = (size_t)32 * (a.d / 2) * (sizeof(double2) + (elt_bytes == 2 ? sizeof(float2) : 0));
   const int cpr = a.d / 2 / (16 / elt_bytes);
   const int n_q = ar.q_src ? ar.n_q : 0;
   const int cols = (a.n_kv + n_q) * cpr;

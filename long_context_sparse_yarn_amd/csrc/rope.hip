@@ -13,9 +13,11 @@
 // once (shared by every head) while their first loads are in flight; each
 // thread then owns one (head, 8-pair chunk) column and walks the rows two
 // at a time, loading both halves of the chunk and writing both rotated
-// halves.  Pairs are rotated in fp64 and rounded once to the storage type
-// (an fp32 rotation would lose many bf16 ulps where the two products nearly
-// cancel).  The kernel is HBM-bound: each element is read and written once.
+// halves.  Every output carries the bits of the pair's fp64 rotation rounded
+// once to the storage type; for bf16 rows they come from fp32 arithmetic
+// where an error bound shows that it rounds the same way, and from fp64
+// otherwise (sa_rope.h), since a plain fp32 rotation would lose bf16 ulps
+// where the two products nearly cancel.
 #include "sa_device.h"
 #include "sa_kernels.h"
 #include "sa_rope.h"
@@ -33,42 +35,30 @@ constexpr int kRowsPerThread = 4;    // aim: each thread walks about this many r
 template <int ELT>
 struct Rot;
 template <>
-struct Rot<2> {                      // bf16: 8 values in one 16-byte vector, fp64 math
-  typedef double2 Entry;
+struct Rot<2> {                      // bf16: 8 values in one 16-byte vector
   u32x4 w;
   __device__ __forceinline__ void load(const char* p) { w = ld16(p); }
-  __device__ __forceinline__ double get(int i) const {
-    const uint32_t u = w[i >> 1];
-    return (double)((i & 1) ? bf16_hi(u) : bf16_lo(u));
-  }
-  __device__ __forceinline__ static Entry entry(double c, double s) { return make_double2(c, s); }
-  __device__ __forceinline__ static void rotate(const Rot& a, const Rot& b, const Entry* e,
-                                                char* pa, char* pb) {
-    uint32_t y1[8], y2[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double u = a.get(i), v = b.get(i);
-      y1[i] = f64_to_bf16_bits(rot_first(u, v, e[i].x, e[i].y));
-      y2[i] = f64_to_bf16_bits(rot_second(u, v, e[i].x, e[i].y));
-    }
-    st16(pa, u32x4{y1[0] | (y1[1] << 16), y1[2] | (y1[3] << 16), y1[4] | (y1[5] << 16),
-                   y1[6] | (y1[7] << 16)});
-    st16(pb, u32x4{y2[0] | (y2[1] << 16), y2[2] | (y2[3] << 16), y2[4] | (y2[5] << 16),
-                   y2[6] | (y2[7] << 16)});
+  static constexpr bool kF32Table = true;
+  // fp32 arithmetic where it provably rounds like the fp64 rotation (sa_rope.h)
+  __device__ __forceinline__ static void rotate(const Rot& a, const Rot& b, const float2* fe,
+                                                const double2* de, float k2, char* pa, char* pb) {
+    u32x4 wa, wb;
+    sa_rope::rot8_bf16(a.w, b.w, fe, de, k2, &wa, &wb);
+    st16(pa, wa);
+    st16(pb, wb);
   }
 };
 template <>
 struct Rot<4> {                      // fp32: 8 values in two 16-byte vectors, fp64 math
-  typedef double2 Entry;
   f32x4 w0, w1;
+  static constexpr bool kF32Table = false;
   __device__ __forceinline__ void load(const char* p) {
     w0 = *reinterpret_cast<const f32x4*>(p);
     w1 = *reinterpret_cast<const f32x4*>(p + 16);
   }
   __device__ __forceinline__ double get(int i) const { return (double)(i < 4 ? w0[i] : w1[i - 4]); }
-  __device__ __forceinline__ static Entry entry(double c, double s) { return make_double2(c, s); }
-  __device__ __forceinline__ static void rotate(const Rot& a, const Rot& b, const Entry* e,
-                                                char* pa, char* pb) {
+  __device__ __forceinline__ static void rotate(const Rot& a, const Rot& b, const float2*,
+                                                const double2* e, float, char* pa, char* pb) {
     f32x4 o[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -85,10 +75,10 @@ struct Rot<4> {                      // fp32: 8 values in two 16-byte vectors, f
 
 template <int ELT>
 __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
-  typedef typename Rot<ELT>::Entry Entry;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  Entry* cs = reinterpret_cast<Entry*>(smem);            // [rows][half]
   const int half = a.d >> 1;
+  double2* cs = reinterpret_cast<double2*>(smem);          // [rows][half] fp64
+  float2* cs32 = reinterpret_cast<float2*>(cs + rows * half);   // [rows][half] fp32 (bf16 rows)
   const int cpr = half >> 3;                             // 8-pair chunks per head
   const int per_row = a.H * cpr;                         // <= kThreads (launcher)
   const int rstep = kThreads / per_row;
@@ -103,33 +93,35 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
   char* dst = reinterpret_cast<char*>(a.x) + (int64_t)row0 * rowbytes + col;
   const int hb = half * ELT;
 
-  Rot<ELT> x1[2], x2[2];
-  auto load = [&](int r, int k) {
+  // every row of this thread (at most kRowsPerThread) is loaded up front, so
+  // that all of the workgroup's reads are in flight while the table is built
+  Rot<ELT> x1[kRowsPerThread], x2[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int r = r0 + k * rstep;
     if (active && r < nrows) {
       x1[k].load(src + r * rowbytes);
       x2[k].load(src + r * rowbytes + hb);
     }
-  };
-  load(r0, 0);
-  load(r0 + rstep, 1);
+  }
   for (int e = threadIdx.x; e < nrows * half; e += kThreads) {
     const int r = e / half, i = e - r * half;
     const int t = (row0 + r) % a.T;
     double sn, cn;
     sincos_reduced((double)(a.offset + t) * a.inv_freq[i], &sn, &cn);
-    cs[e] = Rot<ELT>::entry(cn * a.conc, sn * a.conc);
+    const double cc = cn * a.conc, ss = sn * a.conc;
+    cs[e] = make_double2(cc, ss);
+    if (Rot<ELT>::kF32Table) cs32[e] = make_float2((float)cc, (float)ss);
   }
   __syncthreads();
   if (!active) return;
-  for (int r = r0; r < nrows; r += 2 * rstep) {
-    Rot<ELT>::rotate(x1[0], x2[0], &cs[r * half + 8 * ch], dst + r * rowbytes,
-                     dst + r * rowbytes + hb);
-    load(r + 2 * rstep, 0);
-    const int r1 = r + rstep;
-    if (r1 < nrows)
-      Rot<ELT>::rotate(x1[1], x2[1], &cs[r1 * half + 8 * ch], dst + r1 * rowbytes,
-                       dst + r1 * rowbytes + hb);
-    load(r1 + 2 * rstep, 1);
+  const float k2 = sa_rope::bf16_rot_k2(a.conc);
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int r = r0 + k * rstep;
+    if (r < nrows)
+      Rot<ELT>::rotate(x1[k], x2[k], &cs32[r * half + 8 * ch], &cs[r * half + 8 * ch], k2,
+                       dst + r * rowbytes, dst + r * rowbytes + hb);
   }
 }
 
@@ -180,9 +172,10 @@ hipError_t launch_rope(const RopeArgs& a, int elt_bytes, hipStream_t s) {
     return hipGetLastError();
   }
   const int rstep = kThreads / (a.H * (half / 8));
+  // rows per workgroup: at most kRowsPerThread per thread (all loaded at once)
   const int rows = rstep * kRowsPerThread < kRows ? rstep * kRowsPerThread : kRows;
   const int grid = (a.BT + rows - 1) / rows;
-  const size_t lds = (size_t)rows * half * 16;
+  const size_t lds = (size_t)rows * half * (elt_bytes == 2 ? 24 : 16);
   if (elt_bytes == 2)
     hipLaunchKernelGGL(rope_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a, rows);
   else

@@ -65,4 +65,90 @@ __device__ __forceinline__ double rot_second(double u, double v, double cc, doub
   return fma(v, cc, u * ss);
 }
 
+// ---- bf16 rows: the same bits from fp32 arithmetic where that is provably
+// safe.  For a pair (u, v) of bf16 values and the fp64 entries (cc, ss),
+// |cc|, |ss| <= c (the concentration), the fp32 evaluation
+//     y32 = fmaf(u, cc32, -(v*ss32)),   cc32, ss32 = fp32 roundings of cc, ss,
+// differs from the fp64 value y64 = rot_first(u, v, cc, ss) by at most
+// 1.5 * 2^-23 (|u cc| + |v ss|) (two representation errors and two
+// roundings of 2^-24; the fp64 errors are 2^-29 times smaller), so by less
+// than E = 2^-22 c (|u| + |v|).  Rounding to bf16 changes only at midpoints
+// of bf16 intervals.  y32 lies in its interval at distance dist <= ulp/2
+// from the interval's midpoint, and the nearest other midpoint is at least
+// ulp/4 away (ulp/4 where the interval starts a binade).  So if
+//     dist > 2E
+// then E < ulp/4 and E < dist: y64 lies on y32's side of every midpoint and
+// both round to the same bf16.  Then the fp32 value is used (packed to bf16
+// by the hardware conversion, round to nearest even); otherwise -- near-ties,
+// strong cancellation, NaN or infinity, |u| + |v| below 2^-100 where fp32
+// products may underflow -- the fp64 rotation is evaluated.  Likewise for
+// rot_second (same E).  k2 = 2 * 2^-22 * c, rounded up with room for the
+// rounding of |u| + |v| (bf16_rot_k2).
+__device__ __forceinline__ float bf16_rot_k2(double conc) {
+  return (float)(conc * 0x1p-21 * (1.0 + 0x1p-12));
+}
+__device__ __forceinline__ float bf16_mid(float y) {
+  return __uint_as_float((__float_as_uint(y) & 0xFFFF0000u) | 0x8000u);
+}
+
+// Rotate 8 pairs: a holds coordinates i..i+7 (bf16), b coordinates
+// i+d/2..i+d/2+7; fe / de the fp32 / fp64 (c*cos, c*sin) of pairs i..i+7.
+// Writes the rotated halves to *wa, *wb with the bits of the fp64 rotation
+// rounded once (f64_to_bf16_bits).
+__device__ __forceinline__ void rot8_bf16(u32x4 a, u32x4 b, const float2* fe,
+                                          const double2* de, float k2, u32x4* wa, u32x4* wb) {
+  // fp32 values of pair i; the three conditions for using them go into wave
+  // masks (scalar ANDs), not into per-lane bits
+  auto fast = [&](int i, float* f1, float* f2, uint64_t* okm) {
+    const float u = (i & 1) ? bf16_hi(a[i >> 1]) : bf16_lo(a[i >> 1]);
+    const float v = (i & 1) ? bf16_hi(b[i >> 1]) : bf16_lo(b[i >> 1]);
+    const float2 e = fe[i];
+    *f1 = fmaf(u, e.x, -(v * e.y));
+    *f2 = fmaf(v, e.x, u * e.y);
+    const float sum = fabsf(u) + fabsf(v);
+    const float tol = sum * k2;
+    *okm &= __builtin_amdgcn_ballot_w64(sum >= 0x1p-100f) &
+            __builtin_amdgcn_ballot_w64(fabsf(*f1 - bf16_mid(*f1)) > tol) &
+            __builtin_amdgcn_ballot_w64(fabsf(*f2 - bf16_mid(*f2)) > tol);
+  };
+  const uint64_t live = __builtin_amdgcn_ballot_w64(true);
+  float y1[8], y2[8];
+  uint64_t okm = live;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fast(i, &y1[i], &y2[i], &okm);
+  u32x4 ra, rb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ra[j] = pack_bf16x2(y1[2 * j], y1[2 * j + 1]);
+    rb[j] = pack_bf16x2(y2[2 * j], y2[2 * j + 1]);
+  }
+  if (okm != live) {
+    // rare: find the pairs that failed again and take their fp64 rotation
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float f1, f2;
+      uint64_t m = live;
+      fast(i, &f1, &f2, &m);
+      const bool mine = (m >> __lane_id()) & 1;
+      if (!mine) {
+        const double u = (double)((i & 1) ? bf16_hi(a[i >> 1]) : bf16_lo(a[i >> 1]));
+        const double v = (double)((i & 1) ? bf16_hi(b[i >> 1]) : bf16_lo(b[i >> 1]));
+        const double2 e = de[i];
+        const uint32_t r1 = f64_to_bf16_bits(rot_first(u, v, e.x, e.y));
+        const uint32_t r2 = f64_to_bf16_bits(rot_second(u, v, e.x, e.y));
+        const int j = i >> 1;
+        if (i & 1) {
+          ra[j] = (ra[j] & 0xFFFFu) | (r1 << 16);
+          rb[j] = (rb[j] & 0xFFFFu) | (r2 << 16);
+        } else {
+          ra[j] = (ra[j] & 0xFFFF0000u) | r1;
+          rb[j] = (rb[j] & 0xFFFF0000u) | r2;
+        }
+      }
+    }
+  }
+  *wa = ra;
+  *wb = rb;
+}
+
 }  // namespace sa_rope

@@ -53,6 +53,44 @@ def test_rope_matches_oracle(dtype, B, T, H, d, off, y):
     assert (ulp == 0).mean() >= 0.999
 
 
+def _bf16_rne_bits(x32: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.int64) & 0xFFFF
+
+
+@pytest.mark.parametrize("d,H,off,cancel", [(64, 8, 0, False), (96, 8, 4000, False),
+                                            (128, 4, 131000, False), (64, 8, 77, True)])
+def test_bf16_rope_carries_the_fp64_rotation_bits(d, H, off, cancel):
+    """bf16 rows are rotated in fp32 wherever an error bound shows that the
+    result rounds like the fp64 rotation, in fp64 elsewhere.  Both must give
+    the fp64 rotation's bits: the fp32-row kernel computes that same fp64
+    value (same angle tables) and rounds it to fp32, whose bf16 rounding is
+    the fp64 value's own except where the fp32 value sits exactly on a bf16
+    midpoint (skipped).  cancel=True draws pairs whose two products nearly
+    cancel, the case that sends outputs to the fp64 path."""
+    rng = np.random.default_rng(d + H + off)
+    B, T = 4, 1024
+    x = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    if cancel:
+        half = d // 2
+        # v close to u (and to -u) makes u*cos - v*sin or v*cos + u*sin small at many angles
+        x[..., half:] = x[..., :half] * rng.choice([-1.0, 1.0], size=x[..., :half].shape) \
+            * (1 + 2.0 ** -9 * rng.standard_normal(x[..., :half].shape)).astype(np.float32)
+    x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # bf16-exact
+    y = lib_yarn(d, Yarn())
+    xb = dev(x, "bf16")
+    sa.yarn_rope_apply(xb, off, y)
+    xf = dev(x, "f32")
+    sa.yarn_rope_apply(xf, off, y)
+    torch.cuda.synchronize()
+    got = _bits(xb) & 0xFFFF
+    f32 = xf.cpu().numpy()
+    want = _bf16_rne_bits(f32)
+    on_mid = (f32.view(np.uint32) & np.uint32(0xFFFF)) == np.uint32(0x8000)
+    assert on_mid.mean() < 1e-3
+    assert np.array_equal(got[~on_mid], want[~on_mid])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rope_out_of_place_equals_in_place(dtype):
     y = Yarn()
