@@ -152,6 +152,38 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   const E* vsrc0 = vsrc + (srow * a.n_kv + h0) * d;
   E* dst0 = kc + (((int64_t)b * a.C + key_lo) * a.n_kv + h0) * d;
   const int rstride = a.n_kv * d;
+  // this head group's share of the Q heads, rotated at the same rows
+  const int qh0 = grp * qpg;
+  const int nq = ar.q_src ? max(0, min(qpg, ar.n_q - qh0)) : 0;
+  const int64_t qoff = (srow * ar.n_q + qh0) * d;
+
+  // bf16: one column space over the group's K and Q heads (column = head,
+  // 8-pair chunk); a thread keeps one column and steps over rows.  Its first
+  // row is loaded here, before the V copy and the table, so that those reads
+  // are in flight while the table is built (deeper prefetch measured slower:
+  // the registers it holds cost occupancy).
+  constexpr int kMaxRows = 1;
+  const int cpr = half / VEC;
+  const int ncols = (nh + nq) * cpr;
+  const bool pre = ELT == 2 && ncols > 0 && ncols <= kThreads;
+  const int crstep = pre ? kThreads / ncols : 1;
+  const int ccol = pre ? threadIdx.x % ncols : 0, cr0 = pre ? threadIdx.x / ncols : 0;
+  const bool cact = pre && cr0 < crstep;
+  const int chh = ccol / cpr, cc0 = (ccol - chh * cpr) * VEC;
+  const bool cq = chh >= nh;
+  const E* csrc = cq ? reinterpret_cast<const E*>(ar.q_src) + qoff + (chh - nh) * d : src0 + chh * d;
+  E* cdst = cq ? reinterpret_cast<E*>(ar.q_dst) + qoff + (chh - nh) * d : dst0 + chh * d;
+  const int cs_stride = cq ? ar.n_q * d : rstride;          // source row stride
+  const int cd_stride = cq ? ar.n_q * d : rstride;          // destination row stride
+  u32x4 pu[kMaxRows], pv[kMaxRows];
+#pragma unroll
+  for (int k = 0; k < kMaxRows; ++k) {
+    const int r = cr0 + k * crstep;
+    if (cact && r < nk) {
+      pu[k] = ld16(csrc + r * cs_stride + cc0);
+      pv[k] = ld16(csrc + r * cs_stride + cc0 + half);
+    }
+  }
 
   // V: straight into the blocked layout (no LDS)
   if (nh > 0)
@@ -220,17 +252,34 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
       }
     }
   };
-  if (nh > 0) rotate_rows(src0, rstride, dst0, rstride, nh);
-  if (ar.q_src) {
-    // this head group's share of the Q heads, rotated at the same rows
-    const int qh0 = grp * qpg;
-    const int nq = min(qpg, ar.n_q - qh0);
-    if (nq > 0) {
-      const int64_t qoff = (srow * ar.n_q + qh0) * d;
-      rotate_rows(reinterpret_cast<const E*>(ar.q_src) + qoff, ar.n_q * d,
-                  reinterpret_cast<E*>(ar.q_dst) + qoff, ar.n_q * d, nq);
+  if (pre) {
+    if (cact) {
+      // the prefetched rows, then any further ones (more than kMaxRows per thread)
+#pragma unroll
+      for (int k = 0; k < kMaxRows; ++k) {
+        const int r = cr0 + k * crstep;
+        if (r < nk) {
+          u32x4 w1, w2;
+          sa_rope::rot8_bf16(pu[k], pv[k], &tab32[r * half + cc0], &tab[r * half + cc0], k2,
+                             &w1, &w2);
+          st16(cdst + r * cd_stride + cc0, w1);
+          st16(cdst + r * cd_stride + cc0 + half, w2);
+        }
+      }
+      for (int r = cr0 + kMaxRows * crstep; r < nk; r += crstep) {
+        const u32x4 u = ld16(csrc + r * cs_stride + cc0), v = ld16(csrc + r * cs_stride + cc0 + half);
+        u32x4 w1, w2;
+        sa_rope::rot8_bf16(u, v, &tab32[r * half + cc0], &tab[r * half + cc0], k2, &w1, &w2);
+        st16(cdst + r * cd_stride + cc0, w1);
+        st16(cdst + r * cd_stride + cc0 + half, w2);
+      }
     }
+    return;
   }
+  if (nh > 0) rotate_rows(src0, rstride, dst0, rstride, nh);
+  if (nq > 0)
+    rotate_rows(reinterpret_cast<const E*>(ar.q_src) + qoff, ar.n_q * d,
+                reinterpret_cast<E*>(ar.q_dst) + qoff, ar.n_q * d, nq);
 }
 
 // Rows of positions [p0, p0 + n) from one cache to another; a workgroup owns
