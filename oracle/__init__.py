@@ -14,6 +14,7 @@ Modules
   attention  masks, sink-augmented softmax, GQA; a per-query form and a
              dense mask-matrix form
   kvcache    append-only cache with snapshot/restore; KV byte count
+  qkv        fused qkv projection (x W^T + b rounded once) and its [Q | K | V] split
   ring       sliding-window ring cache of band layers (W rows, slot p mod W),
              its band mask in ring coordinates, KV entry counts
 
