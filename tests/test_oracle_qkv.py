@@ -77,9 +77,9 @@ def test_split_is_q_k_v_head_major(n_q, n_kv, d):
 
 
 def test_rounded_once_not_per_term():
-    # bf16 ulp at 1 is 2^-7; 3*2^-9 is 0.375 ulp.  Rounding each partial sum
+    # bf16 ulp at 1 is 2^-7; 3*2^-10 is 0.375 ulp.  Rounding each partial sum
     # to bf16 would keep 1 twice; the exact 1 + 0.75 ulp rounds to 1 + 2^-7
-    t = 3.0 * 2.0 ** -9
+    t = 3.0 * 2.0 ** -10
     x = np.array([[1.0, t, t]])
     W = np.array([[1.0, 1.0, 1.0]])
     assert qkv_project(x, W, np.zeros(1))[0, 0] == 1.0 + 2.0 ** -7
