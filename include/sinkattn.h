@@ -284,6 +284,40 @@ int sinkattn_prefill_rope(const void* q, const sa_kv_cache* c, const float* sink
                           int window, float sm_scale, int64_t q_offset,
                           const sa_yarn* y, void* stream);
 
+/* ---- The layer's fused qkv projection with RoPE and append ----
+ * "GQA Attention" study note on gpt-oss, How it works: after the norm, one
+ * fused bf16 linear layer (with bias) of width d_qkv = d_h (n_q + 2 n_kv)
+ * produces Q, K and V; rotary embeddings run on Q and K.  "MoE-Xtend"
+ * README, ROPE + SCALING and KV CACHE: rotation at the global position,
+ * then K and V are appended.
+ *
+ * Bytes of workspace sinkattn_qkv_rope_append needs for T tokens of head
+ * dimension d_h (a per-position fp64 (c cos, c sin) table); 0 on invalid
+ * arguments. */
+size_t sinkattn_qkv_workspace_bytes(int T, int d_h);
+
+/* qkv = x W^T + b, accumulated in fp32 and rounded once to bf16 (what a
+ * bf16 linear layer returns; the fp32 summation order is the kernel's),
+ * split [Q | K | V] with each part head-major (column h*d_h + e of a part is
+ * coordinate e of head h); then exactly what kv_cache_append_rope_qk(c, Q,
+ * q_rot, K, V) does with those bf16 values: Q rotated at positions
+ * kv_cache_offset(c) + t into q_rot, K rotated into the cache rows, V
+ * appended, the offset advanced by T.
+ *   x:      device [B, T, d_model] bf16 (the normed hidden states)
+ *   w_qkv:  device [d_qkv, d_model] bf16 (a linear layer's [out, in] weight)
+ *   b_qkv:  device [d_qkv] bf16
+ *   q_rot:  device [B, T, n_q, d_h] bf16, written
+ *   workspace: device scratch of sinkattn_qkv_workspace_bytes(T, d_h)
+ *      bytes, overwritten.
+ * The cache must be a linear bf16 cache (a ring is SA_ERR_ARG: use its
+ * stage) with d_h in {64, 96, 128} (SA_ERR_SHAPE); n_kv and d_h are the
+ * cache's; d_model a multiple of 64 (SA_ERR_SHAPE); room for T rows
+ * (SA_ERR_CAPACITY); y->d_h == d_h. */
+int sinkattn_qkv_rope_append(sa_kv_cache* c, const void* x, const void* w_qkv,
+                             const void* b_qkv, void* q_rot, int B, int T, int d_model,
+                             int n_q, const sa_yarn* y, void* workspace, size_t ws_bytes,
+                             void* stream);
+
 /* Bytes of fp32 workspace that sinkattn_decode needs for any cache offset up
  * to `capacity` with these shapes (0 on invalid arguments). */
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h,

@@ -79,6 +79,9 @@ _sinkattn_prefill = _sig("sinkattn_prefill", _i32, _vp, _vp, _vp, _vp, _i32, _i3
                          _i32, _i32, _f32, _i64, _vp)
 _sinkattn_prefill_rope = _sig("sinkattn_prefill_rope", _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                               _i32, _i32, _i32, _i32, _f32, _i64, ctypes.POINTER(SaYarn), _vp)
+_sinkattn_qkv_ws = _sig("sinkattn_qkv_workspace_bytes", _sz, _i32, _i32)
+_sinkattn_qkv = _sig("sinkattn_qkv_rope_append", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                     _i32, ctypes.POINTER(SaYarn), _vp, _sz, _vp)
 _sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
 _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                         _i32, _f32, _vp, _sz, _vp)
@@ -391,6 +394,38 @@ def sinkattn_prefill_rope(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, 
                                   float(sm_scale), int(q_offset), ctypes.byref(ys),
                                   _stream(stream)))
     return out
+
+
+def qkv_workspace_bytes(T: int, d: int) -> int:
+    return int(_sinkattn_qkv_ws(int(T), int(d)))
+
+
+def qkv_rope_append(cache: KVCache, x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: torch.Tensor,
+                    n_q: int, y: "Yarn", q_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sinkattn_qkv_rope_append: x [B, T, d_model] bf16, w_qkv [d_qkv, d_model],
+    b_qkv [d_qkv]; writes the rotated queries to q_out [B, T, n_q, d] (new
+    if not given) and appends K, V to the cache.  Returns q_out."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, d_model]")
+    B, T, dm = x.shape
+    d, n_kv = cache.d, cache.n_kv
+    dq = d * (n_q + 2 * n_kv)
+    if tuple(w_qkv.shape) != (dq, dm) or tuple(b_qkv.shape) != (dq,):
+        raise ValueError("w_qkv must be [d (n_q + 2 n_kv), d_model] and b_qkv [d_qkv]")
+    if q_out is None:
+        q_out = torch.empty((B, T, n_q, d), dtype=x.dtype, device=x.device)
+    elif tuple(q_out.shape) != (B, T, n_q, d) or q_out.dtype != x.dtype:
+        raise ValueError("q_out must be [B, T, n_q, d] of x's dtype")
+    need = qkv_workspace_bytes(T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ys = y.c_struct()
+    _check(_sinkattn_qkv(cache.handle, _dev(x, "x"), _dev(w_qkv, "w_qkv"), _dev(b_qkv, "b_qkv"),
+                         _dev(q_out, "q_out"), B, T, dm, int(n_q), ctypes.byref(ys),
+                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                         _stream(stream)))
+    return q_out
 
 
 def decode_workspace_bytes(B, n_q, n_kv, d, capacity) -> int:

@@ -1,0 +1,247 @@
+// sinkattn_qkv_rope_append: the layer's fused qkv projection with the RoPE
+// and cache append as its epilogue, on the gfx950 matrix cores.
+//
+// What is computed ("GQA Attention" study note on gpt-oss, How it works;
+// "MoE-Xtend" README, ROPE + SCALING and KV CACHE): qkv = x W^T + b for the
+// hidden states x [B*T, d_model] and the fused weight W [d_qkv, d_model],
+// d_qkv = d (n_q + 2 n_kv), rounded once to bf16 as a bf16 linear layer
+// returns it; split [Q | K | V], each head-major; Q rotated at positions
+// pos0 + t into q_rot, K rotated into the cache rows, V appended unrotated.
+// Every rotated value carries the bits of yarn_rope applied to the bf16
+// projection (the fp64 rotation rounded once, sa_rope.h).
+//
+// How:
+//  * C^T = W x^T with v_mfma_f32_16x16x32_bf16: a workgroup (4 waves) owns
+//    128 tokens x 2 heads (2d features); wave (wf, wt) owns head wf of the
+//    pair and 64 of the tokens, so each lane ends with 4 consecutive
+//    features of one token per 16x16 tile, and the two halves of a RoPE
+//    pair (e, e + d/2) sit in the same lane (d/2 is a multiple of 16).
+//  * Both operands are contiguous along d_model (W is the linear layer's
+//    [out, in] matrix), so 64-wide slices of W and x go global -> LDS with
+//    16-byte global_load_lds, 16-byte chunk c of row r at slot c ^ (r & 7)
+//    (conflict-free operand reads); two LDS stages, one barrier per stage.
+//  * Epilogue in registers: + bias (fp32), one rounding to bf16, rotation
+//    against a per-position table of fp64 (c cos, c sin) built by a small
+//    kernel first (the same sincos_reduced as every RoPE path), fp32 where
+//    the error bound proves the same rounding and fp64 otherwise; Q and K
+//    leave as 8-byte rows (4 features), V as 2-byte stores into the blocked
+//    layout (16 lanes = 16 consecutive keys of one coordinate).
+#include "sa_device.h"
+#include "sa_kernels.h"
+#include "sa_rope.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTM = 128;      // tokens per workgroup
+constexpr int kKS = 64;       // contraction elements per LDS stage
+
+__device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(lds_block)), 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// tab[t][i] = (c cos, c sin)(pos0 + t) * inv_freq_i), fp64
+__global__ __launch_bounds__(kThreads) void rope_table_kernel(QkvArgs a) {
+  const int half = a.d / 2;
+  const int64_t n = (int64_t)a.T * half;
+  for (int64_t e = blockIdx.x * (int64_t)kThreads + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int t = (int)(e / half), i = (int)(e - (int64_t)t * half);
+    double sn, cn;
+    sa_rope::sincos_reduced((double)(a.pos0 + t) * a.inv_freq[i], &sn, &cn);
+    a.tab[e] = make_double2(cn * a.conc, sn * a.conc);
+  }
+}
+
+// bf16 value (as fp32) of fp32 x, round to nearest even
+__device__ __forceinline__ float round_bf16(float x) {
+  return __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, int n_mt) {
+  constexpr int FT = D / 16;            // 16-feature tiles per head (per wave)
+  constexpr int TT = 4;                 // 16-token tiles per wave
+  constexpr int WROWS = 2 * D;          // W rows per workgroup
+  constexpr int WBUF = WROWS * kKS;     // elements per stage
+  constexpr int XBUF = kTM * kKS;
+  constexpr int WBLK = WROWS * 8 / 64;  // 1 KB blocks per W stage
+  constexpr int XBLK = kTM * 8 / 64;
+  constexpr int WBW = WBLK / 4, XBW = XBLK / 4;
+  static_assert(WBLK % 4 == 0 && XBLK % 4 == 0, "blocks split evenly over 4 waves");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (WBUF + XBUF)];
+  auto Wb = [&](int s) { return lds + s * (WBUF + XBUF); };
+  auto Xb = [&](int s) { return lds + s * (WBUF + XBUF) + WBUF; };
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int wf = wave & 1, wt = wave >> 1;
+  const int mt = blockIdx.x % n_mt, nt = blockIdx.x / n_mt;
+  const int M = a.B * a.T;
+  const int H = a.n_q + 2 * a.n_kv;             // heads of the fused width
+  const int dqkv = H * D;
+  const int m0 = mt * kTM, f0 = nt * WROWS;
+
+  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+  const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w);
+  // global element offset (without k0) of the chunk each lane fetches into
+  // slot `lane` of its blocks; rows past the ends are clamped (never stored)
+  uint32_t w_off[WBW], x_off[XBW];
+#pragma unroll
+  for (int i = 0; i < WBW; ++i) {
+    const int sl = 64 * (wave + 4 * i) + lane;
+    const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
+    const int row = min(f0 + r, dqkv - 1);
+    w_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < XBW; ++i) {
+    const int sl = 64 * (wave + 4 * i) + lane;
+    const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
+    const int row = min(m0 + r, M - 1);
+    x_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
+  }
+  auto load_stage = [&](int s, int k0) {
+#pragma unroll
+    for (int i = 0; i < WBW; ++i) lds_direct16(wg + w_off[i] + k0, &Wb(s)[512 * (wave + 4 * i)]);
+#pragma unroll
+    for (int i = 0; i < XBW; ++i) lds_direct16(xg + x_off[i] + k0, &Xb(s)[512 * (wave + 4 * i)]);
+  };
+  // operand reads: row r, chunk c -> r*64 + 8*(c ^ (r & 7)); the rows of a
+  // lane's tiles differ by multiples of 16, so r & 7 = j & 7
+  const int swz = j & 7;
+  const int wrow0 = D * wf + j, xrow0 = 64 * wt + j;
+
+  f32x4 acc[FT][TT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = a.d_model / kKS;
+  load_stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int s = ks & 1;
+    if (ks + 1 < nks) load_stage(s ^ 1, (ks + 1) * kKS);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int cofs = 8 * ((g4 + 4 * kk) ^ swz);
+      u32x4 A[FT], Bx[TT];
+#pragma unroll
+      for (int f = 0; f < FT; ++f) A[f] = ld16(&Wb(s)[(wrow0 + 16 * f) * kKS + cofs]);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) Bx[t] = ld16(&Xb(s)[(xrow0 + 16 * t) * kKS + cofs]);
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[f][t] = mfma16x16x32(A[f], Bx[t], acc[f][t]);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds features 16f + 4*g4 + r of token 16t + j
+  const int hd = 2 * nt + wf;                     // head in the fused width
+  if (hd >= H) return;
+  const int kind = hd < a.n_q ? 0 : (hd < a.n_q + a.n_kv ? 1 : 2);   // Q, K, V
+  const int hh = kind == 0 ? hd : (kind == 1 ? hd - a.n_q : hd - a.n_q - a.n_kv);
+  const uint16_t* bg = reinterpret_cast<const uint16_t*>(a.bias) + (int64_t)hd * D;
+  float val[FT][TT][4];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    const u32x2 bb = *reinterpret_cast<const u32x2*>(bg + 16 * f + 4 * g4);
+    const float bv[4] = {bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[f][t][r] = round_bf16(acc[f][t][r] + bv[r]);
+  }
+  const float k2 = sa_rope::bf16_rot_k2(a.conc);
+  uint16_t* qo = reinterpret_cast<uint16_t*>(a.q_rot);
+  uint16_t* kc = reinterpret_cast<uint16_t*>(a.kc);
+  uint16_t* vc = reinterpret_cast<uint16_t*>(a.vc);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const int m = m0 + 64 * wt + 16 * t + j;
+    if (m >= M) continue;
+    const int b = m / a.T, tt = m - b * a.T;
+    const int64_t crow = a.row0 + tt;               // cache row of this token
+    if (kind == 2) {
+      uint16_t* vp = vc + (((int64_t)b * (a.C / 32) + crow / 32) * a.n_kv + hh) * (int64_t)D * 32 +
+                     crow % 32;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vp[(16 * f + 4 * g4 + r) * 32] = (uint16_t)(__float_as_uint(val[f][t][r]) >> 16);
+      continue;
+    }
+    uint16_t* row = kind == 0 ? qo + (((int64_t)b * a.T + tt) * a.n_q + hh) * D
+                              : kc + (((int64_t)b * a.C + crow) * a.n_kv + hh) * D;
+    const double2* tb = a.tab + (int64_t)tt * (D / 2);
+#pragma unroll
+    for (int f = 0; f < FT / 2; ++f) {
+      const int e = 16 * f + 4 * g4;                // pair index of r = 0
+      uint32_t y1[4], y2[4];
+      bool ok = true;
+      double2 cs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cs[r] = tb[e + r];
+        const float u = val[f][t][r], v = val[f + FT / 2][t][r];
+        const float cc = (float)cs[r].x, ss = (float)cs[r].y;
+        const float f1 = fmaf(u, cc, -(v * ss)), f2 = fmaf(v, cc, u * ss);
+        const float sum = fabsf(u) + fabsf(v), tol = sum * k2;
+        ok = ok & (sum >= 0x1p-100f) & (fabsf(f1 - sa_rope::bf16_mid(f1)) > tol) &
+             (fabsf(f2 - sa_rope::bf16_mid(f2)) > tol);
+        y1[r] = __float_as_uint(round_bf16(f1)) >> 16;
+        y2[r] = __float_as_uint(round_bf16(f2)) >> 16;
+      }
+      if (__builtin_amdgcn_ballot_w64(!ok) != 0) {   // rare: the fp64 rotation
+        if (!ok) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const double u = val[f][t][r], v = val[f + FT / 2][t][r];
+            y1[r] = f64_to_bf16_bits(sa_rope::rot_first(u, v, cs[r].x, cs[r].y));
+            y2[r] = f64_to_bf16_bits(sa_rope::rot_second(u, v, cs[r].x, cs[r].y));
+          }
+        }
+      }
+      *reinterpret_cast<u32x2*>(row + e) = u32x2{y1[0] | (y1[1] << 16), y1[2] | (y1[3] << 16)};
+      *reinterpret_cast<u32x2*>(row + e + D / 2) =
+          u32x2{y2[0] | (y2[1] << 16), y2[2] | (y2[3] << 16)};
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const QkvArgs& a, hipStream_t s) {
+  const int M = a.B * a.T;
+  const int n_mt = (M + kTM - 1) / kTM;
+  const int H = a.n_q + 2 * a.n_kv;
+  const int n_nt = (H + 1) / 2;
+  hipLaunchKernelGGL(qkv_rope_append_kernel<D>, dim3((unsigned)(n_mt * n_nt)), dim3(kThreads), 0,
+                     s, a, n_mt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.T * (a.d / 2);
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                     dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (a.d) {
+    case 64: return launch_d<64>(a, s);
+    case 96: return launch_d<96>(a, s);
+    case 128: return launch_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}

@@ -57,6 +57,24 @@ struct AppendRopeArgs {  // rotate K rows at their cache positions, then append
 };
 hipError_t launch_append_rope(const AppendRopeArgs& a, int elt_bytes, hipStream_t s);
 
+// Fused qkv projection with the RoPE + append epilogue.
+struct QkvArgs {
+  const void* x;        // [B*T, d_model] bf16 (hidden states after the norm)
+  const void* w;        // [d_qkv, d_model] bf16, d_qkv = d (n_q + 2 n_kv)
+  const void* bias;     // [d_qkv] bf16
+  void* q_rot;          // [B, T, n_q, d] bf16
+  void* kc;             // cache K [B, C, n_kv, d]
+  void* vc;             // cache V [B, C/32, n_kv, d, 32]
+  double2* tab;         // workspace [T][d/2]: (c cos, c sin) at position pos0 + t
+  int B, T, d_model, n_q, n_kv, d;
+  int64_t C;            // cache capacity (rows)
+  int64_t row0;         // cache row of token 0
+  int64_t pos0;         // global position of token 0
+  double conc;
+  double inv_freq[SA_MAX_HALF];
+};
+hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s);
+
 struct AttnArgs {
   const void* q;        // [B, T_q, n_q, d]
   const void* kc;       // [B, C, n_kv, d]

@@ -593,6 +593,63 @@ int sinkattn_prefill_rope(const void* q, const sa_kv_cache* c, const float* sink
                         stream);
 }
 
+size_t sinkattn_qkv_workspace_bytes(int T, int d_h) {
+  if (T <= 0 || d_h <= 0 || d_h % 2) return 0;
+  return (size_t)T * (size_t)(d_h / 2) * 16;
+}
+
+int sinkattn_qkv_rope_append(sa_kv_cache* c, const void* x, const void* w_qkv, const void* b_qkv,
+                             void* q_rot, int B, int T, int d_model, int n_q, const sa_yarn* y,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  if (!c || !x || !w_qkv || !b_qkv || !q_rot || !workspace) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(x) || misaligned(w_qkv) || misaligned(b_qkv) || misaligned(q_rot) ||
+      misaligned(workspace))
+    return fail(SA_ERR_ARG, "x, w_qkv, b_qkv, q_rot and workspace must be 16-byte aligned");
+  if (c->ring)
+    return fail(SA_ERR_ARG, "the fused projection appends to a linear cache (a stage for a ring)");
+  if (c->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "the fused projection is bf16 only");
+  if (B <= 0 || T <= 0 || n_q <= 0 || d_model <= 0) return fail(SA_ERR_ARG, "non-positive size");
+  if (B != c->B) return fail(SA_ERR_SHAPE, "B %d differs from the cache's %d", B, c->B);
+  const int d = c->d_h;
+  if (d != 64 && d != 96 && d != 128)
+    return fail(SA_ERR_SHAPE, "the fused projection supports d_h in {64, 96, 128}, got %d", d);
+  if (d_model % 64) return fail(SA_ERR_SHAPE, "d_model must be a multiple of 64, got %d", d_model);
+  const int64_t M = (int64_t)B * T;
+  const int64_t dqkv = (int64_t)d * (n_q + 2 * c->n_kv);
+  if (M * d_model > UINT32_MAX || dqkv * d_model > UINT32_MAX || M * n_q > INT32_MAX)
+    return fail(SA_ERR_ARG, "B*T*d_model or d_qkv*d_model too large");
+  const int64_t row = c->offset - c->base;
+  if (row + T > c->capacity)
+    return fail(SA_ERR_CAPACITY, "append of %d rows at row %lld exceeds capacity %lld", T,
+                (long long)row, (long long)c->capacity);
+  const size_t need = sinkattn_qkv_workspace_bytes(T, d);
+  if (ws_bytes < need) return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  QkvArgs a;
+  memset(&a, 0, sizeof a);
+  int st = yarn_table(y, d, a.inv_freq, &a.conc);
+  if (st != SA_OK) return st;
+  a.x = x;
+  a.w = w_qkv;
+  a.bias = b_qkv;
+  a.q_rot = q_rot;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.tab = reinterpret_cast<double2*>(workspace);
+  a.B = B;
+  a.T = T;
+  a.d_model = d_model;
+  a.n_q = n_q;
+  a.n_kv = c->n_kv;
+  a.d = d;
+  a.C = c->capacity;
+  a.row0 = row;
+  a.pos0 = c->offset;
+  hipError_t e = launch_qkv_rope_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused projection launch");
+  appended(c, T);
+  return ok();
+}
+
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h, int64_t capacity) {
   if (B <= 0 || n_q <= 0 || n_kv <= 0 || d_h <= 0 || capacity <= 0 || n_q % n_kv) return 0;
   const int64_t S = decode_max_splits(B, n_kv, capacity);

@@ -251,3 +251,37 @@ def test_ring_create_and_host_bookkeeping():
     assert B._kv_cache_restore(r, ctypes.byref(snap)) == SA_OK
     for h in (r, r2, lin, lin3, linf):
         B._kv_cache_destroy(h)
+
+
+def test_qkv_errors_before_any_launch():
+    Q = B._sinkattn_qkv
+    y64 = B.SaYarn(64, 150000.0, 32.0, 4096, 1.0, 32.0)
+    x, w, b, q, ws = (ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000),
+                      ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000))
+    need = B._sinkattn_qkv_ws(100, 64)
+    assert need == 100 * 32 * 16
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    args = lambda **k: dict(dict(c=h, x=x, w=w, b=b, q=q, B=2, T=100, dm=128, n_q=8, y=ctypes.byref(y64),
+                                 ws=ws, wsb=need), **k)
+    call = lambda a: Q(a["c"], a["x"], a["w"], a["b"], a["q"], a["B"], a["T"], a["dm"], a["n_q"], a["y"],
+                       a["ws"], a["wsb"], None)
+    assert call(args(x=None)) == SA_ERR_ARG
+    assert call(args(x=ctypes.c_void_p(0x30008))) == SA_ERR_ARG            # misaligned
+    assert call(args(dm=100)) == SA_ERR_SHAPE                                # d_model % 64
+    assert call(args(B=3)) == SA_ERR_SHAPE                                   # B != cache
+    assert call(args(T=247)) == SA_ERR_CAPACITY                              # 10 + 247 > 256
+    assert call(args(wsb=need - 16)) == SA_ERR_ARG
+    assert call(args(T=0)) == SA_ERR_ARG
+    y96 = B.SaYarn(96, 150000.0, 32.0, 4096, 1.0, 32.0)
+    assert call(args(y=ctypes.byref(y96))) == SA_ERR_SHAPE                   # yarn d_h differs
+    assert B._kv_cache_offset(h) == 10
+    B._kv_cache_destroy(h)
+    st, hf = create(dtype=1, Bn=2, C=256, n_kv=2, d=64)
+    assert call(args(c=hf)) == SA_ERR_DTYPE
+    B._kv_cache_destroy(hf)
+    st, h80 = create(Bn=2, C=256, n_kv=2, d=80)
+    assert call(args(c=h80)) == SA_ERR_SHAPE
+    B._kv_cache_destroy(h80)
+    st, r = ring(Bn=2, W=128, n_kv=2, d=64)
+    assert call(args(c=r)) == SA_ERR_ARG                                     # a ring: use its stage
+    B._kv_cache_destroy(r)
