@@ -11,11 +11,13 @@
 // projection (the fp64 rotation rounded once, sa_rope.h).
 //
 // How:
-//  * C^T = W x^T with v_mfma_f32_16x16x32_bf16: a workgroup (4 waves) owns
-//    128 tokens x 2 heads (2d features); wave (wf, wt) owns head wf of the
-//    pair and 64 of the tokens, so each lane ends with 4 consecutive
-//    features of one token per 16x16 tile, and the two halves of a RoPE
-//    pair (e, e + d/2) sit in the same lane (d/2 is a multiple of 16).
+//  * C^T = W x^T with v_mfma_f32_16x16x32_bf16: a workgroup (8 waves) owns
+//    256 tokens x 256 features (4 heads at d = 64, 2 at d = 128; 2 heads,
+//    192 features at d = 96), so each byte staged from L2 feeds >= 110
+//    flops; wave (wf, wt) owns half of the features (whole heads) and 64 of
+//    the tokens, so each lane ends with 4 consecutive features of one token
+//    per 16x16 tile, and the two halves of a RoPE pair (e, e + d/2) sit in
+//    the same lane (d/2 is a multiple of 16).
 //  * Both operands are contiguous along d_model (W is the linear layer's
 //    [out, in] matrix), so 64-wide slices of W and x go global -> LDS with
 //    16-byte global_load_lds, 16-byte chunk c of row r at slot c ^ (r & 7)
@@ -32,8 +34,8 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTM = 128;      // tokens per workgroup
+constexpr int kThreads = 512;  // 8 waves: 2 feature halves x 4 token quarters
+constexpr int kTM = 256;       // tokens per workgroup
 constexpr int kKS = 64;       // contraction elements per LDS stage
 
 __device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* lds_block) {
@@ -62,27 +64,31 @@ __device__ __forceinline__ float round_bf16(float x) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, int n_mt) {
-  constexpr int FT = D / 16;            // 16-feature tiles per head (per wave)
+  constexpr int HPW = D == 64 ? 4 : 2;  // heads per workgroup
+  constexpr int F = HPW * D;            // features per workgroup (256, 192, 256)
+  constexpr int FW = F / 2;             // features per wave
+  constexpr int FT = FW / 16;           // 16-feature tiles per wave
+  constexpr int HW = HPW / 2;           // heads per wave
   constexpr int TT = 4;                 // 16-token tiles per wave
-  constexpr int WROWS = 2 * D;          // W rows per workgroup
-  constexpr int WBUF = WROWS * kKS;     // elements per stage
+  constexpr int WBUF = F * kKS;         // elements per stage
   constexpr int XBUF = kTM * kKS;
-  constexpr int WBLK = WROWS * 8 / 64;  // 1 KB blocks per W stage
+  constexpr int NWV = kThreads / 64;    // waves
+  constexpr int WBLK = F * 8 / 64;      // 1 KB blocks per W stage
   constexpr int XBLK = kTM * 8 / 64;
-  constexpr int WBW = WBLK / 4, XBW = XBLK / 4;
-  static_assert(WBLK % 4 == 0 && XBLK % 4 == 0, "blocks split evenly over 4 waves");
+  constexpr int WBW = WBLK / NWV, XBW = XBLK / NWV;
+  static_assert(WBLK % NWV == 0 && XBLK % NWV == 0, "blocks split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (WBUF + XBUF)];
   auto Wb = [&](int s) { return lds + s * (WBUF + XBUF); };
   auto Xb = [&](int s) { return lds + s * (WBUF + XBUF) + WBUF; };
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
-  const int wf = wave & 1, wt = wave >> 1;
+  const int wf = wave & 1, wt = wave >> 1;       // feature half, 64-token quarter
   const int mt = blockIdx.x % n_mt, nt = blockIdx.x / n_mt;
   const int M = a.B * a.T;
   const int H = a.n_q + 2 * a.n_kv;             // heads of the fused width
   const int dqkv = H * D;
-  const int m0 = mt * kTM, f0 = nt * WROWS;
+  const int m0 = mt * kTM, f0 = nt * F;
 
   const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
   const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w);
@@ -91,28 +97,28 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
   uint32_t w_off[WBW], x_off[XBW];
 #pragma unroll
   for (int i = 0; i < WBW; ++i) {
-    const int sl = 64 * (wave + 4 * i) + lane;
+    const int sl = 64 * (wave + NWV * i) + lane;
     const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
     const int row = min(f0 + r, dqkv - 1);
     w_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
   }
 #pragma unroll
   for (int i = 0; i < XBW; ++i) {
-    const int sl = 64 * (wave + 4 * i) + lane;
+    const int sl = 64 * (wave + NWV * i) + lane;
     const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
     const int row = min(m0 + r, M - 1);
     x_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
   }
   auto load_stage = [&](int s, int k0) {
 #pragma unroll
-    for (int i = 0; i < WBW; ++i) lds_direct16(wg + w_off[i] + k0, &Wb(s)[512 * (wave + 4 * i)]);
+    for (int i = 0; i < WBW; ++i) lds_direct16(wg + w_off[i] + k0, &Wb(s)[512 * (wave + NWV * i)]);
 #pragma unroll
-    for (int i = 0; i < XBW; ++i) lds_direct16(xg + x_off[i] + k0, &Xb(s)[512 * (wave + 4 * i)]);
+    for (int i = 0; i < XBW; ++i) lds_direct16(xg + x_off[i] + k0, &Xb(s)[512 * (wave + NWV * i)]);
   };
   // operand reads: row r, chunk c -> r*64 + 8*(c ^ (r & 7)); the rows of a
   // lane's tiles differ by multiples of 16, so r & 7 = j & 7
   const int swz = j & 7;
-  const int wrow0 = D * wf + j, xrow0 = 64 * wt + j;
+  const int wrow0 = FW * wf + j, xrow0 = 64 * wt + j;
 
   f32x4 acc[FT][TT];
 #pragma unroll
@@ -144,86 +150,92 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds features 16f + 4*g4 + r of token 16t + j
-  const int hd = 2 * nt + wf;                     // head in the fused width
-  if (hd >= H) return;
-  const int kind = hd < a.n_q ? 0 : (hd < a.n_q + a.n_kv ? 1 : 2);   // Q, K, V
-  const int hh = kind == 0 ? hd : (kind == 1 ? hd - a.n_q : hd - a.n_q - a.n_kv);
-  const uint16_t* bg = reinterpret_cast<const uint16_t*>(a.bias) + (int64_t)hd * D;
-  float val[FT][TT][4];
-#pragma unroll
-  for (int f = 0; f < FT; ++f) {
-    const u32x2 bb = *reinterpret_cast<const u32x2*>(bg + 16 * f + 4 * g4);
-    const float bv[4] = {bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) val[f][t][r] = round_bf16(acc[f][t][r] + bv[r]);
-  }
+  // ---- epilogue: lane holds features 16f + 4*g4 + r (of the wave's FW) of
+  // token 16t + j (of its 64); the wave's features are HW whole heads
   const float k2 = sa_rope::bf16_rot_k2(a.conc);
   uint16_t* qo = reinterpret_cast<uint16_t*>(a.q_rot);
   uint16_t* kc = reinterpret_cast<uint16_t*>(a.kc);
   uint16_t* vc = reinterpret_cast<uint16_t*>(a.vc);
+  constexpr int FH = D / 16;                      // feature tiles per head
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int m = m0 + 64 * wt + 16 * t + j;
-    if (m >= M) continue;
-    const int b = m / a.T, tt = m - b * a.T;
-    const int64_t crow = a.row0 + tt;               // cache row of this token
-    if (kind == 2) {
-      uint16_t* vp = vc + (((int64_t)b * (a.C / 32) + crow / 32) * a.n_kv + hh) * (int64_t)D * 32 +
-                     crow % 32;
+  for (int hw = 0; hw < HW; ++hw) {
+    const int hd = HPW * nt + HW * wf + hw;       // head in the fused width
+    if (hd >= H) break;
+    const int kind = hd < a.n_q ? 0 : (hd < a.n_q + a.n_kv ? 1 : 2);   // Q, K, V
+    const int hh = kind == 0 ? hd : (kind == 1 ? hd - a.n_q : hd - a.n_q - a.n_kv);
+    const uint16_t* bg = reinterpret_cast<const uint16_t*>(a.bias) + (int64_t)hd * D;
+    float val[FH][TT][4];
 #pragma unroll
-      for (int f = 0; f < FT; ++f)
+    for (int f = 0; f < FH; ++f) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(bg + 16 * f + 4 * g4);
+      const float bv[4] = {bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vp[(16 * f + 4 * g4 + r) * 32] = (uint16_t)(__float_as_uint(val[f][t][r]) >> 16);
-      continue;
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) val[f][t][r] = round_bf16(acc[FH * hw + f][t][r] + bv[r]);
     }
-    uint16_t* row = kind == 0 ? qo + (((int64_t)b * a.T + tt) * a.n_q + hh) * D
-                              : kc + (((int64_t)b * a.C + crow) * a.n_kv + hh) * D;
-    const double2* tb = a.tab + (int64_t)tt * (D / 2);
 #pragma unroll
-    for (int f = 0; f < FT / 2; ++f) {
-      const int e = 16 * f + 4 * g4;                // pair index of r = 0
-      uint32_t y1[4], y2[4];
-      bool ok = true;
-      double2 cs[4];
+    for (int t = 0; t < TT; ++t) {
+      const int m = m0 + 64 * wt + 16 * t + j;
+      if (m >= M) continue;
+      const int b = m / a.T, tt = m - b * a.T;
+      const int64_t crow = a.row0 + tt;             // cache row of this token
+      if (kind == 2) {
+        uint16_t* vp = vc + (((int64_t)b * (a.C / 32) + crow / 32) * a.n_kv + hh) * (int64_t)D * 32 +
+                       crow % 32;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        cs[r] = tb[e + r];
-        const float u = val[f][t][r], v = val[f + FT / 2][t][r];
-        const float cc = (float)cs[r].x, ss = (float)cs[r].y;
-        const float f1 = fmaf(u, cc, -(v * ss)), f2 = fmaf(v, cc, u * ss);
-        const float sum = fabsf(u) + fabsf(v), tol = sum * k2;
-        ok = ok & (sum >= 0x1p-100f) & (fabsf(f1 - sa_rope::bf16_mid(f1)) > tol) &
-             (fabsf(f2 - sa_rope::bf16_mid(f2)) > tol);
-        y1[r] = __float_as_uint(round_bf16(f1)) >> 16;
-        y2[r] = __float_as_uint(round_bf16(f2)) >> 16;
+        for (int f = 0; f < FH; ++f)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            vp[(16 * f + 4 * g4 + r) * 32] = (uint16_t)(__float_as_uint(val[f][t][r]) >> 16);
+        continue;
       }
-      if (__builtin_amdgcn_ballot_w64(!ok) != 0) {   // rare: the fp64 rotation
-        if (!ok) {
+      uint16_t* row = kind == 0 ? qo + (((int64_t)b * a.T + tt) * a.n_q + hh) * D
+                                : kc + (((int64_t)b * a.C + crow) * a.n_kv + hh) * D;
+      const double2* tb = a.tab + (int64_t)tt * (D / 2);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const double u = val[f][t][r], v = val[f + FT / 2][t][r];
-            y1[r] = f64_to_bf16_bits(sa_rope::rot_first(u, v, cs[r].x, cs[r].y));
-            y2[r] = f64_to_bf16_bits(sa_rope::rot_second(u, v, cs[r].x, cs[r].y));
+      for (int f = 0; f < FH / 2; ++f) {
+        const int e = 16 * f + 4 * g4;              // pair index of r = 0
+        uint32_t y1[4], y2[4];
+        bool ok = true;
+        double2 cs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          cs[r] = tb[e + r];
+          const float u = val[f][t][r], v = val[f + FH / 2][t][r];
+          const float cc = (float)cs[r].x, ss = (float)cs[r].y;
+          const float f1 = fmaf(u, cc, -(v * ss)), f2 = fmaf(v, cc, u * ss);
+          const float sum = fabsf(u) + fabsf(v), tol = sum * k2;
+          ok = ok & (sum >= 0x1p-100f) & (fabsf(f1 - sa_rope::bf16_mid(f1)) > tol) &
+               (fabsf(f2 - sa_rope::bf16_mid(f2)) > tol);
+          y1[r] = __float_as_uint(round_bf16(f1)) >> 16;
+          y2[r] = __float_as_uint(round_bf16(f2)) >> 16;
+        }
+        if (__builtin_amdgcn_ballot_w64(!ok) != 0) {   // rare: the fp64 rotation
+          if (!ok) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const double u = val[f][t][r], v = val[f + FH / 2][t][r];
+              y1[r] = f64_to_bf16_bits(sa_rope::rot_first(u, v, cs[r].x, cs[r].y));
+              y2[r] = f64_to_bf16_bits(sa_rope::rot_second(u, v, cs[r].x, cs[r].y));
+            }
           }
         }
+        *reinterpret_cast<u32x2*>(row + e) = u32x2{y1[0] | (y1[1] << 16), y1[2] | (y1[3] << 16)};
+        *reinterpret_cast<u32x2*>(row + e + D / 2) =
+            u32x2{y2[0] | (y2[1] << 16), y2[2] | (y2[3] << 16)};
       }
-      *reinterpret_cast<u32x2*>(row + e) = u32x2{y1[0] | (y1[1] << 16), y1[2] | (y1[3] << 16)};
-      *reinterpret_cast<u32x2*>(row + e + D / 2) =
-          u32x2{y2[0] | (y2[1] << 16), y2[2] | (y2[3] << 16)};
     }
   }
 }
 
 template <int D>
 hipError_t launch_d(const QkvArgs& a, hipStream_t s) {
+  constexpr int HPW = D == 64 ? 4 : 2;
   const int M = a.B * a.T;
   const int n_mt = (M + kTM - 1) / kTM;
   const int H = a.n_q + 2 * a.n_kv;
-  const int n_nt = (H + 1) / 2;
+  const int n_nt = (H + HPW - 1) / HPW;
   hipLaunchKernelGGL(qkv_rope_append_kernel<D>, dim3((unsigned)(n_mt * n_nt)), dim3(kThreads), 0,
                      s, a, n_mt);
   return hipGetLastError();
