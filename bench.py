@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
 # valid only for the kernel sources it was measured on.
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "e057beb4f1060980", "bytes": 88971422}
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "a42622dd891aba8e", "bytes": 88944861}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_kernels.h")
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
@@ -355,6 +355,64 @@ def decode_extra(sa, torch, steps_warm=4):
     return {"workload": w.name, **res}
 
 
+QKV_D_MODEL = {"gpt-oss": 2880, "gpt-oss-lite": 768}   # residual widths (study note; visual guide)
+
+
+def qkv_extra(sa, torch):
+    """The fused qkv projection with the RoPE + append epilogue
+    (sinkattn_qkv_rope_append) on the two prefill workloads' shapes, seeded
+    random bf16 weights: TFLOP/s of the projection (2 B T d_qkv d_model per
+    launch), against the same step done as torch's bf16 linear (the
+    library GEMM) followed by kv_cache_append_rope_qk."""
+    import workloads as wl
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    for w, key in ((wl.GPTOSS_PREFILL, "gpt-oss"), (wl.LITE_PREFILL, "gpt-oss-lite")):
+        dm = QKV_D_MODEL[key]
+        y = sa.Yarn(w.d_h, w.yarn.base, w.yarn.factor, w.yarn.orig_ctx, w.yarn.alpha, w.yarn.beta)
+        N = w.d_h * (w.n_q + 2 * w.n_kv)
+        x = torch.randn(w.B, w.T, dm, device="cuda", generator=g).to(torch.bfloat16)
+        W = (torch.randn(N, dm, device="cuda", generator=g) / dm ** 0.5).to(torch.bfloat16)
+        b = (0.1 * torch.randn(N, device="cuda", generator=g)).to(torch.bfloat16)
+        c = sa.KVCache.empty(w.B, w.capacity, w.n_kv, w.d_h)
+        snap = c.snapshot()
+        qo = torch.empty(w.B, w.T, w.n_q, w.d_h, device="cuda", dtype=torch.bfloat16)
+        ws = torch.empty(sa.qkv_workspace_bytes(w.T, w.d_h), dtype=torch.uint8, device="cuda")
+
+        def fused():
+            c.restore(snap)
+            sa.qkv_rope_append(c, x, W, b, w.n_q, y, q_out=qo, workspace=ws)
+
+        def separate():
+            c.restore(snap)
+            qkv = torch.nn.functional.linear(x, W, b)
+            q = qkv[..., :w.n_q * w.d_h].reshape(w.B, w.T, w.n_q, w.d_h).contiguous()
+            k = qkv[..., w.n_q * w.d_h:(w.n_q + w.n_kv) * w.d_h].reshape(
+                w.B, w.T, w.n_kv, w.d_h).contiguous()
+            v = qkv[..., (w.n_q + w.n_kv) * w.d_h:].reshape(w.B, w.T, w.n_kv, w.d_h).contiguous()
+            c.append_rope_qk(q, k, v, y, q_out=qo)
+
+        fl = 2.0 * w.B * w.T * N * dm
+        res = {"B": w.B, "T": w.T, "d_model": dm, "d_qkv": N, "gflop": round(fl / 1e9, 2)}
+        for nm, f in (("fused", fused), ("torch_linear_then_append_rope_qk", separate)):
+            f()
+            torch.cuda.synchronize()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            for _ in range(KERNEL_REPEAT):
+                f()
+            b_.record()
+            torch.cuda.synchronize()
+            us = a_.elapsed_time(b_) / KERNEL_REPEAT * 1e3
+            res[nm] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
+                       "frac_mfma": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        out[key] = res
+        del x, W, b, c, qo, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, layers, budget_s):
     """The oracle as it stands on a bounded sample of the timed step:
     RoPE of all of Q and K (fp64) and attention for a seeded sample of query
@@ -466,6 +524,7 @@ def main():
         del gl
         torch.cuda.empty_cache()
         line["extra"]["long_decode"] = decode_extra(sa, torch)
+        line["extra"]["qkv_projection"] = qkv_extra(sa, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, layers, args.cpu_seconds)
     print(json.dumps(line), flush=True)
