@@ -15,6 +15,8 @@ Modules
              dense mask-matrix form
   kvcache    append-only cache with snapshot/restore; KV byte count
   qkv        fused qkv projection (x W^T + b rounded once) and its [Q | K | V] split
+  moe        top-k router with a stable tie-break, softmax over the selected
+             logits, dispatch by expert, SwiGLU experts, weighted combine
   ring       sliding-window ring cache of band layers (W rows, slot p mod W),
              its band mask in ring coordinates, KV entry counts
 
