@@ -318,6 +318,56 @@ int sinkattn_qkv_rope_append(sa_kv_cache* c, const void* x, const void* w_qkv,
                              int n_q, const sa_yarn* y, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* ---- MoE layer: top-k router, dispatch, selected SwiGLU experts ----
+ * "MoE-Xtend" README, MOE ROUTING: S = X W_r^T, I = topk(S, k), w =
+ * softmax over the k selected logits, y = sum_i w_i E_i(x); the batched form
+ * groups token rows by expert and evaluates only the selected experts; top-k
+ * ties must break consistently.  "GPT-OSS-Lite" visual guide, Architecture
+ * Specifications: 8 routed experts, 2 active per token, 1 shared expert,
+ * SwiGLU experts (ffn 1536).
+ * Shapes: x [N, d_model] bf16 (the normed hidden states); w_router [E,
+ * d_model] bf16; w13 [E, 2 ffn, d_model] bf16, the gate rows W1 then the
+ * up rows W3 of each expert (linear layers' [out, in] weights); w2 [E,
+ * d_model, ffn] bf16.  Limits: 1 <= E <= 64, 1 <= k <= min(8, E), d_model a
+ * multiple of 64, ffn a multiple of 128 (SA_ERR_SHAPE otherwise).  All
+ * device pointers caller-owned and 16-byte aligned. */
+
+/* Router: logits = x W_r^T rounded once to bf16 (logits: device [N, E]
+ * bf16, written); per token the k largest logits, largest first, equal
+ * logits in increasing expert id (expert_ids: device int32 [N, k]); weights
+ * = softmax of those k logits in fp32 (device float [N, k]). */
+int moe_route(const void* x, int N, int d_model, const void* w_router, int E, int k,
+              void* logits, int32_t* expert_ids, float* weights, void* stream);
+
+/* Bytes of scratch moe_dispatch needs for N tokens and E experts. */
+size_t moe_dispatch_workspace_bytes(int N, int E);
+
+/* Group the (token, slot) pairs by expert, deterministically: rows (device
+ * int32 [N*k]) lists token*k + slot for expert 0's pairs in token order,
+ * then expert 1's, ...; expert_start (device int32 [E+1]) holds the first
+ * row of each expert and the total.  expert_ids: device int32 [N, k], the
+ * k ids of a token distinct and in [0, E) (ids outside are skipped and
+ * leave their rows unwritten). */
+int moe_dispatch(const int32_t* expert_ids, int N, int E, int k, int32_t* rows,
+                 int32_t* expert_start, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace moe_layer needs (ffn_shared = 0: no shared expert). */
+size_t moe_workspace_bytes(int N, int d_model, int E, int k, int ffn, int ffn_shared);
+
+/* The whole layer: moe_route, moe_dispatch, then for each expert's rows
+ * h = bf16(silu(a) * b), a = bf16(x W1^T), b = bf16(x W3^T), and
+ * o = bf16(h W2^T); y = bf16(sum over the token's slots of w * o, plus the
+ * shared expert's o with weight 1 when ffn_shared > 0 (w13_shared [2
+ * ffn_shared, d_model], w2_shared [d_model, ffn_shared]; both null and
+ * ffn_shared = 0 otherwise)), summed in fp32 in slot order (shared last).
+ * y: device [N, d_model] bf16.  The workspace (moe_workspace_bytes) holds
+ * the logits, ids, weights, dispatch lists, the gated activations and the
+ * per-slot outputs; its contents are overwritten. */
+int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, int k,
+              const void* w13, const void* w2, int ffn, const void* w13_shared,
+              const void* w2_shared, int ffn_shared, void* y, void* workspace,
+              size_t ws_bytes, void* stream);
+
 /* Bytes of fp32 workspace that sinkattn_decode needs for any cache offset up
  * to `capacity` with these shapes (0 on invalid arguments). */
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h,

@@ -82,6 +82,12 @@ _sinkattn_prefill_rope = _sig("sinkattn_prefill_rope", _i32, _vp, _vp, _vp, _vp,
 _sinkattn_qkv_ws = _sig("sinkattn_qkv_workspace_bytes", _sz, _i32, _i32)
 _sinkattn_qkv = _sig("sinkattn_qkv_rope_append", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                      _i32, ctypes.POINTER(SaYarn), _vp, _sz, _vp)
+_moe_route = _sig("moe_route", _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp)
+_moe_dispatch_ws = _sig("moe_dispatch_workspace_bytes", _sz, _i32, _i32)
+_moe_dispatch = _sig("moe_dispatch", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
+_moe_ws = _sig("moe_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
+_moe_layer = _sig("moe_layer", _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp,
+                  _i32, _vp, _vp, _sz, _vp)
 _sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
 _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                         _i32, _f32, _vp, _sz, _vp)
@@ -426,6 +432,62 @@ def qkv_rope_append(cache: KVCache, x: torch.Tensor, w_qkv: torch.Tensor, b_qkv:
                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                          _stream(stream)))
     return q_out
+
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int, stream=None):
+    """moe_route: x [N, d_model], w_router [E, d_model] (bf16) -> (logits bf16
+    [N, E], expert ids int32 [N, k], weights float32 [N, k])."""
+    N, dm = x.shape
+    E = w_router.shape[0]
+    logits = torch.empty((N, E), dtype=torch.bfloat16, device=x.device)
+    ids = torch.empty((N, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    _check(_moe_route(_dev(x, "x"), N, dm, _dev(w_router, "w_router"), E, int(k),
+                      _dev(logits, "logits"), _dev(ids, "ids"), _dev(w, "weights"), _stream(stream)))
+    return logits, ids, w
+
+
+def moe_dispatch(ids: torch.Tensor, E: int, stream=None):
+    """moe_dispatch: ids int32 [N, k] -> (rows int32 [N*k] = token*k + slot
+    grouped by expert then token, expert_start int32 [E+1])."""
+    N, k = ids.shape
+    rows = torch.empty(N * k, dtype=torch.int32, device=ids.device)
+    start = torch.empty(E + 1, dtype=torch.int32, device=ids.device)
+    ws = torch.empty(max(int(_moe_dispatch_ws(N, E)), 16), dtype=torch.uint8, device=ids.device)
+    _check(_moe_dispatch(_dev(ids, "ids"), N, int(E), k, _dev(rows, "rows"), _dev(start, "start"),
+                         _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+    return rows, start
+
+
+def moe_workspace_bytes(N, d_model, E, k, ffn, ffn_shared=0) -> int:
+    return int(_moe_ws(N, d_model, E, k, ffn, ffn_shared))
+
+
+def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, k: int,
+              shared=None, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_layer: x [N, d_model]; w_router [E, d_model]; w13 [E, 2 ffn,
+    d_model]; w2 [E, d_model, ffn]; shared = (w13s [2 ffn_s, d_model], w2s
+    [d_model, ffn_s]) or None.  Returns y [N, d_model] bf16."""
+    N, dm = x.shape
+    E, two_ffn, _ = w13.shape
+    ffn = two_ffn // 2
+    if shared is not None:
+        w13s, w2s = shared
+        ffn_s = w13s.shape[0] // 2
+        p13, p2 = _dev(w13s, "w13_shared"), _dev(w2s, "w2_shared")
+    else:
+        ffn_s, p13, p2 = 0, None, None
+    if out is None:
+        out = torch.empty((N, dm), dtype=torch.bfloat16, device=x.device)
+    need = moe_workspace_bytes(N, dm, E, k, ffn, ffn_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(_moe_layer(_dev(x, "x"), N, dm, _dev(w_router, "w_router"), E, int(k), _dev(w13, "w13"),
+                      _dev(w2, "w2"), ffn, p13, p2, ffn_s, _dev(out, "out"),
+                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                      _stream(stream)))
+    return out
 
 
 def decode_workspace_bytes(B, n_q, n_kv, d, capacity) -> int:

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsinkattn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["sinkattn_abi.hip", "rope.hip", "append.hip", "prefill.hip", "decode.hip", "qkv.hip",
+SOURCES = ["sinkattn_abi.hip", "rope.hip", "append.hip", "prefill.hip", "decode.hip", "qkv.hip", "moe.hip",
            "attn_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -19,9 +19,7 @@
 //    per 16x16 tile, and the two halves of a RoPE pair (e, e + d/2) sit in
 //    the same lane (d/2 is a multiple of 16).
 //  * Both operands are contiguous along d_model (W is the linear layer's
-//    [out, in] matrix), so 64-wide slices of W and x go global -> LDS with
-//    16-byte global_load_lds, 16-byte chunk c of row r at slot c ^ (r & 7)
-//    (conflict-free operand reads); two LDS stages, one barrier per stage.
+//    [out, in] matrix); the contraction is the shared GEMM core (sa_gemm.h).
 //  * Epilogue in registers: + bias (fp32), one rounding to bf16, rotation
 //    against a per-position table of fp64 (c cos, c sin) built by a small
 //    kernel first (the same sincos_reduced as every RoPE path), fp32 where
@@ -30,19 +28,13 @@
 //    layout (16 lanes = 16 consecutive keys of one coordinate).
 #include "sa_device.h"
 #include "sa_kernels.h"
+#include "sa_gemm.h"
 #include "sa_rope.h"
 
 namespace {
 
-constexpr int kThreads = 512;  // 8 waves: 2 feature halves x 4 token quarters
-constexpr int kTM = 256;       // tokens per workgroup
-constexpr int kKS = 64;       // contraction elements per LDS stage
-
-__device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* lds_block) {
-  __builtin_amdgcn_global_load_lds(
-      src, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(lds_block)), 16, 0, 0);
-}
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+constexpr int kThreads = sa_gemm::kThreads;   // 8 waves: 2 feature halves x 4 token quarters
+constexpr int kTM = sa_gemm::kTM;             // tokens per workgroup
 
 // tab[t][i] = (c cos, c sin)(pos0 + t) * inv_freq_i), fp64
 __global__ __launch_bounds__(kThreads) void rope_table_kernel(QkvArgs a) {
@@ -66,20 +58,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, int n_mt) {
   constexpr int HPW = D == 64 ? 4 : 2;  // heads per workgroup
   constexpr int F = HPW * D;            // features per workgroup (256, 192, 256)
-  constexpr int FW = F / 2;             // features per wave
-  constexpr int FT = FW / 16;           // 16-feature tiles per wave
   constexpr int HW = HPW / 2;           // heads per wave
-  constexpr int TT = 4;                 // 16-token tiles per wave
-  constexpr int WBUF = F * kKS;         // elements per stage
-  constexpr int XBUF = kTM * kKS;
-  constexpr int NWV = kThreads / 64;    // waves
-  constexpr int WBLK = F * 8 / 64;      // 1 KB blocks per W stage
-  constexpr int XBLK = kTM * 8 / 64;
-  constexpr int WBW = WBLK / NWV, XBW = XBLK / NWV;
-  static_assert(WBLK % NWV == 0 && XBLK % NWV == 0, "blocks split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (WBUF + XBUF)];
-  auto Wb = [&](int s) { return lds + s * (WBUF + XBUF); };
-  auto Xb = [&](int s) { return lds + s * (WBUF + XBUF) + WBUF; };
+  using G = sa_gemm::Gemm<F>;
+  constexpr int TT = G::TT;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_ELEMS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
@@ -90,65 +72,24 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
   const int dqkv = H * D;
   const int m0 = mt * kTM, f0 = nt * F;
 
-  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
-  const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w);
-  // global element offset (without k0) of the chunk each lane fetches into
-  // slot `lane` of its blocks; rows past the ends are clamped (never stored)
-  uint32_t w_off[WBW], x_off[XBW];
+  // element offsets of the chunks this lane stages; rows past the ends are
+  // clamped (their results are never stored)
+  uint32_t w_off[G::WBW], x_off[G::XBW];
 #pragma unroll
-  for (int i = 0; i < WBW; ++i) {
-    const int sl = 64 * (wave + NWV * i) + lane;
-    const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
-    const int row = min(f0 + r, dqkv - 1);
-    w_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
+  for (int i = 0; i < G::WBW; ++i) {
+    int r, c;
+    G::w_slot(i, &r, &c);
+    w_off[i] = (uint32_t)min(f0 + r, dqkv - 1) * (uint32_t)a.d_model + 8 * c;
   }
 #pragma unroll
-  for (int i = 0; i < XBW; ++i) {
-    const int sl = 64 * (wave + NWV * i) + lane;
-    const int r = sl >> 3, c = (sl & 7) ^ (r & 7);
-    const int row = min(m0 + r, M - 1);
-    x_off[i] = (uint32_t)row * (uint32_t)a.d_model + 8 * c;
+  for (int i = 0; i < G::XBW; ++i) {
+    int r, c;
+    G::x_slot(i, &r, &c);
+    x_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)a.d_model + 8 * c;
   }
-  auto load_stage = [&](int s, int k0) {
-#pragma unroll
-    for (int i = 0; i < WBW; ++i) lds_direct16(wg + w_off[i] + k0, &Wb(s)[512 * (wave + NWV * i)]);
-#pragma unroll
-    for (int i = 0; i < XBW; ++i) lds_direct16(xg + x_off[i] + k0, &Xb(s)[512 * (wave + NWV * i)]);
-  };
-  // operand reads: row r, chunk c -> r*64 + 8*(c ^ (r & 7)); the rows of a
-  // lane's tiles differ by multiples of 16, so r & 7 = j & 7
-  const int swz = j & 7;
-  const int wrow0 = FW * wf + j, xrow0 = 64 * wt + j;
-
-  f32x4 acc[FT][TT];
-#pragma unroll
-  for (int f = 0; f < FT; ++f)
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = a.d_model / kKS;
-  load_stage(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int s = ks & 1;
-    if (ks + 1 < nks) load_stage(s ^ 1, (ks + 1) * kKS);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int cofs = 8 * ((g4 + 4 * kk) ^ swz);
-      u32x4 A[FT], Bx[TT];
-#pragma unroll
-      for (int f = 0; f < FT; ++f) A[f] = ld16(&Wb(s)[(wrow0 + 16 * f) * kKS + cofs]);
-#pragma unroll
-      for (int t = 0; t < TT; ++t) Bx[t] = ld16(&Xb(s)[(xrow0 + 16 * t) * kKS + cofs]);
-#pragma unroll
-      for (int f = 0; f < FT; ++f)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[f][t] = mfma16x16x32(A[f], Bx[t], acc[f][t]);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
+  f32x4 acc[G::FT][TT];
+  G::run(reinterpret_cast<const uint16_t*>(a.w), w_off, reinterpret_cast<const uint16_t*>(a.x),
+         x_off, a.d_model, lds, acc);
 
   // ---- epilogue: lane holds features 16f + 4*g4 + r (of the wave's FW) of
   // token 16t + j (of its 64); the wave's features are HW whole heads

@@ -75,6 +75,34 @@ struct QkvArgs {
 };
 hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s);
 
+// MoE layer: router, dispatch, experts, combine.
+struct MoeArgs {
+  const void* x;          // [N, d_model] bf16
+  const void* w_router;   // [E, d_model] bf16
+  int N, d_model, E, k;   // E <= 64, k <= 8
+  void* logits;           // [N, E] bf16
+  int32_t* ids;           // [N, k]
+  float* weights;         // [N, k]
+  int32_t* counts;        // [blocks of 256 tokens, E]
+  int32_t* offsets;       // [blocks, E]
+  int32_t* expert_start;  // [E + 1]
+  int32_t* tile_start;    // [E + 1]: first 256-row tile of each expert
+  int32_t* rows;          // [N * k]: token * k + slot, by expert then token
+  float* out_slots;       // [N, k + 1, d_model]: weighted expert outputs (slot k: shared)
+  void* y;                // [N, d_model] bf16
+};
+struct MoeGroup {         // one set of SwiGLU experts
+  const void* w13;        // [E, 2 ffn, d_model]: gate rows, then up rows
+  const void* w2;         // [E, d_model, ffn]
+  void* h;                // [rows, ffn] bf16 scratch
+  int ffn;
+  int shared;             // 1: one expert over every token, weight 1, slot k
+};
+hipError_t launch_moe_route(const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_dispatch(const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_experts(const MoeArgs& a, const MoeGroup& g, hipStream_t s);
+hipError_t launch_moe_combine(const MoeArgs& a, int nslots, hipStream_t s);
+
 struct AttnArgs {
   const void* q;        // [B, T_q, n_q, d]
   const void* kc;       // [B, C, n_kv, d]

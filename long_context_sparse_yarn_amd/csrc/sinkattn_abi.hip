@@ -650,6 +650,161 @@ int sinkattn_qkv_rope_append(sa_kv_cache* c, const void* x, const void* w_qkv, c
   return ok();
 }
 
+// ---- MoE layer
+namespace {
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+struct MoeLayout {          // byte offsets of the workspace sections
+  size_t logits, ids, weights, counts, offsets, expert_start, tile_start, rows, h, hs, out, total;
+};
+static MoeLayout moe_layout(int N, int d_model, int E, int k, int ffn, int ffn_s) {
+  MoeLayout L;
+  const size_t nblk = ((size_t)N + 255) / 256;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.logits = take((size_t)N * E * 2);
+  L.ids = take((size_t)N * k * 4);
+  L.weights = take((size_t)N * k * 4);
+  L.counts = take(nblk * E * 4);
+  L.offsets = take(nblk * E * 4);
+  L.expert_start = take((size_t)(E + 1) * 4);
+  L.tile_start = take((size_t)(E + 1) * 4);
+  L.rows = take((size_t)N * k * 4);
+  L.h = take((size_t)N * k * ffn * 2);
+  L.hs = take((size_t)N * ffn_s * 2);
+  L.out = take((size_t)N * (k + 1) * d_model * 4);
+  L.total = o;
+  return L;
+}
+static int moe_check(int N, int d_model, int E, int k) {
+  if (N <= 0 || d_model <= 0) return fail(SA_ERR_ARG, "non-positive size");
+  if (E < 1 || E > 64) return fail(SA_ERR_SHAPE, "E must be in [1, 64], got %d", E);
+  if (k < 1 || k > 8 || k > E) return fail(SA_ERR_SHAPE, "k must be in [1, min(8, E)], got %d", k);
+  if (d_model % 64) return fail(SA_ERR_SHAPE, "d_model must be a multiple of 64, got %d", d_model);
+  if ((int64_t)N * d_model > UINT32_MAX || (int64_t)N * k > INT32_MAX)
+    return fail(SA_ERR_ARG, "N too large");
+  return SA_OK;
+}
+}  // namespace
+
+size_t moe_workspace_bytes(int N, int d_model, int E, int k, int ffn, int ffn_shared) {
+  if (N <= 0 || d_model <= 0 || E <= 0 || k <= 0 || ffn < 0 || ffn_shared < 0) return 0;
+  return moe_layout(N, d_model, E, k, ffn, ffn_shared).total;
+}
+
+int moe_route(const void* x, int N, int d_model, const void* w_router, int E, int k, void* logits,
+              int32_t* expert_ids, float* weights, void* stream) {
+  if (!x || !w_router || !logits || !expert_ids || !weights) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(x) || misaligned(w_router)) return fail(SA_ERR_ARG, "x and w_router must be 16-byte aligned");
+  int st = moe_check(N, d_model, E, k);
+  if (st != SA_OK) return st;
+  MoeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.w_router = w_router;
+  a.N = N;
+  a.d_model = d_model;
+  a.E = E;
+  a.k = k;
+  a.logits = logits;
+  a.ids = expert_ids;
+  a.weights = weights;
+  hipError_t e = launch_moe_route(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
+size_t moe_dispatch_workspace_bytes(int N, int E) {
+  if (N <= 0 || E <= 0) return 0;
+  const size_t nblk = ((size_t)N + 255) / 256;
+  return 2 * align256(nblk * E * 4) + align256((size_t)(E + 1) * 4);
+}
+
+int moe_dispatch(const int32_t* expert_ids, int N, int E, int k, int32_t* rows,
+                 int32_t* expert_start, void* workspace, size_t ws_bytes, void* stream) {
+  if (!expert_ids || !rows || !expert_start || !workspace) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(workspace)) return fail(SA_ERR_ARG, "workspace must be 16-byte aligned");
+  if (N <= 0) return fail(SA_ERR_ARG, "non-positive size");
+  if (E < 1 || E > 64 || k < 1 || k > 8 || k > E) return fail(SA_ERR_SHAPE, "need 1 <= k <= min(8, E), E <= 64");
+  if ((int64_t)N * k > INT32_MAX) return fail(SA_ERR_ARG, "N too large");
+  const size_t need = moe_dispatch_workspace_bytes(N, E);
+  if (ws_bytes < need) return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  const size_t nblk = ((size_t)N + 255) / 256;
+  char* w = static_cast<char*>(workspace);
+  MoeArgs a;
+  memset(&a, 0, sizeof a);
+  a.N = N;
+  a.E = E;
+  a.k = k;
+  a.ids = const_cast<int32_t*>(expert_ids);
+  a.counts = reinterpret_cast<int32_t*>(w);
+  a.offsets = reinterpret_cast<int32_t*>(w + align256(nblk * E * 4));
+  a.tile_start = reinterpret_cast<int32_t*>(w + 2 * align256(nblk * E * 4));
+  a.expert_start = expert_start;
+  a.rows = rows;
+  hipError_t e = launch_moe_dispatch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  return ok();
+}
+
+int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, int k,
+              const void* w13, const void* w2, int ffn, const void* w13_shared,
+              const void* w2_shared, int ffn_shared, void* y, void* workspace, size_t ws_bytes,
+              void* stream) {
+  if (!x || !w_router || !w13 || !w2 || !y || !workspace) return fail(SA_ERR_ARG, "null argument");
+  if (misaligned(x) || misaligned(w_router) || misaligned(w13) || misaligned(w2) || misaligned(y) ||
+      misaligned(workspace))
+    return fail(SA_ERR_ARG, "pointers must be 16-byte aligned");
+  int st = moe_check(N, d_model, E, k);
+  if (st != SA_OK) return st;
+  if (ffn <= 0 || ffn % 128) return fail(SA_ERR_SHAPE, "ffn must be a positive multiple of 128, got %d", ffn);
+  const bool shared = ffn_shared > 0;
+  if (shared) {
+    if (!w13_shared || !w2_shared) return fail(SA_ERR_ARG, "shared expert weights are null");
+    if (misaligned(w13_shared) || misaligned(w2_shared)) return fail(SA_ERR_ARG, "pointers must be 16-byte aligned");
+    if (ffn_shared % 128) return fail(SA_ERR_SHAPE, "ffn_shared must be a multiple of 128, got %d", ffn_shared);
+  } else if (ffn_shared < 0 || w13_shared || w2_shared) {
+    return fail(SA_ERR_ARG, "no shared expert: ffn_shared = 0 and null shared weights");
+  }
+  if ((int64_t)N * k * ffn > UINT32_MAX || (int64_t)N * ffn_shared > UINT32_MAX ||
+      (int64_t)2 * ffn * d_model > UINT32_MAX || (int64_t)2 * ffn_shared * d_model > UINT32_MAX)
+    return fail(SA_ERR_ARG, "sizes too large");
+  const MoeLayout L = moe_layout(N, d_model, E, k, ffn, shared ? ffn_shared : 0);
+  if (ws_bytes < L.total) return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+  char* w = static_cast<char*>(workspace);
+  MoeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.w_router = w_router;
+  a.N = N;
+  a.d_model = d_model;
+  a.E = E;
+  a.k = k;
+  a.logits = w + L.logits;
+  a.ids = reinterpret_cast<int32_t*>(w + L.ids);
+  a.weights = reinterpret_cast<float*>(w + L.weights);
+  a.counts = reinterpret_cast<int32_t*>(w + L.counts);
+  a.offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  a.expert_start = reinterpret_cast<int32_t*>(w + L.expert_start);
+  a.tile_start = reinterpret_cast<int32_t*>(w + L.tile_start);
+  a.rows = reinterpret_cast<int32_t*>(w + L.rows);
+  a.out_slots = reinterpret_cast<float*>(w + L.out);
+  a.y = y;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_moe_route(a, s);
+  if (e == hipSuccess) e = launch_moe_dispatch(a, s);
+  if (e == hipSuccess) {
+    MoeGroup g{w13, w2, w + L.h, ffn, 0};
+    e = launch_moe_experts(a, g, s);
+  }
+  if (e == hipSuccess && shared) {
+    MoeGroup g{w13_shared, w2_shared, w + L.hs, ffn_shared, 1};
+    e = launch_moe_experts(a, g, s);
+  }
+  if (e == hipSuccess) e = launch_moe_combine(a, shared ? k + 1 : k, s);
+  if (e != hipSuccess) return hip_fail(e, "moe launch");
+  return ok();
+}
+
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h, int64_t capacity) {
   if (B <= 0 || n_q <= 0 || n_kv <= 0 || d_h <= 0 || capacity <= 0 || n_q % n_kv) return 0;
   const int64_t S = decode_max_splits(B, n_kv, capacity);

@@ -285,3 +285,30 @@ def test_qkv_errors_before_any_launch():
     st, r = ring(Bn=2, W=128, n_kv=2, d=64)
     assert call(args(c=r)) == SA_ERR_ARG                                     # a ring: use its stage
     B._kv_cache_destroy(r)
+
+
+def test_moe_errors_before_any_launch():
+    x, w, y, ws = (ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000),
+                   ctypes.c_void_p(0x60000))
+    ids, wt, lg = ctypes.c_void_p(0x70000), ctypes.c_void_p(0x80000), ctypes.c_void_p(0x90000)
+    R = B._moe_route
+    assert R(x, 100, 64, w, 65, 2, lg, ids, wt, None) == SA_ERR_SHAPE        # E > 64
+    assert R(x, 100, 64, w, 8, 9, lg, ids, wt, None) == SA_ERR_SHAPE         # k > 8
+    assert R(x, 100, 64, w, 2, 3, lg, ids, wt, None) == SA_ERR_SHAPE         # k > E
+    assert R(x, 100, 96, w, 8, 2, lg, ids, wt, None) == SA_ERR_SHAPE         # d_model % 64
+    assert R(None, 100, 64, w, 8, 2, lg, ids, wt, None) == SA_ERR_ARG
+    assert R(x, 0, 64, w, 8, 2, lg, ids, wt, None) == SA_ERR_ARG
+    D = B._moe_dispatch
+    need = B._moe_dispatch_ws(1000, 8)
+    assert need > 0
+    assert D(ids, 1000, 8, 2, y, y, ws, need - 1, None) == SA_ERR_ARG
+    assert D(ids, 1000, 65, 2, y, y, ws, need, None) == SA_ERR_SHAPE
+    L = B._moe_layer
+    nb = B._moe_ws(100, 64, 8, 2, 128, 0)
+    assert nb > 0 and B._moe_ws(100, 64, 8, 2, 128, 128) > nb
+    assert L(x, 100, 64, w, 8, 2, w, w, 100, None, None, 0, y, ws, nb, None) == SA_ERR_SHAPE   # ffn % 128
+    assert L(x, 100, 64, w, 8, 2, w, w, 128, None, None, 0, y, ws, nb - 1, None) == SA_ERR_ARG
+    assert L(x, 100, 64, w, 8, 2, w, w, 128, w, None, 128, y, ws, 1 << 30, None) == SA_ERR_ARG  # half the shared
+    assert L(x, 100, 64, w, 8, 2, w, w, 128, w, w, 0, y, ws, 1 << 30, None) == SA_ERR_ARG       # weights, no ffn
+    assert L(x, 100, 64, w, 8, 2, w, w, 128, None, None, 0, ctypes.c_void_p(0x50004), ws, nb,
+             None) == SA_ERR_ARG
