@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
 # valid only for the kernel sources it was measured on.
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "a42622dd891aba8e", "bytes": 88944861}
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "a54282df5826b878", "bytes": 88906397}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_kernels.h")
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
@@ -413,6 +413,68 @@ def qkv_extra(sa, torch):
     return out
 
 
+# GPT-OSS-Lite MoE layer (visual guide, Architecture Specifications): 8 routed
+# SwiGLU experts of width 1536, top 2, one shared expert, d_model 768, on the
+# prefill workload's 4 x 4096 tokens
+MOE_LITE = {"N": 4 * 4096, "d_model": 768, "E": 8, "k": 2, "ffn": 1536, "ffn_shared": 1536}
+
+
+def moe_extra(sa, torch):
+    """moe_layer on the GPT-OSS-Lite MoE shape with seeded random bf16
+    weights: TFLOP/s of the expert GEMMs actually run (router, N k routed
+    rows through gate, up and down, N rows through the shared expert),
+    against the same layer written with torch ops (bf16 linears, topk,
+    one masked gather per expert)."""
+    c = MOE_LITE
+    N, dm, E, k, ffn, fs = c["N"], c["d_model"], c["E"], c["k"], c["ffn"], c["ffn_shared"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    rn = lambda *sh, fan: (torch.randn(*sh, device="cuda", generator=g) / fan ** 0.5).to(torch.bfloat16)
+    x = torch.randn(N, dm, device="cuda", generator=g).to(torch.bfloat16)
+    wr, w13, w2 = rn(E, dm, fan=dm), rn(E, 2 * ffn, dm, fan=dm), rn(E, dm, ffn, fan=ffn)
+    w13s, w2s = rn(2 * fs, dm, fan=dm), rn(dm, fs, fan=fs)
+    ws = torch.empty(sa.moe_workspace_bytes(N, dm, E, k, ffn, fs), dtype=torch.uint8, device="cuda")
+    y = torch.empty(N, dm, dtype=torch.bfloat16, device="cuda")
+
+    def fused():
+        sa.moe_layer(x, wr, w13, w2, k, shared=(w13s, w2s), out=y, workspace=ws)
+
+    def torch_layer():
+        logits = torch.nn.functional.linear(x, wr)
+        val, idx = torch.topk(logits.float(), k, dim=1)
+        wts = torch.softmax(val, dim=1)
+        acc = torch.zeros(N, dm, dtype=torch.float32, device="cuda")
+        for e in range(E):
+            tok, slot = (idx == e).nonzero(as_tuple=True)
+            xe = x[tok]
+            gu = torch.nn.functional.linear(xe, w13[e])
+            h = (torch.nn.functional.silu(gu[:, :ffn].float()) * gu[:, ffn:].float()).to(torch.bfloat16)
+            acc.index_add_(0, tok, wts[tok, slot][:, None] * torch.nn.functional.linear(h, w2[e]).float())
+        gu = torch.nn.functional.linear(x, w13s)
+        h = (torch.nn.functional.silu(gu[:, :fs].float()) * gu[:, fs:].float()).to(torch.bfloat16)
+        return (acc + torch.nn.functional.linear(h, w2s).float()).to(torch.bfloat16)
+
+    fl = 2.0 * N * dm * E + 2.0 * N * k * (2 * ffn * dm + ffn * dm) + 2.0 * N * (2 * fs * dm + fs * dm)
+    res = {"workload": "GPT-OSS-Lite MoE: %d tokens, d_model %d, %d experts top %d, SwiGLU %d, "
+                       "shared %d" % (N, dm, E, k, ffn, fs), "gflop": round(fl / 1e9, 2)}
+    for nm, f in (("moe_layer", fused), ("torch_ops", torch_layer)):
+        f()
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = KERNEL_REPEAT if nm == "moe_layer" else 5
+        a_.record()
+        for _ in range(reps):
+            f()
+        b_.record()
+        torch.cuda.synchronize()
+        us = a_.elapsed_time(b_) / reps * 1e3
+        res[nm] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
+                   "frac_mfma": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    del x, wr, w13, w2, w13s, w2s, ws, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, layers, budget_s):
     """The oracle as it stands on a bounded sample of the timed step:
     RoPE of all of Q and K (fp64) and attention for a seeded sample of query
@@ -525,6 +587,7 @@ def main():
         torch.cuda.empty_cache()
         line["extra"]["long_decode"] = decode_extra(sa, torch)
         line["extra"]["qkv_projection"] = qkv_extra(sa, torch)
+        line["extra"]["moe_layer"] = moe_extra(sa, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, layers, args.cpu_seconds)
     print(json.dumps(line), flush=True)
