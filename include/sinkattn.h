@@ -329,7 +329,8 @@ int sinkattn_qkv_rope_append(sa_kv_cache* c, const void* x, const void* w_qkv,
  * d_model] bf16; w13 [E, 2 ffn, d_model] bf16, the gate rows W1 then the
  * up rows W3 of each expert (linear layers' [out, in] weights); w2 [E,
  * d_model, ffn] bf16.  Limits: 1 <= E <= 64, 1 <= k <= min(8, E), d_model a
- * multiple of 64, ffn a multiple of 128 (SA_ERR_SHAPE otherwise).  All
+ * multiple of 64, ffn a multiple of 128 (SA_ERR_SHAPE otherwise);
+ * ceil(N / 256) * E <= 16384 (SA_ERR_ARG).  All
  * device pointers caller-owned and 16-byte aligned. */
 
 /* Router: logits = x W_r^T rounded once to bf16 (logits: device [N, E]

@@ -27,7 +27,8 @@
 //    rows, so a lane holds both factors of its features and applies
 //    silu(a) * b in registers.  Down: the expert's rows are contiguous; the
 //    epilogue scales by the token's routing weight and writes an fp32 row
-//    per (token, slot).  A combine pass sums the slots in order.
+//    per (token, slot).  The slots are summed in order by the shared
+//    expert's down pass when there is one, else by a combine pass.
 #include "sa_device.h"
 #include "sa_gemm.h"
 #include "sa_kernels.h"
@@ -127,12 +128,15 @@ __global__ __launch_bounds__(kBlock) void moe_count_kernel(MoeArgs a) {
 // one workgroup: thread e turns expert e's per-block counts into offsets
 __global__ __launch_bounds__(64) void moe_scan_kernel(MoeArgs a, int nblk) {
   __shared__ int tot[64], first[64];
+  extern __shared__ int cnt[];                    // [nblk][E], loaded in parallel
   const int e = threadIdx.x;
+  for (int i = threadIdx.x; i < nblk * a.E; i += 64) cnt[i] = a.counts[i];
+  __syncthreads();
   int run = 0;
   if (e < a.E)
     for (int b = 0; b < nblk; ++b) {
-      const int c = a.counts[b * a.E + e];
-      a.offsets[b * a.E + e] = run;
+      const int c = cnt[b * a.E + e];
+      cnt[b * a.E + e] = run;
       run += c;
     }
   tot[e] = e < a.E ? run : 0;
@@ -150,8 +154,7 @@ __global__ __launch_bounds__(64) void moe_scan_kernel(MoeArgs a, int nblk) {
     a.tile_start[a.E] = ts;
   }
   __syncthreads();
-  if (e < a.E)
-    for (int b = 0; b < nblk; ++b) a.offsets[b * a.E + e] += first[e];
+  for (int i = threadIdx.x; i < nblk * a.E; i += 64) a.offsets[i] = cnt[i] + first[i % a.E];
 }
 
 __global__ __launch_bounds__(kBlock) void moe_scatter_kernel(MoeArgs a) {
@@ -247,7 +250,11 @@ __global__ __launch_bounds__(kThreads) void moe_up_kernel(MoeArgs a, MoeGroup g,
 }
 
 // out = w * (h W2^T) for 256 rows of one expert x 256 output features
-__global__ __launch_bounds__(kThreads) void moe_down_kernel(MoeArgs a, MoeGroup g, int n_ft) {
+// combine: the shared expert, run last, adds the k routed slots of its rows
+// in slot order and writes y (the same sums, in the same order, as
+// moe_combine_kernel over k + 1 slots)
+__global__ __launch_bounds__(kThreads) void moe_down_kernel(MoeArgs a, MoeGroup g, int n_ft,
+                                                            int combine) {
   using G = sa_gemm::Gemm<256>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_ELEMS];
   const int tile = blockIdx.x / n_ft, ft = blockIdx.x % n_ft;
@@ -290,6 +297,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(MoeArgs a, MoeGroup 
       wgt = a.weights[code];
     }
     float* orow = a.out_slots + ((int64_t)tok * S + slot) * dm;
+    const float* trow = a.out_slots + (int64_t)tok * S * dm;
 #pragma unroll
     for (int f = 0; f < G::FT; ++f) {
       const int feat = f0 + 128 * wf + 16 * f + 4 * g4;
@@ -297,7 +305,15 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(MoeArgs a, MoeGroup 
       f32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = wgt * round_bf16(acc[f][t][q]);
-      *reinterpret_cast<f32x4*>(orow + feat) = o;
+      if (combine) {
+        f32x4 sum = *reinterpret_cast<const f32x4*>(trow + feat);
+        for (int sl = 1; sl < a.k; ++sl) sum += *reinterpret_cast<const f32x4*>(trow + sl * dm + feat);
+        sum += o;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.y) + (int64_t)tok * dm + feat) =
+            u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(orow + feat) = o;
+      }
     }
   }
 }
@@ -334,18 +350,20 @@ hipError_t launch_moe_route(const MoeArgs& a, hipStream_t s) {
 hipError_t launch_moe_dispatch(const MoeArgs& a, hipStream_t s) {
   const int nblk = (a.N + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(moe_count_kernel, dim3(nblk), dim3(kBlock), 0, s, a);
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(64), 0, s, a, nblk);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(64), (size_t)nblk * a.E * sizeof(int), s, a,
+                     nblk);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_moe_experts(const MoeArgs& a, const MoeGroup& g, hipStream_t s) {
+hipError_t launch_moe_experts(const MoeArgs& a, const MoeGroup& g, bool combine, hipStream_t s) {
   // tiles: an upper bound (one partial tile per expert at most); workgroups
   // past the last tile return at once
   const int tiles = g.shared ? (a.N + kTM - 1) / kTM : (a.N * a.k + kTM - 1) / kTM + a.E;
   const int n_up = g.ffn / 128, n_down = (a.d_model + 255) / 256;
   hipLaunchKernelGGL(moe_up_kernel, dim3(tiles * n_up), dim3(kThreads), 0, s, a, g, n_up);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(tiles * n_down), dim3(kThreads), 0, s, a, g, n_down);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(tiles * n_down), dim3(kThreads), 0, s, a, g, n_down,
+                     combine ? 1 : 0);
   return hipGetLastError();
 }
 

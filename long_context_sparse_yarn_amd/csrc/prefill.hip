@@ -37,7 +37,7 @@
 //    multiple of 8, every XCD serves fixed KV heads and their K/V stays in
 //    that XCD's L2; the longest (latest) query blocks start first.
 #include "sa_device.h"
-#include "sa_kernels.h"
+#include "sa_attn.h"
 #include "sa_rope.h"
 
 

@@ -8,6 +8,8 @@
 
 #define SA_MAX_HALF 128   // d_h <= 256
 
+#include "sa_attn.h"
+
 struct RopeArgs {
   const void* src;      // rows read from here ...
   void* x;              // ... and written here (may be the same buffer)
@@ -100,30 +102,10 @@ struct MoeGroup {         // one set of SwiGLU experts
 };
 hipError_t launch_moe_route(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_dispatch(const MoeArgs& a, hipStream_t s);
-hipError_t launch_moe_experts(const MoeArgs& a, const MoeGroup& g, hipStream_t s);
+// combine: the shared group's down pass also sums the routed slots into y
+hipError_t launch_moe_experts(const MoeArgs& a, const MoeGroup& g, bool combine, hipStream_t s);
 hipError_t launch_moe_combine(const MoeArgs& a, int nslots, hipStream_t s);
 
-struct AttnArgs {
-  const void* q;        // [B, T_q, n_q, d]
-  const void* kc;       // [B, C, n_kv, d]
-  const void* vc;       // [B, C/32, n_kv, d, 32]
-  const float* sinks;   // [n_q]
-  void* out;            // [B, T_q, n_q, d]
-  int B, T_q, n_q, n_kv, d, q_mult, window;
-  int64_t C;            // capacity (rows)
-  int64_t q_offset;     // cache row of query 0 (its global position minus
-                        //   the cache's base; masks use row differences)
-  float sm_scale;
-};
-struct RopeTab {         // YaRN tables for rotating Q inside the prefill kernel
-  int64_t pos_base;     // global position of cache row 0 (q_offset is a row)
-  double conc;
-  double inv_freq[SA_MAX_HALF];
-};
-// rope == nullptr: q is already rotated; otherwise q holds unrotated rows and
-// the kernel rotates them at their positions first (yarn_rope's arithmetic).
-hipError_t launch_prefill_bf16(const AttnArgs& a, const RopeTab* rope, hipStream_t s);
-hipError_t launch_attn_rows_f32(const AttnArgs& a, hipStream_t s);
 
 struct DecodeArgs {
   AttnArgs at;          // T_q == 1, q_offset == cache offset - 1

@@ -682,6 +682,8 @@ static int moe_check(int N, int d_model, int E, int k) {
   if (d_model % 64) return fail(SA_ERR_SHAPE, "d_model must be a multiple of 64, got %d", d_model);
   if ((int64_t)N * d_model > UINT32_MAX || (int64_t)N * k > INT32_MAX)
     return fail(SA_ERR_ARG, "N too large");
+  if (((int64_t)N + 255) / 256 * E * 4 > 65536)     // per-block counts staged in LDS
+    return fail(SA_ERR_ARG, "N * E too large for the dispatch scan (N/256 * E <= 16384)");
   return SA_OK;
 }
 }  // namespace
@@ -726,6 +728,8 @@ int moe_dispatch(const int32_t* expert_ids, int N, int E, int k, int32_t* rows,
   if (N <= 0) return fail(SA_ERR_ARG, "non-positive size");
   if (E < 1 || E > 64 || k < 1 || k > 8 || k > E) return fail(SA_ERR_SHAPE, "need 1 <= k <= min(8, E), E <= 64");
   if ((int64_t)N * k > INT32_MAX) return fail(SA_ERR_ARG, "N too large");
+  if (((int64_t)N + 255) / 256 * E * 4 > 65536)
+    return fail(SA_ERR_ARG, "N * E too large for the dispatch scan (N/256 * E <= 16384)");
   const size_t need = moe_dispatch_workspace_bytes(N, E);
   if (ws_bytes < need) return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   const size_t nblk = ((size_t)N + 255) / 256;
@@ -794,13 +798,13 @@ int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, in
   if (e == hipSuccess) e = launch_moe_dispatch(a, s);
   if (e == hipSuccess) {
     MoeGroup g{w13, w2, w + L.h, ffn, 0};
-    e = launch_moe_experts(a, g, s);
+    e = launch_moe_experts(a, g, false, s);
   }
-  if (e == hipSuccess && shared) {
+  if (e == hipSuccess && shared) {      // the shared expert's down pass also combines
     MoeGroup g{w13_shared, w2_shared, w + L.hs, ffn_shared, 1};
-    e = launch_moe_experts(a, g, s);
+    e = launch_moe_experts(a, g, true, s);
   }
-  if (e == hipSuccess) e = launch_moe_combine(a, shared ? k + 1 : k, s);
+  if (e == hipSuccess && !shared) e = launch_moe_combine(a, k, s);
   if (e != hipSuccess) return hip_fail(e, "moe launch");
   return ok();
 }
