@@ -19,11 +19,13 @@ Modules
              logits, dispatch by expert, SwiGLU experts, weighted combine
   ring       sliding-window ring cache of band layers (W rows, slot p mod W),
              its band mask in ring coordinates, KV entry counts
+  sampling   logit bias and penalties, temperature, top-k / top-p / min-p,
+             greedy decode and the draw from a given uniform
 
 Sources are cited as page title + section.  The pages:
   "MoE-Xtend" README (sections DESIGN CONTRACTS, ARCHITECTURE,
       TOKEN STREAM (DECODE), ATTENTION STACK, ROPE + SCALING, KV CACHE,
-      NOTATION)
+      NOTATION, SAMPLING CONTROLS)
   "GQA Attention" study note on gpt-oss (section "How it works")
   "MoE-Xtend" project summary page
   "GPT-OSS-Lite" README (shapes; the KV-cache reduction figures) and visual
