@@ -369,6 +369,67 @@ int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, in
               const void* w2_shared, int ffn_shared, void* y, void* workspace,
               size_t ws_bytes, void* stream);
 
+/* ---- Sampling controls: from a row of logits to the next token ----
+ * "MoE-Xtend" README, SAMPLING CONTROLS: p = softmax(z / T); top-k keeps
+ * the k most probable tokens, top-p the smallest set whose cumulative
+ * probability reaches p, min-p drops the tokens less probable than a
+ * fraction of the most probable one; logit bias, then repetition, presence
+ * and frequency penalties, then the truncations, then the draw; T = 0 is
+ * greedy.  The project summary page: sampling is deterministic.
+ * Per row, as the library computes it:
+ *   z' = z + bias; a token seen c > 0 times gets z' / r (z' > 0) or z' * r
+ *   (otherwise), then z' - presence, then z' - frequency * c, each step one
+ *   fp32 operation;
+ *   T = 0: the largest z', ties to the lower id;
+ *   T > 0: relative weights e = exp((z' - max z') / T) (fp32) and integer
+ *   masses q = floor(e * 2^40), summed exactly, so the result is
+ *   deterministic; every truncation is a threshold on z' and never splits
+ *   equal logits: top-k keeps z' >= the k-th largest z', top-p (on the
+ *   top-k set) keeps z' >= the logit at which the mass summed in decreasing
+ *   z' first reaches ceil(top_p * top-k mass), min-p keeps e >= min_p;
+ *   the draw takes the first kept token, in increasing id, whose
+ *   cumulative mass exceeds floor(u * kept mass). */
+typedef struct {
+  float temperature;  /* >= 0; 0: greedy                                    */
+  int32_t top_k;      /* >= 0; 0 or >= V: off                               */
+  float top_p;        /* (0, 1]; 1: off                                     */
+  float min_p;        /* [0, 1]; 0: off                                     */
+  float repetition;   /* > 0; 1: off                                        */
+  float presence;     /* finite; 0: off                                     */
+  float frequency;    /* finite; 0: off                                     */
+  int32_t reserved;   /* set to 0                                           */
+} sa_sample_params;
+
+/* Add each id of ids (device int32 [B, H], row stride ids_stride >= H) into
+ * counts (device int32 [B, V]): counts[b, id] += 1 for 0 <= id < V; other
+ * ids are skipped.  Integer atomics: the result does not depend on order. */
+int sample_count_tokens(const int32_t* ids, int B, int H, int64_t ids_stride, int32_t* counts,
+                        int V, void* stream);
+
+/* Bytes of workspace sample_tokens needs for B rows of V logits (0 on
+ * invalid sizes). */
+size_t sample_workspace_bytes(int B, int V);
+
+/* One token per row.  logits: device fp32 [B, V], row stride
+ * logits_stride >= V; bias: device fp32, row b at bias + b * bias_stride
+ * (bias_stride 0: one row for the batch; V or more otherwise), or null;
+ * counts: device int32 [B, V] occurrence counts for the penalties, or null
+ * (penalties off); params: device [B]; u: device fp32 [B], one uniform in
+ * [0, 1) per row (unused by greedy rows).  Outputs: tokens device int32
+ * [B]; n_kept device int32 [B] (the size of the kept set; 1 for greedy
+ * rows), or null; processed device fp32 [B, V] (z' before temperature), or
+ * null.  With update_counts != 0 (counts non-null) counts[b, token] += 1
+ * after the draw, so a decode loop's counts stay on the device.
+ * 1 <= V <= 262144, 1 <= B <= 65535 (SA_ERR_SHAPE otherwise).  A row with
+ * invalid parameters (out of the ranges above, or u outside [0, 1) with
+ * T > 0), or with no finite z' when T > 0 (no z' above -inf when greedy),
+ * gets token -1 and n_kept 0.  All pointers caller-owned; the workspace's
+ * contents are overwritten. */
+int sample_tokens(const float* logits, int B, int V, int64_t logits_stride, const float* bias,
+                  int64_t bias_stride, int32_t* counts, const sa_sample_params* params,
+                  const float* u, int update_counts, int32_t* tokens, int32_t* n_kept,
+                  float* processed, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of fp32 workspace that sinkattn_decode needs for any cache offset up
  * to `capacity` with these shapes (0 on invalid arguments). */
 size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h,

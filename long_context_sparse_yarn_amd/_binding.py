@@ -38,6 +38,12 @@ class SaYarn(ctypes.Structure):
                 ("orig_ctx", _i64), ("ntk_alpha", _f64), ("ntk_beta", _f64)]
 
 
+class SaSampleParams(ctypes.Structure):
+    _fields_ = [("temperature", _f32), ("top_k", ctypes.c_int32), ("top_p", _f32), ("min_p", _f32),
+                ("repetition", _f32), ("presence", _f32), ("frequency", _f32),
+                ("reserved", ctypes.c_int32)]
+
+
 class SaSnapshot(ctypes.Structure):
     _fields_ = [("offset", _i64), ("cache_id", _u64), ("stamp", _u64)]
 
@@ -88,6 +94,10 @@ _moe_dispatch = _sig("moe_dispatch", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
 _moe_ws = _sig("moe_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _moe_layer = _sig("moe_layer", _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp,
                   _i32, _vp, _vp, _sz, _vp)
+_sample_count_tokens = _sig("sample_count_tokens", _i32, _vp, _i32, _i32, _i64, _vp, _i32, _vp)
+_sample_ws = _sig("sample_workspace_bytes", _sz, _i32, _i32)
+_sample_tokens = _sig("sample_tokens", _i32, _vp, _i32, _i32, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                      _vp, _vp, _vp, _sz, _vp)
 _sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
 _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                         _i32, _f32, _vp, _sz, _vp)
@@ -519,3 +529,69 @@ def sinkattn_decode(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window
                             _dev(workspace, "workspace"), workspace.numel() * 4,
                             _stream(stream)))
     return out
+
+
+def sample_params(B: int, temperature=1.0, top_k=0, top_p=1.0, min_p=0.0, repetition=1.0,
+                  presence=0.0, frequency=0.0, device="cuda") -> torch.Tensor:
+    """Per-row sampling parameters (each a scalar or a sequence of B values)
+    packed as B sa_sample_params structs in a device uint8 tensor."""
+    arr = (SaSampleParams * B)()
+    cols = dict(temperature=temperature, top_k=top_k, top_p=top_p, min_p=min_p,
+                repetition=repetition, presence=presence, frequency=frequency)
+    for name, val in cols.items():
+        vals = list(val) if hasattr(val, "__len__") else [val] * B
+        if len(vals) != B:
+            raise ValueError("%s: %d values for %d rows" % (name, len(vals), B))
+        for i, x in enumerate(vals):
+            setattr(arr[i], name, int(x) if name == "top_k" else float(x))
+    raw = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return raw.to(device)
+
+
+def sample_workspace_bytes(B: int, V: int) -> int:
+    return int(_sample_ws(B, V))
+
+
+def sample_count_tokens(ids: torch.Tensor, counts: torch.Tensor, stream=None) -> torch.Tensor:
+    """counts[b, id] += 1 for every id of ids [B, H] (int32) in [0, V);
+    counts: int32 [B, V], updated in place."""
+    B, H = ids.shape
+    V = counts.shape[1]
+    _check(_sample_count_tokens(_dev(ids, "ids") if H else None, B, H, H, _dev(counts, "counts"), V,
+                                _stream(stream)))
+    return counts
+
+
+def sample_tokens(logits: torch.Tensor, params: torch.Tensor, u: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+                  update_counts: bool = False, want_kept: bool = False, want_processed: bool = False,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """sample_tokens: logits fp32 [B, V]; params from sample_params; u fp32 [B];
+    bias fp32 [V] (shared) or [B, V], or None; counts int32 [B, V] or None.
+    Returns tokens int32 [B], plus n_kept int32 [B] and / or the processed
+    logits fp32 [B, V] when asked for."""
+    B, V = logits.shape
+    if bias is not None:
+        bias_stride = 0 if bias.dim() == 1 else bias.shape[1]
+        pb = _dev(bias, "bias")
+    else:
+        bias_stride, pb = 0, None
+    tokens = torch.empty(B, dtype=torch.int32, device=logits.device)
+    kept = torch.empty(B, dtype=torch.int32, device=logits.device) if want_kept else None
+    proc = torch.empty((B, V), dtype=torch.float32, device=logits.device) if want_processed else None
+    need = sample_workspace_bytes(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _check(_sample_tokens(_dev(logits, "logits"), B, V, V, pb, bias_stride,
+                          _dev(counts, "counts") if counts is not None else None,
+                          _dev(params, "params"), _dev(u, "u"), 1 if update_counts else 0,
+                          _dev(tokens, "tokens"), _dev(kept, "n_kept") if kept is not None else None,
+                          _dev(proc, "processed") if proc is not None else None,
+                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(stream)))
+    out = [tokens]
+    if want_kept:
+        out.append(kept)
+    if want_processed:
+        out.append(proc)
+    return tokens if len(out) == 1 else tuple(out)

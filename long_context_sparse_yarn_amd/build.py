@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsinkattn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["sinkattn_abi.hip", "rope.hip", "append.hip", "prefill.hip", "decode.hip", "qkv.hip", "moe.hip",
-           "attn_f32.hip"]
+           "attn_f32.hip", "sample.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -1,0 +1,39 @@
+// Launch arguments of the sampling kernels (sample.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sinkattn.h"
+
+constexpr int kSampleChunk = 4096;      // vocabulary entries per prep / histogram workgroup
+constexpr int kSampleBuckets = 4096;    // first-level histogram: the top 12 bits of the key
+constexpr int kSampleMaxV = 64 * 4096;  // the draw keeps one mass per 64 ids in LDS
+constexpr int kSampleCap = 4096;        // candidates sorted in LDS
+
+struct SampleArgs {
+  const float* logits;
+  int64_t logits_stride;
+  const float* bias;                    // null: no bias
+  int64_t bias_stride;                  // 0: one row shared by the batch
+  int32_t* counts;                      // [B, V] or null
+  const sa_sample_params* params;       // [B]
+  const float* u;                       // [B]
+  int32_t* tokens;                      // [B]
+  int32_t* n_kept;                      // [B] or null
+  float* processed;                     // [B, V] or null
+  // workspace
+  float* zp;                            // [B, V] processed logits
+  float* chunk_max;                     // [B, C]
+  int32_t* chunk_arg;                   // [B, C]
+  uint32_t* hist_count;                 // [B, kSampleBuckets]
+  unsigned long long* hist_mass;        // [B, kSampleBuckets]
+  unsigned long long* cand;             // [B, kSampleCap] tokens at or above the min-p key
+  uint32_t* ncand;                      // [B]
+  int B, V, C;
+  int update_counts;
+};
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+hipError_t launch_sample_count(const int32_t* ids, int B, int H, int64_t ids_stride, int32_t* counts,
+                               int V, hipStream_t s);

@@ -1,0 +1,712 @@
+// Sampling controls on gfx950: processed logits, top-k / top-p / min-p and
+// the draw.
+//
+// "MoE-Xtend" README, SAMPLING CONTROLS: p = softmax(z / T); top-k, top-p
+// and min-p truncations after logit bias and the repetition, presence and
+// frequency penalties; T = 0 is greedy.  The project summary page: sampling
+// is deterministic.
+//
+// Every truncation is a threshold on an order-preserving 32-bit key of the
+// processed logit z': top-k the largest key whose count at or above it
+// reaches k, top-p the largest key whose mass at or above it reaches
+// ceil(top_p * top-k mass), min-p the smallest key whose weight reaches
+// min_p (weights are monotone in the key: bisection).  Masses are integers,
+// q = floor(e * 2^40) with e = 2^((z' - m) log2(e) / T) <= 1, so every sum
+// is exact and the result does not depend on scheduling.
+//
+// Three launches per call:
+//  1. prep (grid chunks x rows, the whole chip): z' stored once, per-chunk
+//     maximum and its lowest id; clears the row's histogram and candidate
+//     counter.  The only pass over the inputs in HBM.
+//  2. histogram (chunks x rows): a 4096-bucket histogram (counts, masses) of
+//     the key's top 12 bits in LDS, added into the row's global one with
+//     integer atomics; when min-p is on, the tokens at or above the min-p key
+//     are also gathered into a per-row candidate list.
+//  3. select (one 1024-thread workgroup per row): greedy rows take the
+//     merged argmax.  Otherwise the kept set is finished in LDS when it lies
+//     in a small ranking prefix: the min-p candidates of launch 2, or the
+//     tokens above a bound read off the histogram, gathered in one pass; the
+//     candidates are sorted (bitonic, key then id), the thresholds read off
+//     their prefix masses, and the kept ones re-sorted by id for the draw.
+//     Otherwise two more radix levels (12 + 8 bits, one pass each over z' in
+//     L2) give each threshold, and the draw sums the kept mass of every run
+//     of 64 ids, scans those sums, and scans the one run holding the target.
+#pragma clang fp contract(off)
+
+#include "sa_device.h"
+#include "sa_sample.h"
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+constexpr int kPer = kSampleChunk / kPrepThreads;   // 16 entries per thread
+constexpr int kNB = kSampleBuckets;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelPer = 16;                         // loads in flight per thread in a select pass
+constexpr int kCap = kSampleCap;
+constexpr float kFltMax = 3.4028235e38f;
+typedef unsigned long long u64;
+
+// Order-preserving key: a larger float gets a larger key; -0 and +0 share one.
+__device__ __forceinline__ uint32_t fkey(float z) {
+  const uint32_t u = __float_as_uint(z + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fval(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ float temp_coef(float T) { return SA_LOG2E / T; }
+// exp((z - m) / T) as 2^((z - m) c), c = log2(e) / T; exactly 1 at the maximum
+__device__ __forceinline__ float rel_weight(float z, float m, float c) {
+  const float d = z - m;
+  return fast_exp2(d == 0.f ? 0.f : d * c);
+}
+__device__ __forceinline__ u64 fixed_mass(float e) { return (u64)(e * 1099511627776.0f); }  // 2^40
+__device__ __forceinline__ u64 mass_of_key(uint32_t k, float m, float c) {
+  return fixed_mass(rel_weight(fval(k), m, c));
+}
+
+// The smallest key whose weight reaches min_p (0 < min_p <= 1): the
+// maximum's weight is 1 and -inf's is 0, so bisection between them.
+__device__ __forceinline__ uint32_t minp_key(float m, float c, float min_p) {
+  uint32_t lo = fkey(-INFINITY), hi = fkey(m);
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    if (rel_weight(fval(mid), m, c) >= min_p) hi = mid; else lo = mid;
+  }
+  return hi;
+}
+
+__device__ __forceinline__ bool params_ok(const sa_sample_params& p, float u) {
+  const bool base = p.temperature >= 0.f && p.temperature <= kFltMax && p.top_k >= 0 && p.top_p > 0.f &&
+                    p.top_p <= 1.f && p.min_p >= 0.f && p.min_p <= 1.f && p.repetition > 0.f &&
+                    p.repetition <= kFltMax && fabsf(p.presence) <= kFltMax && fabsf(p.frequency) <= kFltMax;
+  return base && (p.temperature == 0.f || (u >= 0.f && u < 1.f));
+}
+
+// (v, a) beats (bv, ba): larger value, or equal value and lower id; -1 is no entry
+__device__ __forceinline__ bool better(float v, int a, float bv, int ba) {
+  return a >= 0 && (ba < 0 || v > bv || (v == bv && a < ba));
+}
+
+__device__ __forceinline__ u64 wave_sum_u64(u64 x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Row maximum and its lowest id from the per-chunk results (every thread).
+__device__ __forceinline__ void row_max(const SampleArgs& a, int b, float* m, int* arg) {
+  float bv = 0.f;
+  int ba = -1;
+  for (int c = 0; c < a.C; ++c) {
+    const float v = a.chunk_max[(int64_t)b * a.C + c];
+    const int i = a.chunk_arg[(int64_t)b * a.C + c];
+    if (better(v, i, bv, ba)) {
+      bv = v;
+      ba = i;
+    }
+  }
+  *m = ba >= 0 ? bv : -INFINITY;
+  *arg = ba;
+}
+
+// ------------------------------------------------------------------ prep
+__global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a) {
+  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const sa_sample_params P = a.params[b];
+  const bool pen = a.counts && (P.repetition != 1.f || P.presence != 0.f || P.frequency != 0.f);
+  const float* L = a.logits + (int64_t)b * a.logits_stride;
+  const float* Bi = a.bias ? a.bias + (int64_t)b * a.bias_stride : nullptr;
+  const int32_t* Cn = pen ? a.counts + (int64_t)b * a.V : nullptr;
+  const int v0 = c * kSampleChunk + tid;
+  float z[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    z[j] = v < a.V ? L[v] : 0.f;
+  }
+  if (Bi) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int v = v0 + j * kPrepThreads;
+      if (v < a.V) z[j] = z[j] + Bi[v];
+    }
+  }
+  if (pen) {
+    int n[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int v = v0 + j * kPrepThreads;
+      n[j] = v < a.V ? Cn[v] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (n[j] > 0) {
+        float t = z[j] > 0.f ? z[j] / P.repetition : z[j] * P.repetition;
+        t = t - P.presence;
+        z[j] = t - P.frequency * (float)n[j];
+      }
+    }
+  }
+  float* Z = a.zp + (int64_t)b * a.V;
+  float* O = a.processed ? a.processed + (int64_t)b * a.V : nullptr;
+  float best = 0.f;
+  int arg = -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    if (v < a.V) {
+      Z[v] = z[j];
+      if (O) O[v] = z[j];
+      if (z[j] > -INFINITY && (arg < 0 || z[j] > best)) {   // NaN never wins
+        best = z[j];
+        arg = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(best, m, 64);
+    const int oa = __shfl_xor(arg, m, 64);
+    if (better(ov, oa, best, arg)) {
+      best = ov;
+      arg = oa;
+    }
+  }
+  __shared__ float wv[kPrepThreads / 64];
+  __shared__ int wa[kPrepThreads / 64];
+  if ((tid & 63) == 0) {
+    wv[tid >> 6] = best;
+    wa[tid >> 6] = arg;
+  }
+  // clear this chunk's share of the row's histogram (filled by the next launch)
+  const int share = (kNB + a.C - 1) / a.C;
+  for (int i = c * share + tid; i < min(kNB, (c + 1) * share); i += kPrepThreads) {
+    a.hist_count[(int64_t)b * kNB + i] = 0u;
+    a.hist_mass[(int64_t)b * kNB + i] = 0ull;
+  }
+  if (c == 0 && tid == 0) a.ncand[b] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    float bv = wv[0];
+    int ba = wa[0];
+    for (int w = 1; w < kPrepThreads / 64; ++w)
+      if (better(wv[w], wa[w], bv, ba)) {
+        bv = wv[w];
+        ba = wa[w];
+      }
+    a.chunk_max[(int64_t)b * a.C + c] = ba >= 0 ? bv : -INFINITY;
+    a.chunk_arg[(int64_t)b * a.C + c] = ba;
+  }
+}
+
+// ------------------------------------------------------------- histogram
+__global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a) {
+  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const sa_sample_params P = a.params[b];
+  if (!params_ok(P, a.u[b]) || P.temperature == 0.f) return;
+  float m;
+  int arg;
+  row_max(a, b, &m, &arg);
+  if (!(fabsf(m) <= kFltMax)) return;               // no finite maximum: the row has no token
+  const float cT = temp_coef(P.temperature);
+  const bool gather = P.min_p > 0.f;
+  const uint32_t km = gather ? minp_key(m, cT, P.min_p) : 0u;
+  __shared__ uint32_t hc[kNB];
+  __shared__ u64 hm[kNB];
+  for (int i = tid; i < kNB; i += kPrepThreads) {
+    hc[i] = 0u;
+    hm[i] = 0ull;
+  }
+  __syncthreads();
+  const float* Z = a.zp + (int64_t)b * a.V;
+  const int v0 = c * kSampleChunk + tid;
+  float z[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    z[j] = v < a.V ? Z[v] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    const uint32_t k = fkey(z[j]);
+    if (v < a.V) {
+      atomicAdd(&hc[k >> 20], 1u);
+      const u64 q = fixed_mass(rel_weight(z[j], m, cT));
+      if (q) atomicAdd(&hm[k >> 20], q);
+    }
+    if (gather) {
+      const bool take = v < a.V && k >= km;
+      const u64 mask = __ballot(take);
+      if (mask) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
+        base = __shfl(base, 0, 64);
+        const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        if (take && slot < (uint32_t)kCap)
+          a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kNB; i += kPrepThreads) {
+    if (hc[i]) atomicAdd(&a.hist_count[(int64_t)b * kNB + i], hc[i]);
+    if (hm[i]) atomicAdd(&a.hist_mass[(int64_t)b * kNB + i], hm[i]);
+  }
+}
+
+// ---------------------------------------------------------------- select
+struct SelShared {
+  uint32_t c1[kNB];                       // first-level histogram (from the global one)
+  u64 m1[kNB];
+  union {
+    struct {
+      uint32_t c[kNB];
+      u64 m[kNB];
+    } h;                                  // deeper radix levels
+    struct {
+      u64 key[kCap];
+      u64 cum[kCap];
+    } cand;                               // candidates
+    u64 grp[kSampleMaxV / 64];            // kept mass per run of 64 ids
+  } u;
+  u64 wtot[3][kSelWaves];
+  uint32_t digit;
+  u64 add_cnt, add_mass;
+  uint32_t ncand;
+  int idx;
+  u64 val;
+};
+
+// Exclusive prefix sums over the workgroup's threads of three values, and totals.
+__device__ void block_scan3(SelShared& S, const u64 (&x)[3], u64 (&excl)[3], u64 (&tot)[3]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u64 inc[3] = {x[0], x[1], x[2]};
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u64 y = __shfl_up(inc[i], d, 64);
+      if (lane >= d) inc[i] += y;
+    }
+  }
+  if (lane == 63)
+    for (int i = 0; i < 3; ++i) S.wtot[i][w] = inc[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    u64 base = 0, t = 0;
+    for (int k = 0; k < kSelWaves; ++k) {
+      const u64 v = S.wtot[i][k];
+      if (k < w) base += v;
+      t += v;
+    }
+    excl[i] = base + inc[i] - x[i];
+    tot[i] = t;
+  }
+  __syncthreads();
+}
+
+// f(v, z, valid) over the row, kSelPer loads in flight per thread; every
+// lane of every wave calls f the same number of times (ballots allowed).
+// Thread t sees v = v0 + j * 1024 + t: lanes of a wave hold 64 consecutive ids.
+template <class F>
+__device__ __forceinline__ void row_pass(const float* Z, int V, F f) {
+  for (int v0 = 0; v0 < V; v0 += kSelPer * kSelThreads) {
+    float z[kSelPer];
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int v = v0 + j * kSelThreads + (int)threadIdx.x;
+      z[j] = v < V ? Z[v] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int v = v0 + j * kSelThreads + (int)threadIdx.x;
+      f(v, z[j], v < V);
+    }
+  }
+}
+
+// Scanning buckets from the top digit down: the digit at which above_w plus
+// the weight (count or mass) of the buckets at and above it first reaches
+// target.  S.digit gets it; S.add_cnt / S.add_mass the counts and masses of
+// the buckets above it.  The caller guarantees that the target is reached.
+__device__ void pick_digit(SelShared& S, const uint32_t* cnt, const u64* mass, int NB, bool by_mass,
+                           u64 target, u64 above_w) {
+  const int t = threadIdx.x;
+  u64 cw[4], cc[4], cm[4];
+  u64 x[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = 4 * t + i;
+    cc[i] = pos < NB ? cnt[NB - 1 - pos] : 0;
+    cm[i] = pos < NB ? mass[NB - 1 - pos] : 0;
+    cw[i] = by_mass ? cm[i] : cc[i];
+    x[0] += cw[i];
+    x[1] += cc[i];
+    x[2] += cm[i];
+  }
+  u64 ex[3], tot[3];
+  if (t == 0) S.digit = 0;
+  block_scan3(S, x, ex, tot);
+  u64 run = above_w + ex[0], rc = ex[1], rm = ex[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (run < target && run + cw[i] >= target) {
+      S.digit = (uint32_t)(NB - 1 - (4 * t + i));
+      S.add_cnt = rc;
+      S.add_mass = rm;
+    }
+    run += cw[i];
+    rc += cc[i];
+    rm += cm[i];
+  }
+  __syncthreads();
+}
+
+// One pass over z': histogram of (key >> digit_shift) & digit_mask over the
+// keys with key >> prefix_shift == prefix.
+__device__ void level_pass(SelShared& S, const float* Z, int V, float m, float cT, uint32_t prefix,
+                           int prefix_shift, int digit_shift, uint32_t digit_mask) {
+  for (int i = threadIdx.x; i < kNB; i += kSelThreads) {
+    S.u.h.c[i] = 0u;
+    S.u.h.m[i] = 0ull;
+  }
+  __syncthreads();
+  row_pass(Z, V, [&](int v, float z, bool valid) {
+    const uint32_t k = fkey(z);
+    if (valid && (k >> prefix_shift) == prefix) {
+      const uint32_t d = (k >> digit_shift) & digit_mask;
+      atomicAdd(&S.u.h.c[d], 1u);
+      const u64 q = fixed_mass(rel_weight(z, m, cT));
+      if (q) atomicAdd(&S.u.h.m[d], q);
+    }
+  });
+  __syncthreads();
+}
+
+// The largest key K whose tokens at or above it have count (by_mass: mass)
+// >= target (target <= the row's total), with the mass at or above K.
+// Level 1 from S.c1/m1; levels 2 (12 bits) and 3 (8 bits) by passes over z'.
+__device__ void descend(SelShared& S, const float* Z, int V, float m, float cT, bool by_mass, u64 target,
+                        uint32_t* K, u64* mass_ge) {
+  pick_digit(S, S.c1, S.m1, kNB, by_mass, target, 0);
+  const uint32_t d1 = S.digit;
+  u64 ac = S.add_cnt, am = S.add_mass;
+  __syncthreads();
+  level_pass(S, Z, V, m, cT, d1, 20, 8, 0xFFFu);
+  pick_digit(S, S.u.h.c, S.u.h.m, kNB, by_mass, target, by_mass ? am : ac);
+  const uint32_t d2 = S.digit;
+  ac += S.add_cnt;
+  am += S.add_mass;
+  __syncthreads();
+  level_pass(S, Z, V, m, cT, (d1 << 12) | d2, 8, 0, 0xFFu);
+  pick_digit(S, S.u.h.c, S.u.h.m, 256, by_mass, target, by_mass ? am : ac);
+  const uint32_t d3 = S.digit;
+  am += S.add_mass;
+  *K = (d1 << 20) | (d2 << 8) | d3;
+  *mass_ge = am + S.u.h.m[d3];
+  __syncthreads();
+}
+
+// In-place bitonic sort, descending, of S.u.cand.key[0, n), n a power of two.
+__device__ void sort_desc(SelShared& S, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kSelThreads) {
+        const int p = i ^ j;
+        if (p > i) {
+          const u64 x = S.u.cand.key[i], y = S.u.cand.key[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? x < y : x > y) {
+            S.u.cand.key[i] = y;
+            S.u.cand.key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Pads S.u.cand.key[n, 2^ceil(log2 n)) with 0 (sorts last) and sorts.
+__device__ void pad_sort(SelShared& S, int n) {
+  const int np = pow2_at_least(max(n, 2));
+  for (int i = n + (int)threadIdx.x; i < np; i += kSelThreads) S.u.cand.key[i] = 0ull;
+  __syncthreads();
+  sort_desc(S, np);
+}
+
+// Inclusive prefix over the first n candidates of mass_of(e) into S.u.cand.cum.
+template <class F>
+__device__ void cand_prefix(SelShared& S, int n, F mass_of) {
+  u64 q[4];
+  u64 x[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * (int)threadIdx.x + i;
+    q[i] = e < n ? mass_of(e) : 0;
+    x[0] += q[i];
+  }
+  u64 ex[3], tot[3];
+  block_scan3(S, x, ex, tot);
+  u64 run = ex[0];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * (int)threadIdx.x + i;
+    run += q[i];
+    if (e < n) S.u.cand.cum[e] = run;
+  }
+  __syncthreads();
+}
+
+// The candidates S.u.cand.key[0, n) (key << 32 | ~id) are every token at or
+// above some key, a prefix of the ranking that holds the kept set; a
+// threshold that falls below them is not the binding one.  Returns the
+// token (and the kept count in *kept), or -1.
+__device__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
+                             float m, float cT, u64 q_all, uint32_t Km, int* kept) {
+  pad_sort(S, n);
+  cand_prefix(S, n, [&](int e) { return mass_of_key((uint32_t)(S.u.cand.key[e] >> 32), m, cT); });
+  auto key_at = [&](int e) { return (uint32_t)(S.u.cand.key[e] >> 32); };
+  // the last candidate whose key is >= K, plus one (0: none)
+  auto count_ge = [&](uint32_t K) {
+    if (threadIdx.x == 0) S.idx = 0;
+    __syncthreads();
+    for (int e = (int)threadIdx.x; e < n; e += kSelThreads)
+      if (key_at(e) >= K && (e + 1 == n || key_at(e + 1) < K)) S.idx = e + 1;
+    __syncthreads();
+    const int r = S.idx;
+    __syncthreads();
+    return r;
+  };
+  uint32_t Kk = 0, Kp = 0;
+  u64 qk = q_all;
+  if (kA && n >= P.top_k) {
+    Kk = key_at(P.top_k - 1);
+    qk = S.u.cand.cum[count_ge(Kk) - 1];
+  }
+  if (pA) {
+    const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
+    if (threadIdx.x == 0) S.idx = -1;
+    __syncthreads();
+    for (int e = (int)threadIdx.x; e < n; e += kSelThreads)
+      if (S.u.cand.cum[e] >= tau && (e == 0 || S.u.cand.cum[e - 1] < tau)) S.idx = e;
+    __syncthreads();
+    if (S.idx >= 0) Kp = key_at(S.idx);
+    __syncthreads();
+  }
+  const uint32_t Ks = max(max(Kk, Kp), Km);
+  const int nk = count_ge(Ks);
+  if (nk == 0) return -1;
+  const u64 qn = S.u.cand.cum[nk - 1];
+  u64 t = (u64)((double)u * (double)qn);
+  if (t >= qn) t = qn - 1;
+  __syncthreads();
+  // the kept tokens by increasing id: (~id << 32 | key), descending
+  for (int e = (int)threadIdx.x; e < nk; e += kSelThreads) {
+    const u64 x = S.u.cand.key[e];
+    S.u.cand.key[e] = ((u64)(uint32_t)x << 32) | (x >> 32);
+  }
+  __syncthreads();
+  pad_sort(S, nk);
+  cand_prefix(S, nk, [&](int e) { return mass_of_key((uint32_t)S.u.cand.key[e], m, cT); });
+  if (threadIdx.x == 0) S.idx = nk - 1;
+  __syncthreads();
+  for (int e = (int)threadIdx.x; e < nk; e += kSelThreads)
+    if (S.u.cand.cum[e] > t && (e == 0 || S.u.cand.cum[e - 1] <= t)) S.idx = e;
+  __syncthreads();
+  *kept = nk;
+  return (int)~(uint32_t)(S.u.cand.key[S.idx] >> 32);
+}
+
+__global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a) {
+  __shared__ SelShared S;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const sa_sample_params P = a.params[b];
+  const float u = a.u[b];
+  int token = -1, kept = 0;
+  float m;
+  int arg;
+  row_max(a, b, &m, &arg);
+  const bool ok = params_ok(P, u);
+  const bool greedy = ok && P.temperature == 0.f;
+  if (greedy && arg >= 0) {
+    token = arg;
+    kept = 1;
+  }
+  if (ok && !greedy && fabsf(m) <= kFltMax) {
+    const int V = a.V;
+    const float* Z = a.zp + (int64_t)b * V;
+    const float cT = temp_coef(P.temperature);
+    const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
+    const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;
+    for (int i = tid; i < kNB; i += kSelThreads) {
+      S.c1[i] = a.hist_count[(int64_t)b * kNB + i];
+      S.m1[i] = a.hist_mass[(int64_t)b * kNB + i];
+    }
+    __syncthreads();
+    u64 q_all;
+    {
+      u64 x[3] = {0, 0, 0}, ex[3], tot[3];
+      for (int i = 0; i < 4; ++i) x[0] += S.m1[4 * tid + i];
+      block_scan3(S, x, ex, tot);
+      q_all = tot[0];
+    }
+    const uint32_t gathered = mA ? a.ncand[b] : 0xFFFFFFFFu;
+    if (mA && gathered <= (uint32_t)kCap && !(kA && pA && (int)gathered < P.top_k)) {
+      // ---- the min-p candidates gathered by the histogram launch
+      const int n = (int)gathered;
+      for (int i = tid; i < n; i += kSelThreads) S.u.cand.key[i] = a.cand[(int64_t)b * kCap + i];
+      __syncthreads();
+      token = finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, &kept);
+    } else {
+      // bucket-aligned bound on the kept set's lowest key, from the histogram
+      uint32_t bk = 0, bp = 0;
+      if (kA) {
+        pick_digit(S, S.c1, S.m1, kNB, false, (u64)P.top_k, 0);
+        bk = S.digit;
+        __syncthreads();
+      }
+      if (pA && !kA) {
+        const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)q_all));
+        pick_digit(S, S.c1, S.m1, kNB, true, tau, 0);
+        bp = S.digit;
+        __syncthreads();
+      }
+      // with both top-k and top-p on, the top-k mass needs every token above Kk
+      const uint32_t blb = (kA && pA) ? bk : max(max(bk, bp), Km >> 20);
+      u64 nb;
+      {
+        u64 x[3] = {0, 0, 0}, ex[3], tot[3];
+        for (int i = 0; i < 4; ++i) x[0] += (uint32_t)(4 * tid + i) >= blb ? S.c1[4 * tid + i] : 0u;
+        block_scan3(S, x, ex, tot);
+        nb = tot[0];
+      }
+      if (nb <= (u64)kCap) {
+        // ---- gather the tokens at or above the bound in one pass
+        if (tid == 0) S.ncand = 0;
+        __syncthreads();
+        const uint32_t klb = blb << 20;
+        row_pass(Z, V, [&](int v, float z, bool valid) {
+          const uint32_t k = fkey(z);
+          const bool take = valid && k >= klb;
+          const u64 mask = __ballot(take);
+          if (mask) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&S.ncand, (uint32_t)__popcll(mask));
+            base = __shfl(base, 0, 64);
+            const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+            if (take && slot < (uint32_t)kCap) S.u.cand.key[slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+          }
+        });
+        __syncthreads();
+        const int n = (int)min(S.ncand, (uint32_t)kCap);
+        token = finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, &kept);
+      } else {
+        // ---- large kept set: radix levels over z', then the draw pass
+        uint32_t Kk = 0, Kp = 0;
+        u64 qk = q_all;
+        if (kA) descend(S, Z, V, m, cT, false, (u64)P.top_k, &Kk, &qk);
+        if (pA) {
+          const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
+          u64 unused;
+          descend(S, Z, V, m, cT, true, tau, &Kp, &unused);
+        }
+        const uint32_t Ks = max(max(Kk, Kp), Km);
+        const int ng = (V + 63) / 64;
+        uint32_t nk_part = 0;
+        if (tid == 0) {
+          S.idx = 0;
+          S.val = 0;
+        }
+        row_pass(Z, V, [&](int v, float z, bool valid) {
+          const bool in = valid && fkey(z) >= Ks;
+          nk_part += in ? 1u : 0u;
+          const u64 s = wave_sum_u64(in ? fixed_mass(rel_weight(z, m, cT)) : 0ull);
+          if (lane == 0 && v < 64 * ng) S.u.grp[v >> 6] = s;
+        });
+        __syncthreads();
+        u64 gq[4];
+        u64 x[3] = {0, (u64)nk_part, 0}, ex[3], tot[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = 4 * tid + i;
+          gq[i] = g < ng ? S.u.grp[g] : 0ull;
+          x[0] += gq[i];
+        }
+        block_scan3(S, x, ex, tot);
+        const u64 qn = tot[0];
+        kept = (int)tot[1];
+        u64 t = (u64)((double)u * (double)qn);
+        if (t >= qn) t = qn - 1;
+        u64 run = ex[0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = 4 * tid + i;
+          if (g < ng && run <= t && t < run + gq[i]) {
+            S.idx = g;
+            S.val = run;
+          }
+          run += gq[i];
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const int g = S.idx;
+          const int v = 64 * g + lane;
+          const float z = v < V ? Z[v] : -INFINITY;
+          const bool in = v < V && fkey(z) >= Ks;
+          u64 inc = in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const u64 y = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += y;
+          }
+          const u64 over = __ballot(S.val + inc > t);
+          if (lane == 0) S.idx = over ? 64 * g + (int)(__ffsll((long long)over) - 1) : -1;
+        }
+        __syncthreads();
+        token = S.idx;
+      }
+    }
+  }
+  if (tid == 0) {
+    a.tokens[b] = token;
+    if (a.n_kept) a.n_kept[b] = token >= 0 ? kept : 0;
+    if (a.update_counts && a.counts && token >= 0) a.counts[(int64_t)b * a.V + token] += 1;
+  }
+}
+
+__global__ __launch_bounds__(256) void sample_count_kernel(const int32_t* ids, int H, int64_t stride,
+                                                           int32_t* counts, int V) {
+  const int b = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= H) return;
+  const int id = ids[(int64_t)b * stride + j];
+  if (id >= 0 && id < V) atomicAdd(&counts[(int64_t)b * V + id], 1);
+}
+
+}  // namespace
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+  const dim3 grid(a.C, a.B);
+  hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_hist_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_select_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_count(const int32_t* ids, int B, int H, int64_t ids_stride, int32_t* counts,
+                               int V, hipStream_t s) {
+  hipLaunchKernelGGL(sample_count_kernel, dim3((H + 255) / 256, B), dim3(256), 0, s, ids, H, ids_stride,
+                     counts, V);
+  return hipGetLastError();
+}

@@ -15,6 +15,7 @@
 
 #include "../../include/sinkattn.h"
 #include "sa_kernels.h"
+#include "sa_sample.h"
 
 namespace {
 
@@ -806,6 +807,91 @@ int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, in
   }
   if (e == hipSuccess && !shared) e = launch_moe_combine(a, k, s);
   if (e != hipSuccess) return hip_fail(e, "moe launch");
+  return ok();
+}
+
+namespace {
+struct SampleLayout {
+  size_t zp, cmax, carg, hcount, hmass, cand, ncand, total;
+};
+SampleLayout sample_layout(int B, int V) {
+  const size_t C = ((size_t)V + kSampleChunk - 1) / kSampleChunk;
+  SampleLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.zp = take((size_t)B * V * 4);
+  L.cmax = take((size_t)B * C * 4);
+  L.carg = take((size_t)B * C * 4);
+  L.hcount = take((size_t)B * kSampleBuckets * 4);
+  L.hmass = take((size_t)B * kSampleBuckets * 8);
+  L.cand = take((size_t)B * kSampleCap * 8);
+  L.ncand = take((size_t)B * 4);
+  L.total = o;
+  return L;
+}
+int sample_shape(int B, int V) {
+  if (B < 1 || B > 65535) return fail(SA_ERR_SHAPE, "B must be in [1, 65535], got %d", B);
+  if (V < 1 || V > kSampleMaxV) return fail(SA_ERR_SHAPE, "V must be in [1, %d], got %d", kSampleMaxV, V);
+  return SA_OK;
+}
+}  // namespace
+
+int sample_count_tokens(const int32_t* ids, int B, int H, int64_t ids_stride, int32_t* counts, int V,
+                        void* stream) {
+  if (!counts || (H > 0 && !ids)) return fail(SA_ERR_ARG, "null argument");
+  int st = sample_shape(B, V);
+  if (st != SA_OK) return st;
+  if (H < 0 || ids_stride < H) return fail(SA_ERR_ARG, "need H >= 0 and ids_stride >= H");
+  if (H == 0) return ok();
+  hipError_t e = launch_sample_count(ids, B, H, ids_stride, counts, V, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "count launch");
+  return ok();
+}
+
+size_t sample_workspace_bytes(int B, int V) {
+  if (B < 1 || B > 65535 || V < 1 || V > kSampleMaxV) return 0;
+  return sample_layout(B, V).total;
+}
+
+int sample_tokens(const float* logits, int B, int V, int64_t logits_stride, const float* bias,
+                  int64_t bias_stride, int32_t* counts, const sa_sample_params* params, const float* u,
+                  int update_counts, int32_t* tokens, int32_t* n_kept, float* processed, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  if (!logits || !params || !u || !tokens || !workspace) return fail(SA_ERR_ARG, "null argument");
+  int st = sample_shape(B, V);
+  if (st != SA_OK) return st;
+  if (logits_stride < V) return fail(SA_ERR_ARG, "logits_stride must be >= V");
+  if (bias && bias_stride != 0 && bias_stride < V) return fail(SA_ERR_ARG, "bias_stride must be 0 or >= V");
+  if (update_counts && !counts) return fail(SA_ERR_ARG, "update_counts needs counts");
+  if (misaligned(workspace)) return fail(SA_ERR_ARG, "workspace must be 16-byte aligned");
+  const SampleLayout L = sample_layout(B, V);
+  if (ws_bytes < L.total) return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+  char* w = static_cast<char*>(workspace);
+  SampleArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = logits;
+  a.logits_stride = logits_stride;
+  a.bias = bias;
+  a.bias_stride = bias ? bias_stride : 0;
+  a.counts = counts;
+  a.params = params;
+  a.u = u;
+  a.tokens = tokens;
+  a.n_kept = n_kept;
+  a.processed = processed;
+  a.zp = reinterpret_cast<float*>(w + L.zp);
+  a.chunk_max = reinterpret_cast<float*>(w + L.cmax);
+  a.chunk_arg = reinterpret_cast<int32_t*>(w + L.carg);
+  a.hist_count = reinterpret_cast<uint32_t*>(w + L.hcount);
+  a.hist_mass = reinterpret_cast<unsigned long long*>(w + L.hmass);
+  a.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
+  a.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
+  a.B = B;
+  a.V = V;
+  a.C = (V + kSampleChunk - 1) / kSampleChunk;
+  a.update_counts = update_counts ? 1 : 0;
+  hipError_t e = launch_sample(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sample launch");
   return ok();
 }
 

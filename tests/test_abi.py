@@ -312,3 +312,37 @@ def test_moe_errors_before_any_launch():
     assert L(x, 100, 64, w, 8, 2, w, w, 128, w, w, 0, y, ws, 1 << 30, None) == SA_ERR_ARG       # weights, no ffn
     assert L(x, 100, 64, w, 8, 2, w, w, 128, None, None, 0, ctypes.c_void_p(0x50004), ws, nb,
              None) == SA_ERR_ARG
+
+
+def test_sample_errors_before_any_launch():
+    lg, pr, u, tok, ws = (ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000),
+                          ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000))
+    cnt = ctypes.c_void_p(0x80000)
+    assert ctypes.sizeof(B.SaSampleParams) == 32
+    need = B._sample_ws(8, 128000)
+    assert need >= 8 * 128000 * 4 and B._sample_ws(8, 262145) == 0 and B._sample_ws(0, 10) == 0
+    S = B._sample_tokens
+
+    def call(B_=8, V=128000, ls=128000, bias=None, bs=0, counts=None, upd=0, ws_=ws, nb=need, **kw):
+        return S(kw.get("logits", lg), B_, V, ls, bias, bs, counts, kw.get("params", pr), kw.get("u", u),
+                 upd, kw.get("tokens", tok), None, None, ws_, nb, None)
+
+    assert call(V=0) == SA_ERR_SHAPE
+    assert call(V=262145, ls=262145) == SA_ERR_SHAPE
+    assert call(B_=0) == SA_ERR_SHAPE
+    assert call(B_=65536) == SA_ERR_SHAPE
+    assert call(ls=127999) == SA_ERR_ARG                     # row stride below V
+    assert call(bias=lg, bs=5) == SA_ERR_ARG                 # bias stride neither 0 nor >= V
+    assert call(upd=1) == SA_ERR_ARG                         # update without counts
+    assert call(nb=need - 1) == SA_ERR_ARG
+    assert call(ws_=ctypes.c_void_p(0x70008)) == SA_ERR_ARG  # misaligned workspace
+    assert call(logits=None) == SA_ERR_ARG
+    assert call(params=None) == SA_ERR_ARG
+    assert call(u=None) == SA_ERR_ARG
+    assert call(tokens=None) == SA_ERR_ARG
+    C = B._sample_count_tokens
+    assert C(lg, 8, 10, 9, cnt, 100, None) == SA_ERR_ARG     # stride below H
+    assert C(lg, 8, -1, 9, cnt, 100, None) == SA_ERR_ARG
+    assert C(lg, 8, 10, 10, None, 100, None) == SA_ERR_ARG
+    assert C(lg, 8, 10, 10, cnt, 0, None) == SA_ERR_SHAPE
+    assert C(None, 8, 0, 0, cnt, 100, None) == SA_OK         # nothing to count: no launch

@@ -186,3 +186,25 @@ def decode_token(w: Workload, layer: int, step: int,
         "k": normal((w.B, 1, w.n_kv, w.d_h), w.dtype, s, w.cfg_idx, layer, base + 1),
         "v": normal((w.B, 1, w.n_kv, w.d_h), w.dtype, s, w.cfg_idx, layer, base + 2),
     }
+
+
+# ---------------------------------------------------------------- sampling
+# Rows of fp32 logits over the GPT-OSS-Lite vocabulary (128,000 tokens,
+# GPT-OSS-Lite README model diagram) at the long-context decode batch (8).
+SAMPLE_B, SAMPLE_V = 8, 128000
+T_SAMPLE_LOGITS, T_SAMPLE_HISTORY, T_SAMPLE_U, T_SAMPLE_BIAS = 200, 201, 202, 203
+
+
+def sampling_inputs(B: int, V: int, seed: int, scale: float = 2.0, history: int = 64,
+                    bf16_logits: bool = False) -> Dict[str, np.ndarray]:
+    """logits = scale * N(0, 1) fp32 [B, V] (bf16-rounded when asked, so that
+    equal logits occur); history: `history` token ids per row drawn
+    uniformly from [0, V) (int32); u: one uniform in [0, 1) per row
+    (float32); bias: N(0, 1) fp32 [V]."""
+    z = (rng(seed, 7, 0, T_SAMPLE_LOGITS).standard_normal((B, V), dtype=np.float32) * np.float32(scale))
+    if bf16_logits:
+        z = bf16_round(z)
+    h = rng(seed, 7, 0, T_SAMPLE_HISTORY).integers(0, V, size=(B, history)).astype(np.int32)
+    u = rng(seed, 7, 0, T_SAMPLE_U).random(B, dtype=np.float32)
+    bias = rng(seed, 7, 0, T_SAMPLE_BIAS).standard_normal(V, dtype=np.float32)
+    return {"logits": z.astype(np.float32), "history": h, "u": u, "bias": bias}
