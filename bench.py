@@ -475,6 +475,85 @@ def moe_extra(sa, torch):
     return res
 
 
+SAMPLE_CONFIGS = [
+    # name, params (per row), penalties from a 64-token history
+    ("example request (T 0.2, top-p 0.95, min-p 0.05) + penalties",
+     dict(temperature=0.2, top_p=0.95, min_p=0.05, repetition=1.1, presence=0.2, frequency=0.1)),
+    ("top-k 50, T 0.7", dict(temperature=0.7, top_k=50)),
+    ("top-p 0.9, T 1.0", dict(temperature=1.0, top_p=0.9)),
+    ("no truncation, T 1.0", dict(temperature=1.0)),
+    ("greedy", dict(temperature=0.0)),
+]
+
+
+def sample_extra(sa, torch):
+    """sample_tokens on rows of fp32 logits over the GPT-OSS-Lite vocabulary
+    (128,000) at the decode batch (8) and at 64 rows: microseconds per call
+    (all three launches), tokens/s, and HBM GB/s of the inputs it must read
+    (logits, plus the int32 counts when penalties are on), against the same
+    controls written with torch ops (sort, cumsum, masks, inverse CDF)."""
+    import workloads as wl
+    res = {"vocab": wl.SAMPLE_V, "configs": []}
+    for B in (wl.SAMPLE_B, 64):
+        d = wl.sampling_inputs(B, wl.SAMPLE_V, seed=1)
+        lg = torch.from_numpy(d["logits"]).cuda()
+        ut = torch.from_numpy(d["u"]).cuda()
+        counts = torch.zeros((B, wl.SAMPLE_V), dtype=torch.int32, device="cuda")
+        sa.sample_count_tokens(torch.from_numpy(d["history"]).cuda(), counts)
+        ws = torch.empty(sa.sample_workspace_bytes(B, wl.SAMPLE_V), dtype=torch.uint8, device="cuda")
+        for name, p in SAMPLE_CONFIGS:
+            if B != wl.SAMPLE_B and not name.startswith("example"):
+                continue
+            params = sa.sample_params(B, **p)
+            pen = any(k in p for k in ("repetition", "presence", "frequency"))
+            ct = counts if pen else None
+
+            def run():
+                sa.sample_tokens(lg, params, ut, counts=ct, workspace=ws)
+
+            def torch_ops():
+                z = lg
+                if ct is not None:
+                    seen = ct > 0
+                    z = torch.where(seen, torch.where(z > 0, z / p["repetition"], z * p["repetition"]), z)
+                    z = z - p["presence"] * seen.float() - p["frequency"] * ct.float()
+                if p["temperature"] == 0.0:
+                    return z.argmax(dim=1)
+                pr = torch.softmax(z / p["temperature"], dim=1)
+                ps, idx = torch.sort(pr, dim=1, descending=True)
+                keep = torch.ones_like(ps, dtype=torch.bool)
+                if p.get("top_k", 0):
+                    keep[:, p["top_k"]:] = False
+                if p.get("top_p", 1.0) < 1.0:
+                    c = torch.cumsum(ps, dim=1)
+                    keep &= (c - ps) < p["top_p"]
+                if p.get("min_p", 0.0) > 0.0:
+                    keep &= ps >= p["min_p"] * ps[:, :1]
+                ps = ps * keep
+                c = torch.cumsum(ps, dim=1)
+                j = torch.searchsorted(c, (ut * c[:, -1]).unsqueeze(1)).clamp(max=ps.shape[1] - 1)
+                return idx.gather(1, j)
+
+            by = B * wl.SAMPLE_V * (8 if pen else 4)
+            row = {"config": name, "B": B}
+            for nm, f, reps in (("sample_tokens", run, KERNEL_REPEAT), ("torch_ops", torch_ops, 5)):
+                f()
+                torch.cuda.synchronize()
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                for _ in range(reps):
+                    f()
+                b_.record()
+                torch.cuda.synchronize()
+                us = a_.elapsed_time(b_) / reps * 1e3
+                row[nm] = {"us": round(us, 1), "tokens_per_s": round(B / us * 1e6, 0),
+                           "gbs": round(by / us / 1e3, 1), "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
+            res["configs"].append(row)
+        del lg, ut, counts, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, layers, budget_s):
     """The oracle as it stands on a bounded sample of the timed step:
     RoPE of all of Q and K (fp64) and attention for a seeded sample of query
@@ -588,6 +667,7 @@ def main():
         line["extra"]["long_decode"] = decode_extra(sa, torch)
         line["extra"]["qkv_projection"] = qkv_extra(sa, torch)
         line["extra"]["moe_layer"] = moe_extra(sa, torch)
+        line["extra"]["sampling"] = sample_extra(sa, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, layers, args.cpu_seconds)
     print(json.dumps(line), flush=True)

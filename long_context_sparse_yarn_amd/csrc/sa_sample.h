@@ -30,6 +30,7 @@ struct SampleArgs {
   unsigned long long* hist_mass;        // [B, kSampleBuckets]
   unsigned long long* cand;             // [B, kSampleCap] tokens at or above the min-p key
   uint32_t* ncand;                      // [B]
+  unsigned long long* chunk_mass;       // [B, C] mass of each chunk
   int B, V, C;
   int update_counts;
 };

@@ -96,20 +96,30 @@ __device__ __forceinline__ u64 wave_sum_u64(u64 x) {
   return x;
 }
 
-// Row maximum and its lowest id from the per-chunk results (every thread).
-__device__ __forceinline__ void row_max(const SampleArgs& a, int b, float* m, int* arg) {
-  float bv = 0.f;
-  int ba = -1;
-  for (int c = 0; c < a.C; ++c) {
-    const float v = a.chunk_max[(int64_t)b * a.C + c];
-    const int i = a.chunk_arg[(int64_t)b * a.C + c];
-    if (better(v, i, bv, ba)) {
-      bv = v;
-      ba = i;
+// Row maximum and its lowest id from the per-chunk results: wave 0 loads
+// them (C <= 64) and reduces; every thread gets the result through LDS.
+__device__ __forceinline__ void row_max(const SampleArgs& a, int b, float* m, int* arg, float* sv, int* si) {
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x;
+    float bv = c < a.C ? a.chunk_max[(int64_t)b * a.C + c] : 0.f;
+    int ba = c < a.C ? a.chunk_arg[(int64_t)b * a.C + c] : -1;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float ov = __shfl_xor(bv, s, 64);
+      const int oa = __shfl_xor(ba, s, 64);
+      if (better(ov, oa, bv, ba)) {
+        bv = ov;
+        ba = oa;
+      }
+    }
+    if (c == 0) {
+      *sv = bv;
+      *si = ba;
     }
   }
-  *m = ba >= 0 ? bv : -INFINITY;
-  *arg = ba;
+  __syncthreads();
+  *arg = *si;
+  *m = *arg >= 0 ? *sv : -INFINITY;
 }
 
 // ------------------------------------------------------------------ prep
@@ -207,9 +217,11 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const sa_sample_params P = a.params[b];
   if (!params_ok(P, a.u[b]) || P.temperature == 0.f) return;
+  __shared__ float rmv;
+  __shared__ int rmi;
   float m;
   int arg;
-  row_max(a, b, &m, &arg);
+  row_max(a, b, &m, &arg, &rmv, &rmi);
   if (!(fabsf(m) <= kFltMax)) return;               // no finite maximum: the row has no token
   const float cT = temp_coef(P.temperature);
   const bool gather = P.min_p > 0.f;
@@ -229,6 +241,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
     const int v = v0 + j * kPrepThreads;
     z[j] = v < a.V ? Z[v] : 0.f;
   }
+  u64 qsum = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int v = v0 + j * kPrepThreads;
@@ -236,6 +249,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
     if (v < a.V) {
       atomicAdd(&hc[k >> 20], 1u);
       const u64 q = fixed_mass(rel_weight(z[j], m, cT));
+      qsum += q;
       if (q) atomicAdd(&hm[k >> 20], q);
     }
     if (gather) {
@@ -251,7 +265,11 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
       }
     }
   }
+  qsum = wave_sum_u64(qsum);
+  __shared__ u64 wq[kPrepThreads / 64];
+  if (lane == 0) wq[tid >> 6] = qsum;
   __syncthreads();
+  if (tid == 0) a.chunk_mass[(int64_t)b * a.C + c] = wq[0] + wq[1] + wq[2] + wq[3];
   for (int i = tid; i < kNB; i += kPrepThreads) {
     if (hc[i]) atomicAdd(&a.hist_count[(int64_t)b * kNB + i], hc[i]);
     if (hm[i]) atomicAdd(&a.hist_mass[(int64_t)b * kNB + i], hm[i]);
@@ -279,6 +297,8 @@ struct SelShared {
   uint32_t ncand;
   int idx;
   u64 val;
+  float rmv;
+  int rmi;
 };
 
 // Exclusive prefix sums over the workgroup's threads of three values, and totals.
@@ -537,7 +557,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a
   int token = -1, kept = 0;
   float m;
   int arg;
-  row_max(a, b, &m, &arg);
+  row_max(a, b, &m, &arg, &S.rmv, &S.rmi);
   const bool ok = params_ok(P, u);
   const bool greedy = ok && P.temperature == 0.f;
   if (greedy && arg >= 0) {
@@ -550,18 +570,13 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a
     const float cT = temp_coef(P.temperature);
     const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
     const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;
-    for (int i = tid; i < kNB; i += kSelThreads) {
-      S.c1[i] = a.hist_count[(int64_t)b * kNB + i];
-      S.m1[i] = a.hist_mass[(int64_t)b * kNB + i];
+    if (tid < 64) {
+      const u64 x = wave_sum_u64(tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull);
+      if (tid == 0) S.val = x;
     }
     __syncthreads();
-    u64 q_all;
-    {
-      u64 x[3] = {0, 0, 0}, ex[3], tot[3];
-      for (int i = 0; i < 4; ++i) x[0] += S.m1[4 * tid + i];
-      block_scan3(S, x, ex, tot);
-      q_all = tot[0];
-    }
+    const u64 q_all = S.val;           // the row's total mass
+    __syncthreads();
     const uint32_t gathered = mA ? a.ncand[b] : 0xFFFFFFFFu;
     if (mA && gathered <= (uint32_t)kCap && !(kA && pA && (int)gathered < P.top_k)) {
       // ---- the min-p candidates gathered by the histogram launch
@@ -570,6 +585,11 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a
       __syncthreads();
       token = finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, &kept);
     } else {
+      for (int i = tid; i < kNB; i += kSelThreads) {
+        S.c1[i] = a.hist_count[(int64_t)b * kNB + i];
+        S.m1[i] = a.hist_mass[(int64_t)b * kNB + i];
+      }
+      __syncthreads();
       // bucket-aligned bound on the kept set's lowest key, from the histogram
       uint32_t bk = 0, bp = 0;
       if (kA) {
