@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--extra-only", choices=("sampling", "moe", "qkv"), default=None,
+                    help="print only that extra leg's figures (for profiling it alone)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 3 times (reference dispatch for "
@@ -626,6 +628,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}))
+        return
+    if args.extra_only:
+        leg = {"sampling": sample_extra, "moe": moe_extra, "qkv": qkv_extra}[args.extra_only]
+        print(json.dumps({args.extra_only: leg(sa, torch)}), flush=True)
         return
     w = wl.LITE_PREFILL
     layers, ms_step, kern_ms, in_step = time_prefill_step(w, sa, torch, args.steps, args.warmup)

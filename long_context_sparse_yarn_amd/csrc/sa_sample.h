@@ -8,6 +8,7 @@
 
 constexpr int kSampleChunk = 4096;      // vocabulary entries per prep / histogram workgroup
 constexpr int kSampleBuckets = 4096;    // first-level histogram: the top 12 bits of the key
+constexpr int kSampleHist = kSampleBuckets + 64;   // then 64 sums of 64 buckets
 constexpr int kSampleMaxV = 64 * 4096;  // the draw keeps one mass per 64 ids in LDS
 constexpr int kSampleCap = 4096;        // candidates sorted in LDS
 
@@ -26,8 +27,8 @@ struct SampleArgs {
   float* zp;                            // [B, V] processed logits
   float* chunk_max;                     // [B, C]
   int32_t* chunk_arg;                   // [B, C]
-  uint32_t* hist_count;                 // [B, kSampleBuckets]
-  unsigned long long* hist_mass;        // [B, kSampleBuckets]
+  uint32_t* hist_count;                 // [B, kSampleHist]
+  unsigned long long* hist_mass;        // [B, kSampleHist]
   unsigned long long* cand;             // [B, kSampleCap] tokens at or above the min-p key
   uint32_t* ncand;                      // [B]
   unsigned long long* chunk_mass;       // [B, C] mass of each chunk

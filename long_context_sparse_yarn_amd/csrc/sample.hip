@@ -41,9 +41,10 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kPer = kSampleChunk / kPrepThreads;   // 16 entries per thread
 constexpr int kNB = kSampleBuckets;
+constexpr int kHist = kSampleHist;                  // 4096 buckets, then 64 sums of 64 buckets
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelPer = 16;                         // loads in flight per thread in a select pass
+constexpr int kSelPer = 8;                          // loads in flight per thread in a select pass
 constexpr int kCap = kSampleCap;
 constexpr float kFltMax = 3.4028235e38f;
 typedef unsigned long long u64;
@@ -192,10 +193,10 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
     wa[tid >> 6] = arg;
   }
   // clear this chunk's share of the row's histogram (filled by the next launch)
-  const int share = (kNB + a.C - 1) / a.C;
-  for (int i = c * share + tid; i < min(kNB, (c + 1) * share); i += kPrepThreads) {
-    a.hist_count[(int64_t)b * kNB + i] = 0u;
-    a.hist_mass[(int64_t)b * kNB + i] = 0ull;
+  const int share = (kHist + a.C - 1) / a.C;
+  for (int i = c * share + tid; i < min(kHist, (c + 1) * share); i += kPrepThreads) {
+    a.hist_count[(int64_t)b * kHist + i] = 0u;
+    a.hist_mass[(int64_t)b * kHist + i] = 0ull;
   }
   if (c == 0 && tid == 0) a.ncand[b] = 0u;
   __syncthreads();
@@ -271,8 +272,143 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
   __syncthreads();
   if (tid == 0) a.chunk_mass[(int64_t)b * a.C + c] = wq[0] + wq[1] + wq[2] + wq[3];
   for (int i = tid; i < kNB; i += kPrepThreads) {
-    if (hc[i]) atomicAdd(&a.hist_count[(int64_t)b * kNB + i], hc[i]);
-    if (hm[i]) atomicAdd(&a.hist_mass[(int64_t)b * kNB + i], hm[i]);
+    if (hc[i]) atomicAdd(&a.hist_count[(int64_t)b * kHist + i], hc[i]);
+    if (hm[i]) atomicAdd(&a.hist_mass[(int64_t)b * kHist + i], hm[i]);
+  }
+  if (tid < 64) {                                   // the sums of 64 buckets
+    uint32_t sc = 0;
+    u64 sm = 0;
+#pragma unroll 4
+    for (int i = 0; i < 64; ++i) {
+      const int k = 64 * tid + ((i + tid) & 63);      // staggered: no bank conflicts
+      sc += hc[k];
+      sm += hm[k];
+    }
+    if (sc) atomicAdd(&a.hist_count[(int64_t)b * kHist + kNB + tid], sc);
+    if (sm) atomicAdd(&a.hist_mass[(int64_t)b * kHist + kNB + tid], sm);
+  }
+}
+
+// ---------------------------------------------------------- bucket bound
+// The first-level histogram (counts c1, masses m1, 4096 buckets by the key's
+// top 12 bits) tells in which bucket each threshold falls.  One wave does
+// it, lane l holding the 64 buckets 4095 - 64 l - 63 .. 4095 - 64 l, so the
+// gather launch (256 threads) and the select launch (1024) get the same
+// integers.
+
+struct Pick {
+  uint32_t digit;             // bucket at which the running weight reaches the target
+  u64 cnt_above, mass_above;  // counts and masses of the buckets above it
+};
+
+__device__ __forceinline__ void wave_scan3(u64& w, u64& c, u64& m) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const u64 yw = __shfl_up(w, d, 64), yc = __shfl_up(c, d, 64), ym = __shfl_up(m, d, 64);
+    if (lane >= d) {
+      w += yw;
+      c += yc;
+      m += ym;
+    }
+  }
+}
+
+// Scanning the row's buckets (cnt, mass: 4096 buckets then 64 sums of 64)
+// from the top down, the bucket at which the running count (by_mass: mass)
+// first reaches target (target <= the total): first over the 64 sums, then
+// over the 64 buckets of the one that reaches it.  Call from one whole wave.
+__device__ Pick wave_pick(const uint32_t* cnt, const u64* mass, bool by_mass, u64 target) {
+  const int lane = threadIdx.x & 63;
+  const u64 cc = cnt[kNB + 63 - lane], cm = mass[kNB + 63 - lane], cw = by_mass ? cm : cc;
+  u64 iw = cw, ic = cc, im = cm;
+  wave_scan3(iw, ic, im);
+  const u64 h1 = __ballot(iw - cw < target && iw >= target);
+  const int L1 = h1 ? (int)(__ffsll((long long)h1) - 1) : 63;
+  const int sup = 63 - L1;
+  const u64 aw = __shfl(iw - cw, L1, 64), ac = __shfl(ic - cc, L1, 64), am = __shfl(im - cm, L1, 64);
+  const int bk = 64 * sup + 63 - lane;
+  const u64 fc = cnt[bk], fm = mass[bk], fw = by_mass ? fm : fc;
+  u64 jw = fw, jc = fc, jm = fm;
+  wave_scan3(jw, jc, jm);
+  const u64 h2 = __ballot(aw + jw - fw < target && aw + jw >= target);
+  const int L2 = h2 ? (int)(__ffsll((long long)h2) - 1) : 63;
+  Pick p;
+  p.digit = (uint32_t)(64 * sup + 63 - L2);
+  p.cnt_above = ac + __shfl(jc - fc, L2, 64);
+  p.mass_above = am + __shfl(jm - fm, L2, 64);
+  return p;
+}
+
+// Lower bound (bucket) on the keys of the kept set when top-k or top-p is on
+// and min-p is off, and how many tokens lie at or above it: top-k's bucket,
+// or top-p's bucket on the whole mass; with both on, top-k's bucket (the
+// top-k mass needs every token above the k-th).  Call from one whole wave.
+__device__ void wave_bound(const uint32_t* cnt, const u64* mass, const sa_sample_params& P, int V, u64 q_all,
+                           uint32_t* blb, u64* nb) {
+  const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f;
+  if (!kA && !pA) {
+    *blb = 0;
+    *nb = (u64)V;
+    return;
+  }
+  const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)q_all));
+  const Pick p = wave_pick(cnt, mass, !kA, kA ? (u64)P.top_k : tau);
+  *blb = p.digit;
+  *nb = p.cnt_above + cnt[p.digit];
+}
+
+// The row's total mass from the per-chunk sums (one whole wave).
+__device__ __forceinline__ u64 wave_row_mass(const SampleArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  return wave_sum_u64(lane < a.C ? a.chunk_mass[(int64_t)b * a.C + lane] : 0ull);
+}
+
+// ---------------------------------------------------------------- gather
+// Rows with top-k or top-p on and min-p off: the tokens at or above the
+// bucket bound, when there are at most 4096 of them, go to the row's
+// candidate list, every chunk in its own workgroup.
+__global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs a) {
+  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const sa_sample_params P = a.params[b];
+  if (!params_ok(P, a.u[b]) || P.temperature == 0.f || P.min_p > 0.f) return;
+  if (!(P.top_k > 0 && P.top_k < a.V) && !(P.top_p < 1.f)) return;
+  __shared__ float rmv;
+  __shared__ int rmi;
+  __shared__ uint32_t s_blb;
+  __shared__ u64 s_nb;
+  float m;
+  int arg;
+  row_max(a, b, &m, &arg, &rmv, &rmi);
+  if (!(fabsf(m) <= kFltMax)) return;
+  if (tid < 64) {
+    const u64 q_all = wave_row_mass(a, b);
+    uint32_t blb;
+    u64 nb;
+    wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, a.V, q_all, &blb, &nb);
+    if (tid == 0) {
+      s_blb = blb;
+      s_nb = nb;
+    }
+  }
+  __syncthreads();
+  if (s_nb > (u64)kCap) return;                     // the select launch takes the radix path
+  const uint32_t klb = s_blb << 20;
+  const float* Z = a.zp + (int64_t)b * a.V;
+  const int v0 = c * kSampleChunk + tid;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    const uint32_t k = v < a.V ? fkey(Z[v]) : 0u;
+    const bool take = v < a.V && k >= klb;
+    const u64 mask = __ballot(take);
+    if (mask) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
+      base = __shfl(base, 0, 64);
+      const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+      if (take && slot < (uint32_t)kCap) a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+    }
   }
 }
 
@@ -291,14 +427,17 @@ struct SelShared {
     } cand;                               // candidates
     u64 grp[kSampleMaxV / 64];            // kept mass per run of 64 ids
   } u;
+  u64 cm[kSampleMaxV / kSampleChunk];     // kept mass per chunk
   u64 wtot[3][kSelWaves];
   uint32_t digit;
   u64 add_cnt, add_mass;
-  uint32_t ncand;
   int idx;
   u64 val;
   float rmv;
   int rmi;
+  uint32_t blb;
+  u64 nb;
+  int res_token, res_kept;
 };
 
 // Exclusive prefix sums over the workgroup's threads of three values, and totals.
@@ -330,22 +469,23 @@ __device__ void block_scan3(SelShared& S, const u64 (&x)[3], u64 (&excl)[3], u64
   __syncthreads();
 }
 
-// f(v, z, valid) over the row, kSelPer loads in flight per thread; every
-// lane of every wave calls f the same number of times (ballots allowed).
-// Thread t sees v = v0 + j * 1024 + t: lanes of a wave hold 64 consecutive ids.
+// f(v, z, valid) over ids [lo, hi), kSelPer loads in flight per thread; every
+// lane of every wave calls f the same number of times (ballots and wave
+// reductions allowed).  Thread t sees v = lo + v0 + j * 1024 + t: the lanes
+// of a wave hold 64 consecutive ids.
 template <class F>
-__device__ __forceinline__ void row_pass(const float* Z, int V, F f) {
-  for (int v0 = 0; v0 < V; v0 += kSelPer * kSelThreads) {
+__device__ __forceinline__ void row_pass(const float* Z, int lo, int hi, F f) {
+  for (int v0 = lo; v0 < hi; v0 += kSelPer * kSelThreads) {
     float z[kSelPer];
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) {
       const int v = v0 + j * kSelThreads + (int)threadIdx.x;
-      z[j] = v < V ? Z[v] : -INFINITY;
+      z[j] = v < hi ? Z[v] : -INFINITY;
     }
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) {
       const int v = v0 + j * kSelThreads + (int)threadIdx.x;
-      f(v, z[j], v < V);
+      f(j, v, z[j], v < hi);
     }
   }
 }
@@ -396,7 +536,7 @@ __device__ void level_pass(SelShared& S, const float* Z, int V, float m, float c
     S.u.h.m[i] = 0ull;
   }
   __syncthreads();
-  row_pass(Z, V, [&](int v, float z, bool valid) {
+  row_pass(Z, 0, V, [&](int, int, float z, bool valid) {
     const uint32_t k = fkey(z);
     if (valid && (k >> prefix_shift) == prefix) {
       const uint32_t d = (k >> digit_shift) & digit_mask;
@@ -430,6 +570,69 @@ __device__ void descend(SelShared& S, const float* Z, int V, float m, float cT, 
   *K = (d1 << 20) | (d2 << 8) | d3;
   *mass_ge = am + S.u.h.m[d3];
   __syncthreads();
+}
+
+// The draw inside ids [lo, hi) (hi - lo <= 4096 * 64): the first id whose key
+// is >= Ks and whose cumulative kept mass from lo exceeds t (t below the
+// range's kept mass).  Kept masses per run of 64 ids, a scan over the runs,
+// then one wave's scan of the run holding t.  Returns the id (-1 if t is not
+// below the range's kept mass); *kept gets the range's kept count.
+__device__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t Ks, float m, float cT, u64 t,
+                          int* kept) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ng = (hi - lo + 63) / 64;
+  uint32_t nk = 0;
+  row_pass(Z, lo, hi, [&](int, int v, float z, bool valid) {
+    const bool in = valid && fkey(z) >= Ks;
+    nk += in ? 1u : 0u;
+    const u64 s = wave_sum_u64(in ? fixed_mass(rel_weight(z, m, cT)) : 0ull);
+    if (lane == 0 && v < lo + 64 * ng) S.u.grp[(v - lo) >> 6] = s;
+  });
+  if (tid == 0) {
+    S.idx = -1;
+    S.val = 0;
+  }
+  __syncthreads();
+  u64 gq[4];
+  u64 x[3] = {0, (u64)nk, 0}, ex[3], tot[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    gq[i] = g < ng ? S.u.grp[g] : 0ull;
+    x[0] += gq[i];
+  }
+  block_scan3(S, x, ex, tot);
+  *kept = (int)tot[1];
+  u64 run = ex[0];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    if (g < ng && run <= t && t < run + gq[i]) {
+      S.idx = g;
+      S.val = run;
+    }
+    run += gq[i];
+  }
+  __syncthreads();
+  if (wave == 0 && S.idx >= 0) {
+    const int g = S.idx;
+    const int v = lo + 64 * g + lane;
+    const float z = v < hi ? Z[v] : -INFINITY;
+    const bool in = v < hi && fkey(z) >= Ks;
+    u64 inc = in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const u64 y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    const u64 over = __ballot(S.val + inc > t);
+    if (lane == 0) S.res_token = over ? lo + 64 * g + (int)(__ffsll((long long)over) - 1) : -1;
+  }
+  if (tid == 0 && S.idx < 0) S.res_token = -1;
+  __syncthreads();
+  const int r = S.res_token;
+  __syncthreads();
+  return r;
 }
 
 // In-place bitonic sort, descending, of S.u.cand.key[0, n), n a power of two.
@@ -489,12 +692,165 @@ __device__ void cand_prefix(SelShared& S, int n, F mass_of) {
   __syncthreads();
 }
 
+// Thresholds over a ranking prefix that holds the kept set (candidates,
+// sorted): a threshold that falls below the candidates is not the binding
+// one.  key(e), cum(e): key and inclusive mass of the e-th candidate.
+struct Thresholds {
+  uint32_t Ks;
+  u64 qn;
+  int nk;
+};
+
+// Bitonic sort, descending, of the 64 R values a wave holds, element
+// i = 64 r + lane in x[r]: partners 64 or more apart sit in one lane,
+// nearer ones are a shuffle away.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(u64 (&x)[R]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64 * R; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int rj = j / 64;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int p = r ^ rj;
+          if (p > r) {
+            const bool desc = ((64 * r + lane) & k) == 0;
+            const u64 lo = x[r], hi = x[p];
+            const bool swap = desc ? lo < hi : lo > hi;
+            x[r] = swap ? hi : lo;
+            x[p] = swap ? lo : hi;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const u64 y = __shfl_xor(x[r], j, 64);
+          const bool desc = ((64 * r + lane) & k) == 0, lower = (lane & j) == 0;
+          x[r] = (desc == lower) ? (x[r] > y ? x[r] : y) : (x[r] < y ? x[r] : y);
+        }
+      }
+    }
+  }
+}
+__device__ __forceinline__ u64 wave_incl_scan(u64 x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const u64 y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+// Element e (wave-uniform) of a wave-held array.
+template <int R>
+__device__ __forceinline__ u64 wave_at(const u64 (&x)[R], int e) {
+  u64 v = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u64 y = __shfl(x[r], e & 63, 64);
+    if (r == (e >> 6)) v = y;
+  }
+  return v;
+}
+// Inclusive prefix over elements 0..n-1 in order of the masses of the keys
+// in key_of(x[r]).
+template <int R, class K>
+__device__ __forceinline__ void wave_prefix(const u64 (&x)[R], int n, u64 (&cum)[R], float m, float cT, K key_of) {
+  const int lane = threadIdx.x & 63;
+  u64 base = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u64 q = 64 * r + lane < n ? mass_of_key(key_of(x[r]), m, cT) : 0ull;
+    const u64 inc = wave_incl_scan(q);
+    cum[r] = base + inc;
+    base += __shfl(inc, 63, 64);
+  }
+}
+// The first element (in order) for which pred holds, or -1.
+template <int R, class F>
+__device__ __forceinline__ int wave_first(F pred) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u64 h = __ballot(pred(r, 64 * r + lane));
+    if (h) return 64 * r + (int)(__ffsll((long long)h) - 1);
+  }
+  return -1;
+}
+// How many elements pred holds for.
+template <int R, class F>
+__device__ __forceinline__ int wave_count(F pred) {
+  const int lane = threadIdx.x & 63;
+  int c = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) c += __popcll(__ballot(pred(r, 64 * r + lane)));
+  return c;
+}
+
+// At most 64 R candidates (key << 32 | ~id) in S.u.cand.key[0, n): one wave
+// sorts, thresholds and draws in registers, with no barrier.  Call from one
+// whole wave.
+template <int R>
+__device__ int finish_in_wave(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
+                              float m, float cT, u64 q_all, uint32_t Km, int* kept) {
+  const int lane = threadIdx.x & 63;
+  u64 x[R], cum[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = 64 * r + lane < n ? S.u.cand.key[64 * r + lane] : 0ull;
+  wave_sort_desc<R>(x);
+  auto hi_key = [](u64 v) { return (uint32_t)(v >> 32); };
+  wave_prefix<R>(x, n, cum, m, cT, hi_key);
+  uint32_t Kk = 0, Kp = 0;
+  u64 qk = q_all;
+  if (kA && n >= P.top_k) {
+    Kk = hi_key(wave_at<R>(x, P.top_k - 1));
+    const int c = wave_count<R>([&](int r, int e) { return e < n && hi_key(x[r]) >= Kk; });
+    qk = wave_at<R>(cum, c - 1);
+  }
+  if (pA) {
+    const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
+    const int e = wave_first<R>([&](int r, int i) { return i < n && cum[r] >= tau; });
+    if (e >= 0) Kp = hi_key(wave_at<R>(x, e));
+  }
+  const uint32_t Ks = max(max(Kk, Kp), Km);
+  const int nk = wave_count<R>([&](int r, int e) { return e < n && hi_key(x[r]) >= Ks; });
+  if (nk == 0) return -1;
+  const u64 qn = wave_at<R>(cum, nk - 1);
+  u64 t = (u64)((double)u * (double)qn);
+  if (t >= qn) t = qn - 1;
+  // the kept ones by increasing id: (~id << 32 | key), descending
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = 64 * r + lane < nk ? (((u64)(uint32_t)x[r] << 32) | (x[r] >> 32)) : 0ull;
+  wave_sort_desc<R>(x);
+  wave_prefix<R>(x, nk, cum, m, cT, [](u64 v) { return (uint32_t)v; });
+  int at = wave_first<R>([&](int r, int i) { return i < nk && cum[r] > t; });
+  if (at < 0) at = nk - 1;
+  *kept = nk;
+  return (int)~(uint32_t)(wave_at<R>(x, at) >> 32);
+}
+
 // The candidates S.u.cand.key[0, n) (key << 32 | ~id) are every token at or
-// above some key, a prefix of the ranking that holds the kept set; a
-// threshold that falls below them is not the binding one.  Returns the
-// token (and the kept count in *kept), or -1.
+// above some key, a prefix of the ranking that holds the kept set.  Returns
+// the token (and the kept count in *kept), or -1.
 __device__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
                              float m, float cT, u64 q_all, uint32_t Km, int* kept) {
+  if (n <= 256) {
+    if (threadIdx.x < 64) {
+      int k = 0;
+      const int t = n <= 64 ? finish_in_wave<1>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k)
+                            : finish_in_wave<4>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k);
+      if (threadIdx.x == 0) {
+        S.res_token = t;
+        S.res_kept = k;
+      }
+    }
+    __syncthreads();
+    *kept = S.res_kept;
+    return S.res_token;
+  }
   pad_sort(S, n);
   cand_prefix(S, n, [&](int e) { return mass_of_key((uint32_t)(S.u.cand.key[e] >> 32), m, cT); });
   auto key_at = [&](int e) { return (uint32_t)(S.u.cand.key[e] >> 32); };
@@ -549,9 +905,68 @@ __device__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sam
   return (int)~(uint32_t)(S.u.cand.key[S.idx] >> 32);
 }
 
+// Candidates from the row's list in the workspace into LDS, then finish.
+__device__ int finish_from_list(SelShared& S, const SampleArgs& a, int b, int n, bool kA, bool pA,
+                                const sa_sample_params& P, float u, float m, float cT, u64 q_all, uint32_t Km,
+                                int* kept) {
+  for (int i = threadIdx.x; i < n; i += kSelThreads) S.u.cand.key[i] = a.cand[(int64_t)b * kCap + i];
+  __syncthreads();
+  return finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, kept);
+}
+
+// The draw over the whole row for kept = key >= Ks: kept mass per chunk of
+// 4096 ids (one wave sum per chunk per wave), the chunk that holds the
+// target, then draw_range inside it.
+__device__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V, uint32_t Ks, float m, float cT,
+                        float u, int* kept) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int C = a.C;
+  if (tid < C) S.cm[tid] = 0ull;
+  __syncthreads();
+  uint32_t nk = 0;
+  constexpr int kJPerChunk = kSampleChunk / kSelThreads;   // 4 loads of a thread share a chunk
+  u64 part = 0;
+  row_pass(Z, 0, V, [&](int j, int v, float z, bool valid) {
+    const bool in = valid && fkey(z) >= Ks;
+    nk += in ? 1u : 0u;
+    part += in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
+    if ((j % kJPerChunk) == kJPerChunk - 1) {
+      const u64 s = wave_sum_u64(part);
+      part = 0;
+      const int c = (v - j * kSelThreads - tid) / kSampleChunk + j / kJPerChunk;
+      if (lane == 0 && s && c < C) atomicAdd(&S.cm[c], s);
+    }
+  });
+  u64 x[3] = {0, (u64)nk, 0}, ex[3], tot[3];
+  block_scan3(S, x, ex, tot);
+  const int kept_all = (int)tot[1];
+  if (tid < 64) {
+    const u64 cmv = tid < C ? S.cm[tid] : 0ull;
+    const u64 inc = wave_incl_scan(cmv);
+    const u64 qn = __shfl(inc, 63, 64);
+    u64 t = (u64)((double)u * (double)qn);
+    if (t >= qn) t = qn - 1;
+    const u64 hit = __ballot(tid < C && inc > t);
+    const int c = hit ? (int)(__ffsll((long long)hit) - 1) : 0;
+    const u64 before = __shfl(inc, c, 64) - __shfl(cmv, c, 64);   // the whole wave takes part
+    if (tid == 0) {
+      S.idx = c;
+      S.val = t - before;
+    }
+  }
+  __syncthreads();
+  const int c = S.idx;
+  const u64 t_in = S.val;
+  __syncthreads();
+  int k_unused;
+  const int token = draw_range(S, Z, c * kSampleChunk, min(V, (c + 1) * kSampleChunk), Ks, m, cT, t_in, &k_unused);
+  *kept = kept_all;
+  return token;
+}
+
 __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a) {
   __shared__ SelShared S;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const sa_sample_params P = a.params[b];
   const float u = a.u[b];
   int token = -1, kept = 0;
@@ -571,132 +986,79 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a
     const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
     const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;
     if (tid < 64) {
-      const u64 x = wave_sum_u64(tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull);
+      const u64 x = wave_row_mass(a, b);
       if (tid == 0) S.val = x;
     }
     __syncthreads();
     const u64 q_all = S.val;           // the row's total mass
     __syncthreads();
-    const uint32_t gathered = mA ? a.ncand[b] : 0xFFFFFFFFu;
-    if (mA && gathered <= (uint32_t)kCap && !(kA && pA && (int)gathered < P.top_k)) {
+    const uint32_t listed = a.ncand[b];
+    bool done = false;
+    if (mA && listed <= (uint32_t)kCap && !(kA && pA && (int)listed < P.top_k)) {
       // ---- the min-p candidates gathered by the histogram launch
-      const int n = (int)gathered;
-      for (int i = tid; i < n; i += kSelThreads) S.u.cand.key[i] = a.cand[(int64_t)b * kCap + i];
-      __syncthreads();
-      token = finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, &kept);
-    } else {
-      for (int i = tid; i < kNB; i += kSelThreads) {
-        S.c1[i] = a.hist_count[(int64_t)b * kNB + i];
-        S.m1[i] = a.hist_mass[(int64_t)b * kNB + i];
-      }
-      __syncthreads();
-      // bucket-aligned bound on the kept set's lowest key, from the histogram
-      uint32_t bk = 0, bp = 0;
-      if (kA) {
-        pick_digit(S, S.c1, S.m1, kNB, false, (u64)P.top_k, 0);
-        bk = S.digit;
-        __syncthreads();
-      }
-      if (pA && !kA) {
-        const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)q_all));
-        pick_digit(S, S.c1, S.m1, kNB, true, tau, 0);
-        bp = S.digit;
-        __syncthreads();
-      }
-      // with both top-k and top-p on, the top-k mass needs every token above Kk
-      const uint32_t blb = (kA && pA) ? bk : max(max(bk, bp), Km >> 20);
-      u64 nb;
-      {
-        u64 x[3] = {0, 0, 0}, ex[3], tot[3];
-        for (int i = 0; i < 4; ++i) x[0] += (uint32_t)(4 * tid + i) >= blb ? S.c1[4 * tid + i] : 0u;
-        block_scan3(S, x, ex, tot);
-        nb = tot[0];
-      }
-      if (nb <= (u64)kCap) {
-        // ---- gather the tokens at or above the bound in one pass
-        if (tid == 0) S.ncand = 0;
-        __syncthreads();
-        const uint32_t klb = blb << 20;
-        row_pass(Z, V, [&](int v, float z, bool valid) {
-          const uint32_t k = fkey(z);
-          const bool take = valid && k >= klb;
-          const u64 mask = __ballot(take);
-          if (mask) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&S.ncand, (uint32_t)__popcll(mask));
-            base = __shfl(base, 0, 64);
-            const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-            if (take && slot < (uint32_t)kCap) S.u.cand.key[slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
-          }
-        });
-        __syncthreads();
-        const int n = (int)min(S.ncand, (uint32_t)kCap);
-        token = finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, &kept);
-      } else {
-        // ---- large kept set: radix levels over z', then the draw pass
-        uint32_t Kk = 0, Kp = 0;
-        u64 qk = q_all;
-        if (kA) descend(S, Z, V, m, cT, false, (u64)P.top_k, &Kk, &qk);
-        if (pA) {
-          const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
-          u64 unused;
-          descend(S, Z, V, m, cT, true, tau, &Kp, &unused);
-        }
-        const uint32_t Ks = max(max(Kk, Kp), Km);
-        const int ng = (V + 63) / 64;
-        uint32_t nk_part = 0;
+      token = finish_from_list(S, a, b, (int)listed, kA, pA, P, u, m, cT, q_all, Km, &kept);
+      done = true;
+    } else if (!mA && !kA && !pA) {
+      // ---- no truncation: the chunk masses locate the draw
+      if (tid < 64) {
+        const u64 cmv = tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull;
+        const u64 inc = wave_incl_scan(cmv);
+        u64 t = (u64)((double)u * (double)q_all);
+        if (t >= q_all) t = q_all - 1;
+        const u64 hit = __ballot(tid < a.C && inc > t);
+        const int c = hit ? (int)(__ffsll((long long)hit) - 1) : 0;
+        const u64 before = __shfl(inc, c, 64) - __shfl(cmv, c, 64);
         if (tid == 0) {
-          S.idx = 0;
-          S.val = 0;
+          S.idx = c;
+          S.val = t - before;
         }
-        row_pass(Z, V, [&](int v, float z, bool valid) {
-          const bool in = valid && fkey(z) >= Ks;
-          nk_part += in ? 1u : 0u;
-          const u64 s = wave_sum_u64(in ? fixed_mass(rel_weight(z, m, cT)) : 0ull);
-          if (lane == 0 && v < 64 * ng) S.u.grp[v >> 6] = s;
-        });
-        __syncthreads();
-        u64 gq[4];
-        u64 x[3] = {0, (u64)nk_part, 0}, ex[3], tot[3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = 4 * tid + i;
-          gq[i] = g < ng ? S.u.grp[g] : 0ull;
-          x[0] += gq[i];
-        }
-        block_scan3(S, x, ex, tot);
-        const u64 qn = tot[0];
-        kept = (int)tot[1];
-        u64 t = (u64)((double)u * (double)qn);
-        if (t >= qn) t = qn - 1;
-        u64 run = ex[0];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = 4 * tid + i;
-          if (g < ng && run <= t && t < run + gq[i]) {
-            S.idx = g;
-            S.val = run;
-          }
-          run += gq[i];
-        }
-        __syncthreads();
-        if (wave == 0) {
-          const int g = S.idx;
-          const int v = 64 * g + lane;
-          const float z = v < V ? Z[v] : -INFINITY;
-          const bool in = v < V && fkey(z) >= Ks;
-          u64 inc = in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const u64 y = __shfl_up(inc, d, 64);
-            if (lane >= d) inc += y;
-          }
-          const u64 over = __ballot(S.val + inc > t);
-          if (lane == 0) S.idx = over ? 64 * g + (int)(__ffsll((long long)over) - 1) : -1;
-        }
-        __syncthreads();
-        token = S.idx;
       }
+      __syncthreads();
+      const int c = S.idx;
+      const u64 t_in = S.val;
+      __syncthreads();
+      int k_unused;
+      token = draw_range(S, Z, c * kSampleChunk, min(V, (c + 1) * kSampleChunk), 0u, m, cT, t_in, &k_unused);
+      kept = V;
+      done = true;
+    }
+    if (!done) {
+      if (!mA) {
+        if (tid < 64) {
+          uint32_t blb;
+          u64 nb;
+          wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, V, q_all, &blb,
+                     &nb);
+          if (tid == 0) {
+            S.blb = blb;
+            S.nb = nb;
+          }
+        }
+        __syncthreads();
+        if (S.nb <= (u64)kCap) {
+          // ---- gathered by the gather launch: every token at or above the bound
+          token = finish_from_list(S, a, b, (int)min(listed, (uint32_t)kCap), kA, pA, P, u, m, cT, q_all, Km,
+                                   &kept);
+          done = true;
+        }
+      }
+    }
+    if (!done) {
+      // ---- large kept set: radix levels over z', then the draw
+      for (int i = tid; i < kNB; i += kSelThreads) {
+        S.c1[i] = a.hist_count[(int64_t)b * kHist + i];
+        S.m1[i] = a.hist_mass[(int64_t)b * kHist + i];
+      }
+      __syncthreads();
+      uint32_t Kk = 0, Kp = 0;
+      u64 qk = q_all;
+      if (kA) descend(S, Z, V, m, cT, false, (u64)P.top_k, &Kk, &qk);
+      if (pA) {
+        const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
+        u64 unused;
+        descend(S, Z, V, m, cT, true, tau, &Kp, &unused);
+      }
+      token = draw_row(S, a, Z, V, max(max(Kk, Kp), Km), m, cT, u, &kept);
     }
   }
   if (tid == 0) {
@@ -720,6 +1082,7 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
   const dim3 grid(a.C, a.B);
   hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepThreads), 0, s, a);
   hipLaunchKernelGGL(sample_hist_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_gather_kernel, grid, dim3(kPrepThreads), 0, s, a);
   hipLaunchKernelGGL(sample_select_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }

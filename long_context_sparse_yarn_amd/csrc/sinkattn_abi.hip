@@ -822,8 +822,8 @@ SampleLayout sample_layout(int B, int V) {
   L.zp = take((size_t)B * V * 4);
   L.cmax = take((size_t)B * C * 4);
   L.carg = take((size_t)B * C * 4);
-  L.hcount = take((size_t)B * kSampleBuckets * 4);
-  L.hmass = take((size_t)B * kSampleBuckets * 8);
+  L.hcount = take((size_t)B * kSampleHist * 4);
+  L.hmass = take((size_t)B * kSampleHist * 8);
   L.cand = take((size_t)B * kSampleCap * 8);
   L.ncand = take((size_t)B * 4);
   L.rmass = take((size_t)B * C * 8);
