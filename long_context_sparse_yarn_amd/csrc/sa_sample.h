@@ -24,7 +24,8 @@ struct SampleArgs {
   int32_t* n_kept;                      // [B] or null
   float* processed;                     // [B, V] or null
   // workspace
-  float* zp;                            // [B, V] processed logits
+  float* zp;                            // [B, zs] processed logits
+  int64_t zs;                           // row stride of zp: V rounded up to 64
   float* chunk_max;                     // [B, C]
   int32_t* chunk_arg;                   // [B, C]
   uint32_t* hist_count;                 // [B, kSampleHist]

@@ -44,7 +44,7 @@ constexpr int kNB = kSampleBuckets;
 constexpr int kHist = kSampleHist;                  // 4096 buckets, then 64 sums of 64 buckets
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelPer = 8;                          // loads in flight per thread in a select pass
+constexpr int kSelPer = 4;                          // 16-byte loads in flight per thread in a select pass
 constexpr int kCap = kSampleCap;
 constexpr float kFltMax = 3.4028235e38f;
 typedef unsigned long long u64;
@@ -94,6 +94,16 @@ __device__ __forceinline__ bool better(float v, int a, float bv, int ba) {
 __device__ __forceinline__ u64 wave_sum_u64(u64 x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ u64 wave_incl_scan(u64 x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const u64 y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
   return x;
 }
 
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
       }
     }
   }
-  float* Z = a.zp + (int64_t)b * a.V;
+  float* Z = a.zp + (int64_t)b * a.zs;
   float* O = a.processed ? a.processed + (int64_t)b * a.V : nullptr;
   float best = 0.f;
   int arg = -1;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
     hm[i] = 0ull;
   }
   __syncthreads();
-  const float* Z = a.zp + (int64_t)b * a.V;
+  const float* Z = a.zp + (int64_t)b * a.zs;
   const int v0 = c * kSampleChunk + tid;
   float z[kPer];
 #pragma unroll
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs 
   __syncthreads();
   if (s_nb > (u64)kCap) return;                     // the select launch takes the radix path
   const uint32_t klb = s_blb << 20;
-  const float* Z = a.zp + (int64_t)b * a.V;
+  const float* Z = a.zp + (int64_t)b * a.zs;
   const int v0 = c * kSampleChunk + tid;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -469,24 +479,24 @@ __device__ void block_scan3(SelShared& S, const u64 (&x)[3], u64 (&excl)[3], u64
   __syncthreads();
 }
 
-// f(v, z, valid) over ids [lo, hi), kSelPer loads in flight per thread; every
-// lane of every wave calls f the same number of times (ballots and wave
-// reductions allowed).  Thread t sees v = lo + v0 + j * 1024 + t: the lanes
-// of a wave hold 64 consecutive ids.
+// f(j, v, z) over ids [lo, hi) (lo a multiple of 4) in 16-byte loads, z
+// holding ids v .. v+3 (those >= hi are not ids: callers test v + e < hi);
+// kSelPer loads in flight per thread; every lane of every wave calls f the
+// same number of times (ballots and wave reductions allowed).  Thread t
+// sees v = v0 + 4 (j * 1024 + t): the lanes of a wave hold 256 consecutive
+// ids and the workgroup 4096 (one chunk) per j.  Rows of z' are padded to a
+// multiple of 64 floats, so a load that starts below hi stays in the row.
 template <class F>
 __device__ __forceinline__ void row_pass(const float* Z, int lo, int hi, F f) {
-  for (int v0 = lo; v0 < hi; v0 += kSelPer * kSelThreads) {
-    float z[kSelPer];
+  for (int v0 = lo; v0 < hi; v0 += kSelPer * 4 * kSelThreads) {
+    f32x4 z[kSelPer];
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) {
-      const int v = v0 + j * kSelThreads + (int)threadIdx.x;
-      z[j] = v < hi ? Z[v] : -INFINITY;
+      const int v = v0 + 4 * (j * kSelThreads + (int)threadIdx.x);
+      z[j] = v < hi ? *reinterpret_cast<const f32x4*>(Z + v) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) {
-      const int v = v0 + j * kSelThreads + (int)threadIdx.x;
-      f(j, v, z[j], v < hi);
-    }
+    for (int j = 0; j < kSelPer; ++j) f(j, v0 + 4 * (j * kSelThreads + (int)threadIdx.x), z[j]);
   }
 }
 
@@ -536,13 +546,16 @@ __device__ void level_pass(SelShared& S, const float* Z, int V, float m, float c
     S.u.h.m[i] = 0ull;
   }
   __syncthreads();
-  row_pass(Z, 0, V, [&](int, int, float z, bool valid) {
-    const uint32_t k = fkey(z);
-    if (valid && (k >> prefix_shift) == prefix) {
-      const uint32_t d = (k >> digit_shift) & digit_mask;
-      atomicAdd(&S.u.h.c[d], 1u);
-      const u64 q = fixed_mass(rel_weight(z, m, cT));
-      if (q) atomicAdd(&S.u.h.m[d], q);
+  row_pass(Z, 0, V, [&](int, int v, f32x4 z4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = fkey(z4[e]);
+      if (v + e < V && (k >> prefix_shift) == prefix) {
+        const uint32_t d = (k >> digit_shift) & digit_mask;
+        atomicAdd(&S.u.h.c[d], 1u);
+        const u64 q = fixed_mass(rel_weight(z4[e], m, cT));
+        if (q) atomicAdd(&S.u.h.m[d], q);
+      }
     }
   });
   __syncthreads();
@@ -572,21 +585,27 @@ __device__ void descend(SelShared& S, const float* Z, int V, float m, float cT, 
   __syncthreads();
 }
 
-// The draw inside ids [lo, hi) (hi - lo <= 4096 * 64): the first id whose key
-// is >= Ks and whose cumulative kept mass from lo exceeds t (t below the
-// range's kept mass).  Kept masses per run of 64 ids, a scan over the runs,
-// then one wave's scan of the run holding t.  Returns the id (-1 if t is not
-// below the range's kept mass); *kept gets the range's kept count.
+// The draw inside ids [lo, hi) (lo a multiple of 4, hi - lo <= 4096 * 256):
+// the first id whose key is >= Ks and whose cumulative kept mass from lo
+// exceeds t (t below the range's kept mass).  Kept masses per run of 256
+// ids (one wave's load), a scan over the runs, then one wave's scan of the
+// run holding t.  Returns the id (-1 if t is not below the range's kept
+// mass); *kept gets the range's kept count.
 __device__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t Ks, float m, float cT, u64 t,
                           int* kept) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ng = (hi - lo + 63) / 64;
+  const int ng = (hi - lo + 255) / 256;
   uint32_t nk = 0;
-  row_pass(Z, lo, hi, [&](int, int v, float z, bool valid) {
-    const bool in = valid && fkey(z) >= Ks;
-    nk += in ? 1u : 0u;
-    const u64 s = wave_sum_u64(in ? fixed_mass(rel_weight(z, m, cT)) : 0ull);
-    if (lane == 0 && v < lo + 64 * ng) S.u.grp[(v - lo) >> 6] = s;
+  row_pass(Z, lo, hi, [&](int, int v, f32x4 z4) {
+    u64 q = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = v + e < hi && fkey(z4[e]) >= Ks;
+      nk += in ? 1u : 0u;
+      q += in ? fixed_mass(rel_weight(z4[e], m, cT)) : 0ull;
+    }
+    const u64 s = wave_sum_u64(q);
+    if (lane == 0 && v < hi) S.u.grp[(v - lo) >> 8] = s;
   });
   if (tid == 0) {
     S.idx = -1;
@@ -615,18 +634,28 @@ __device__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t
   }
   __syncthreads();
   if (wave == 0 && S.idx >= 0) {
-    const int g = S.idx;
-    const int v = lo + 64 * g + lane;
-    const float z = v < hi ? Z[v] : -INFINITY;
-    const bool in = v < hi && fkey(z) >= Ks;
-    u64 inc = in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
+    const int v = lo + 256 * S.idx + 4 * lane;
+    const f32x4 z4 = v < hi ? *reinterpret_cast<const f32x4*>(Z + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    u64 q[4], own = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const u64 y = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += y;
+    for (int e = 0; e < 4; ++e) {
+      const bool in = v + e < hi && fkey(z4[e]) >= Ks;
+      q[e] = in ? fixed_mass(rel_weight(z4[e], m, cT)) : 0ull;
+      own += q[e];
+    }
+    const u64 inc = wave_incl_scan(own);
+    u64 c = S.val + inc - own;                    // kept mass before this lane's ids
+    int first = 3;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      u64 ce = c;
+      for (int f = 0; f <= e; ++f) ce += q[f];
+      if (ce > t) first = e;
     }
     const u64 over = __ballot(S.val + inc > t);
-    if (lane == 0) S.res_token = over ? lo + 64 * g + (int)(__ffsll((long long)over) - 1) : -1;
+    const int L = over ? (int)(__ffsll((long long)over) - 1) : 0;
+    const int id = __shfl(v + first, L, 64);
+    if (lane == 0) S.res_token = over ? id : -1;
   }
   if (tid == 0 && S.idx < 0) S.res_token = -1;
   __syncthreads();
@@ -734,15 +763,6 @@ __device__ __forceinline__ void wave_sort_desc(u64 (&x)[R]) {
       }
     }
   }
-}
-__device__ __forceinline__ u64 wave_incl_scan(u64 x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const u64 y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
 }
 // Element e (wave-uniform) of a wave-held array.
 template <int R>
@@ -924,18 +944,17 @@ __device__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V
   if (tid < C) S.cm[tid] = 0ull;
   __syncthreads();
   uint32_t nk = 0;
-  constexpr int kJPerChunk = kSampleChunk / kSelThreads;   // 4 loads of a thread share a chunk
-  u64 part = 0;
-  row_pass(Z, 0, V, [&](int j, int v, float z, bool valid) {
-    const bool in = valid && fkey(z) >= Ks;
-    nk += in ? 1u : 0u;
-    part += in ? fixed_mass(rel_weight(z, m, cT)) : 0ull;
-    if ((j % kJPerChunk) == kJPerChunk - 1) {
-      const u64 s = wave_sum_u64(part);
-      part = 0;
-      const int c = (v - j * kSelThreads - tid) / kSampleChunk + j / kJPerChunk;
-      if (lane == 0 && s && c < C) atomicAdd(&S.cm[c], s);
+  row_pass(Z, 0, V, [&](int j, int v, f32x4 z4) {
+    u64 q = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = v + e < V && fkey(z4[e]) >= Ks;
+      nk += in ? 1u : 0u;
+      q += in ? fixed_mass(rel_weight(z4[e], m, cT)) : 0ull;
     }
+    const u64 s = wave_sum_u64(q);
+    const int c = v / kSampleChunk;             // one j of the workgroup is one chunk
+    if (lane == 0 && s && c < C) atomicAdd(&S.cm[c], s);
   });
   u64 x[3] = {0, (u64)nk, 0}, ex[3], tot[3];
   block_scan3(S, x, ex, tot);
@@ -981,7 +1000,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a
   }
   if (ok && !greedy && fabsf(m) <= kFltMax) {
     const int V = a.V;
-    const float* Z = a.zp + (int64_t)b * V;
+    const float* Z = a.zp + (int64_t)b * a.zs;
     const float cT = temp_coef(P.temperature);
     const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
     const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;

@@ -819,7 +819,7 @@ SampleLayout sample_layout(int B, int V) {
   SampleLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
-  L.zp = take((size_t)B * V * 4);
+  L.zp = take((size_t)B * (((size_t)V + 63) / 64 * 64) * 4);
   L.cmax = take((size_t)B * C * 4);
   L.carg = take((size_t)B * C * 4);
   L.hcount = take((size_t)B * kSampleHist * 4);
@@ -881,6 +881,7 @@ int sample_tokens(const float* logits, int B, int V, int64_t logits_stride, cons
   a.n_kept = n_kept;
   a.processed = processed;
   a.zp = reinterpret_cast<float*>(w + L.zp);
+  a.zs = ((int64_t)V + 63) / 64 * 64;
   a.chunk_max = reinterpret_cast<float*>(w + L.cmax);
   a.chunk_arg = reinterpret_cast<int32_t*>(w + L.carg);
   a.hist_count = reinterpret_cast<uint32_t*>(w + L.hcount);
