@@ -566,7 +566,7 @@ hipError_t launch_d(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
 #define SA_PFB64 2, 4
 #endif
 #ifndef SA_PFB96
-#define SA_PFB96 2, 4
+#define SA_PFB96 1, 8
 #endif
 #ifndef SA_PFB128
 #define SA_PFB128 2, 8
