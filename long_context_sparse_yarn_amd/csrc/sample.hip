@@ -69,12 +69,22 @@ __device__ __forceinline__ u64 mass_of_key(uint32_t k, float m, float c) {
 }
 
 // The smallest key whose weight reaches min_p (0 < min_p <= 1): the
-// maximum's weight is 1 and -inf's is 0, so bisection between them.
+// maximum's weight is 1 and -inf's is 0; weights rise with the key, so a
+// search between them: each round the 64 lanes of a wave test 64 evenly
+// spaced keys of (lo, hi] and keep the sub-interval where the test first
+// passes (about six rounds for 32-bit keys).  Every wave that calls it gets
+// the same key.  Call from one whole wave.
 __device__ __forceinline__ uint32_t minp_key(float m, float c, float min_p) {
-  uint32_t lo = fkey(-INFINITY), hi = fkey(m);
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t lo = fkey(-INFINITY), hi = fkey(m);     // weight(lo) < min_p <= weight(hi)
   while (hi - lo > 1) {
-    const uint32_t mid = lo + (hi - lo) / 2;
-    if (rel_weight(fval(mid), m, c) >= min_p) hi = mid; else lo = mid;
+    const uint32_t step = (hi - lo + 63) / 64;
+    const uint32_t k = min(hi, lo + step * (lane + 1));
+    const u64 pass = __ballot(rel_weight(fval(k), m, c) >= min_p);
+    const int f = pass ? (int)(__ffsll((long long)pass) - 1) : 63;
+    const uint32_t nhi = min(hi, lo + step * (uint32_t)(f + 1));
+    lo = f == 0 ? lo : lo + step * (uint32_t)f;
+    hi = nhi;
   }
   return hi;
 }
