@@ -10,27 +10,32 @@
 // processed logit z': top-k the largest key whose count at or above it
 // reaches k, top-p the largest key whose mass at or above it reaches
 // ceil(top_p * top-k mass), min-p the smallest key whose weight reaches
-// min_p (weights are monotone in the key: bisection).  Masses are integers,
-// q = floor(e * 2^40) with e = 2^((z' - m) log2(e) / T) <= 1, so every sum
-// is exact and the result does not depend on scheduling.
+// min_p (weights are monotone in the key, so a search finds it).  Masses
+// are integers, q = floor(e * 2^40) with e = 2^((z' - m) log2(e) / T) <= 1,
+// so every sum is exact and the result does not depend on scheduling.
 //
-// Three launches per call:
-//  1. prep (grid chunks x rows, the whole chip): z' stored once, per-chunk
-//     maximum and its lowest id; clears the row's histogram and candidate
-//     counter.  The only pass over the inputs in HBM.
+// Four launches per call:
+//  1. prep (grid chunks of 4096 x rows, the whole chip): z' stored once,
+//     per-chunk maximum and its lowest id; clears the row's histogram and
+//     candidate counter.  The only pass over the inputs in HBM.
 //  2. histogram (chunks x rows): a 4096-bucket histogram (counts, masses) of
 //     the key's top 12 bits in LDS, added into the row's global one with
-//     integer atomics; when min-p is on, the tokens at or above the min-p key
-//     are also gathered into a per-row candidate list.
-//  3. select (one 1024-thread workgroup per row): greedy rows take the
-//     merged argmax.  Otherwise the kept set is finished in LDS when it lies
-//     in a small ranking prefix: the min-p candidates of launch 2, or the
-//     tokens above a bound read off the histogram, gathered in one pass; the
-//     candidates are sorted (bitonic, key then id), the thresholds read off
-//     their prefix masses, and the kept ones re-sorted by id for the draw.
-//     Otherwise two more radix levels (12 + 8 bits, one pass each over z' in
-//     L2) give each threshold, and the draw sums the kept mass of every run
-//     of 64 ids, scans those sums, and scans the one run holding the target.
+//     integer atomics, plus 64 sums of 64 buckets and each chunk's mass;
+//     when min-p is on, the tokens at or above the min-p key are gathered
+//     into the row's candidate list.
+//  3. gather (chunks x rows), rows with top-k or top-p and no min-p: one
+//     wave reads the bucket of the k-th token or of the top-p crossing off
+//     the histogram; when at most 4096 tokens lie at or above it, every
+//     chunk adds its share to the candidate list.
+//  4. select (one 1024-thread workgroup per row): greedy rows take the
+//     merged argmax.  Candidates (a prefix of the ranking that holds the
+//     kept set) are sorted by key then id (one wave in registers up to 256,
+//     a bitonic sort in LDS beyond), the thresholds read off their prefix
+//     masses, and the kept ones re-sorted by id for the draw.  Without any
+//     truncation the chunk masses locate the draw.  Larger kept sets take
+//     two more radix levels (12 + 8 bits, one pass each over z') per
+//     threshold, then per-chunk kept masses and one scan of the chunk that
+//     holds the target.
 #pragma clang fp contract(off)
 
 #include "sa_device.h"
@@ -730,15 +735,6 @@ __device__ void cand_prefix(SelShared& S, int n, F mass_of) {
   }
   __syncthreads();
 }
-
-// Thresholds over a ranking prefix that holds the kept set (candidates,
-// sorted): a threshold that falls below the candidates is not the binding
-// one.  key(e), cum(e): key and inclusive mass of the e-th candidate.
-struct Thresholds {
-  uint32_t Ks;
-  u64 qn;
-  int nk;
-};
 
 // Bitonic sort, descending, of the 64 R values a wave holds, element
 // i = 64 r + lane in x[r]: partners 64 or more apart sit in one lane,
