@@ -34,6 +34,7 @@ struct SampleArgs {
   uint32_t* ncand;                      // [B]
   unsigned long long* chunk_mass;       // [B, C] mass of each chunk
   int B, V, C;
+  int hist_cpw;                         // chunks per histogram workgroup
   int update_counts;
 };
 

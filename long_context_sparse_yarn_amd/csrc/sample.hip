@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
 
 // ------------------------------------------------------------- histogram
 __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a) {
-  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const sa_sample_params P = a.params[b];
   if (!params_ok(P, a.u[b]) || P.temperature == 0.f) return;
   __shared__ float rmv;
@@ -254,48 +254,55 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
   const uint32_t km = gather ? minp_key(m, cT, P.min_p) : 0u;
   __shared__ uint32_t hc[kNB];
   __shared__ u64 hm[kNB];
+  __shared__ u64 wq[2][kPrepThreads / 64];
   for (int i = tid; i < kNB; i += kPrepThreads) {
     hc[i] = 0u;
     hm[i] = 0ull;
   }
   __syncthreads();
   const float* Z = a.zp + (int64_t)b * a.zs;
-  const int v0 = c * kSampleChunk + tid;
-  float z[kPer];
+  // this workgroup's chunks: hist_cpw consecutive chunks of the row (one
+  // histogram in LDS and one flush for all of them)
+  const int c_end = min(a.C, ((int)blockIdx.x + 1) * a.hist_cpw);
+  for (int c = (int)blockIdx.x * a.hist_cpw; c < c_end; ++c) {
+    const int v0 = c * kSampleChunk + tid;
+    float z[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
-    z[j] = v < a.V ? Z[v] : 0.f;
-  }
-  u64 qsum = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
-    const uint32_t k = fkey(z[j]);
-    if (v < a.V) {
-      atomicAdd(&hc[k >> 20], 1u);
-      const u64 q = fixed_mass(rel_weight(z[j], m, cT));
-      qsum += q;
-      if (q) atomicAdd(&hm[k >> 20], q);
+    for (int j = 0; j < kPer; ++j) {
+      const int v = v0 + j * kPrepThreads;
+      z[j] = v < a.V ? Z[v] : 0.f;
     }
-    if (gather) {
-      const bool take = v < a.V && k >= km;
-      const u64 mask = __ballot(take);
-      if (mask) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
-        base = __shfl(base, 0, 64);
-        const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-        if (take && slot < (uint32_t)kCap)
-          a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+    u64 qsum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int v = v0 + j * kPrepThreads;
+      const uint32_t k = fkey(z[j]);
+      if (v < a.V) {
+        atomicAdd(&hc[k >> 20], 1u);
+        const u64 q = fixed_mass(rel_weight(z[j], m, cT));
+        qsum += q;
+        if (q) atomicAdd(&hm[k >> 20], q);
+      }
+      if (gather) {
+        const bool take = v < a.V && k >= km;
+        const u64 mask = __ballot(take);
+        if (mask) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
+          base = __shfl(base, 0, 64);
+          const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+          if (take && slot < (uint32_t)kCap)
+            a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+        }
       }
     }
+    // the chunk's mass (two buffers: a wave may start the next chunk while
+    // thread 0 still reads this one's)
+    qsum = wave_sum_u64(qsum);
+    if (lane == 0) wq[c & 1][tid >> 6] = qsum;
+    __syncthreads();
+    if (tid == 0) a.chunk_mass[(int64_t)b * a.C + c] = wq[c & 1][0] + wq[c & 1][1] + wq[c & 1][2] + wq[c & 1][3];
   }
-  qsum = wave_sum_u64(qsum);
-  __shared__ u64 wq[kPrepThreads / 64];
-  if (lane == 0) wq[tid >> 6] = qsum;
-  __syncthreads();
-  if (tid == 0) a.chunk_mass[(int64_t)b * a.C + c] = wq[0] + wq[1] + wq[2] + wq[3];
   for (int i = tid; i < kNB; i += kPrepThreads) {
     if (hc[i]) atomicAdd(&a.hist_count[(int64_t)b * kHist + i], hc[i]);
     if (hm[i]) atomicAdd(&a.hist_mass[(int64_t)b * kHist + i], hm[i]);
@@ -1103,10 +1110,18 @@ __global__ __launch_bounds__(256) void sample_count_kernel(const int32_t* ids, i
 
 }  // namespace
 
-hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+#ifndef SA_HIST_WGS
+#define SA_HIST_WGS 384
+#endif
+hipError_t launch_sample(const SampleArgs& args, hipStream_t s) {
+  SampleArgs a = args;
+  // several chunks per histogram workgroup once the batch gives more than
+  // SA_HIST_WGS workgroups (one and a half per CU; swept 128-768), up to 8
+  a.hist_cpw = max(1, min(8, (a.B * a.C) / SA_HIST_WGS));
   const dim3 grid(a.C, a.B);
   hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepThreads), 0, s, a);
-  hipLaunchKernelGGL(sample_hist_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_hist_kernel, dim3((a.C + a.hist_cpw - 1) / a.hist_cpw, a.B), dim3(kPrepThreads), 0, s,
+                     a);
   hipLaunchKernelGGL(sample_gather_kernel, grid, dim3(kPrepThreads), 0, s, a);
   hipLaunchKernelGGL(sample_select_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();

@@ -235,3 +235,13 @@ def test_strided_rows_through_the_c_abi():
             want, _, keep = _oracle_row(d["logits"][b], d["bias"][:V], np.zeros(V, np.int64), rows[b], d["u"][b])
             assert int(tok[b]) == want
             assert int(kept[b]) == (int(keep.sum()) if keep is not None else 1)
+
+
+def test_large_batch_several_chunks_per_histogram_workgroup():
+    """96 rows of the full vocabulary: the histogram launch gives each
+    workgroup several chunks of a row; every path (min-p candidates, gather,
+    radix levels, chunk-mass draw, greedy) in one batch."""
+    B = 96
+    rows = [dict(r) for r in (MIXED + [_params(**PAGE)]) * (B // (len(MIXED) + 1) + 1)][:B]
+    d = sampling_inputs(B, SAMPLE_V, seed=13, scale=1.5)
+    _check(d["logits"], rows, d["u"], max_near=2)
