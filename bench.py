@@ -122,6 +122,10 @@ def run_layer(L, w, sa, ev=None):
         ev[1].record()
 
 
+STEP_STATS = {}       # median and min of the timed steps (ms), from the last time_prefill_step
+IN_STEP_STATS = {}    # per layer: median and min of its in-step prefill launch (ms)
+
+
 def time_prefill_step(w, sa, torch, steps, warmup):
     layers = [Layer(w, i, sa, torch) for i in range(len(w.windows))]
     for _ in range(warmup):
@@ -130,16 +134,21 @@ def time_prefill_step(w, sa, torch, steps, warmup):
     torch.cuda.synchronize()
     evs = {i: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)] for i in range(len(layers))}
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]   # step boundaries
     torch.cuda.synchronize()
-    t0.record()
+    marks[0].record()
     for s in range(steps):
         for i, L in enumerate(layers):
             run_layer(L, w, sa, evs[i][s])
-    t1.record()
+        marks[s + 1].record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / steps
+    per_step = [marks[s].elapsed_time(marks[s + 1]) for s in range(steps)]
+    STEP_STATS.update(median=float(np.median(per_step)), min=float(np.min(per_step)))
     in_step = {i: float(np.mean([a.elapsed_time(b) for a, b in evs[i]])) for i in evs}
+    IN_STEP_STATS.clear()
+    IN_STEP_STATS.update({i: (float(np.median([a.elapsed_time(b) for a, b in evs[i]])),
+                              float(np.min([a.elapsed_time(b) for a, b in evs[i]]))) for i in evs})
     # Kernel durations: an event pair around one launch also spans its
     # dispatch and completion (several microseconds), so each layer's prefill
     # is also timed over KERNEL_REPEAT back-to-back launches on the step's
@@ -638,6 +647,10 @@ def main():
     fl_step = sum(attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window) for L in layers)
     value = fl_step / (ms_step * 1e-3) / 1e12
     per_layer = [prefill_figures(w, L, kern_ms[i], in_step[i]) for i, L in enumerate(layers)]
+    for i, p in enumerate(per_layer):
+        p["kernel_ms_in_step_median"] = round(IN_STEP_STATS[i][0], 4)
+        p["kernel_ms_in_step_min"] = round(IN_STEP_STATS[i][1], 4)
+    step_stats = dict(STEP_STATS)
     full = [p for p in per_layer if p["window"] == 0][0]
     full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
     roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
@@ -651,7 +664,9 @@ def main():
     line = {
         "metric": "sink-GQA attention prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(step_stats["median"], 4), "ms_per_step_min": round(step_stats["min"], 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "global_batch": w.B, "seq_len": w.T, "n_q": w.n_q,
                    "n_kv": w.n_kv, "d_h": w.d_h, "windows": list(w.windows),
