@@ -608,8 +608,16 @@ def cpu_baseline(w, layers, budget_s):
     est = t_rope + t_attn * (fl_total / fl_sample)
     info = threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] + [1])
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(fl_total / est / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": "fp64 numpy oracle: RoPE of all Q and K of both layers (%.2f s) plus "
                       "attention of %d seeded random query rows (all heads, %.2f s, %.3g of the "
                       "step's flops); whole-step time extrapolated by flops" % (
