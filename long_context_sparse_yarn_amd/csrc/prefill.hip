@@ -50,6 +50,12 @@
 #ifndef SA_VALU_LEAD
 #define SA_VALU_LEAD 0
 #endif
+// 1: where it pays (d = 96 with two N tiles per wave), each unit's LDS
+// operands (K for its scores, V for its PV) are read during the previous
+// unit's vector work; 0: always at the start of the unit.
+#ifndef SA_OPS_AHEAD
+#define SA_OPS_AHEAD 1
+#endif
 
 
 namespace {
@@ -97,6 +103,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   constexpr int DT = D / 16;          // coordinate tiles of O^T
   constexpr int KBUF = kTile * k_pitch<D>();
   constexpr bool kPhaseSplit = D != 64;
+  // Reading a unit's operands one unit ahead costs registers: 3% faster for
+  // d = 96 full-causal blocks (212 VGPRs, still two waves per SIMD); d = 64
+  // would drop from three waves per SIMD to two (12% slower) and the d = 96
+  // band shape loses its third wave (20% slower).
+  constexpr bool kOpsAhead = SA_OPS_AHEAD && D == 96 && NT >= 2;
 
   constexpr int VBUF = 2 * D * 32;
   // one LDS arena: three K tiles, three V^T tiles (and, before the first
@@ -383,6 +394,40 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(A, Pk[n], O[dt][n]);
     }
   };
+  // A unit's LDS operands held in registers: the K rows of its scores (KS
+  // steps x 2 M tiles, from K buffer kb, half kh) and the V^T rows of its PV
+  // (DT tiles, from V buffer vb, half vh).  Read one unit ahead, their LDS
+  // latency hides behind the previous unit's vector work.
+  struct Ops { u32x4 k[KS][2]; u32x4 v[DT]; };
+  auto load_ops = [&](Ops& o, int kb, int kh, int vb, int vh) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int mt = 2 * kh + mm;
+        o.k[ks][mm] = ld16(&Kb(kb)[ka[ks] + k_pitch<D>() * (4 * (mt & 1) + 32 * (mt >> 1))]);
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o.v[dt] = ld16(&Vb(vb)[va_off + (vh * D + 16 * dt) * 32]);
+  };
+  auto scores_ops = [&](Scores& S, const Ops& o) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) S.v[mm][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S.v[mm][n] = mfma16x16x32(o.k[ks][mm], qop[n][ks], S.v[mm][n]);
+  };
+  auto pv_ops = [&](const Ops& o, const u32x4 (&Pk)[NT]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(o.v[dt], Pk[n], O[dt][n]);
+  };
   // Move the reference to the true running max (column max across the four
   // lanes of a query) and rescale what has been accumulated.
   auto rescale = [&](const Scores& S) {
@@ -461,17 +506,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // S(u) can be recomputed from K buffer kbc, half hc, first key k0c.  The
   // mask of S(u+1), where it needs one, is applied in place after the main
   // stretch.
+  // oc: this unit's operands (read ahead); on: filled here with the next
+  // unit's, from K buffer kbx half hx and V buffer vbx half vx.
   auto unit = [&](const Scores& Sc, Scores& Sn, const u32x4 (&Pp)[NT], u32x4 (&Pc)[NT],
+                  const Ops& oc, Ops& on, int kbx, int hx, int vbx, int vx,
                   int kbn, int hn, int k0n, int vbp, int hp, int kbc, int hc, int k0c,
                   bool mask_next) {
     float ls[NT];
-    scores(Sn, kbn, hn);
-    pv(vbp, hp, Pp);
+    if constexpr (kOpsAhead) {
+      scores_ops(Sn, oc);
+      pv_ops(oc, Pp);
+    } else {
+      scores(Sn, kbn, hn);
+      pv(vbp, hp, Pp);
+    }
     // d = 96 and 128 run two waves per SIMD: keeping each unit's MFMAs ahead
-    // of its vector work lets one wave's MFMA stretch overlap the other
-    // wave's vector stretch (measured 5% faster at d = 96; d = 64, with
-    // three waves per SIMD, is faster mixed).
+    // of its vector work (measured 5% faster at d = 96; d = 64, with three
+    // waves per SIMD, is faster mixed).
     if constexpr (kPhaseSplit) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kOpsAhead) load_ops(on, kbx, hx, vbx, vx);
     probs(Sc, Pc, ls);
     interleave();
     bool bad = false;
@@ -491,15 +544,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
     if (mask_next) apply_mask(Sn, k0n);
   };
+  // operands of unit 2 t0: K(t0) half 1, V(t0-1) half 1 (zeros)
+  Ops OA, OB;
+  if constexpr (kOpsAhead) load_ops(OA, 0, 1, 2, 1);
   for (int t = t0; t <= t_last; ++t) {
     if (t + 2 <= t_last) load_k(b2, t + 2);
     if (t + 1 <= t_last) load_v(b1, t + 1);
     const int k0 = t * kTile;
-    // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1
-    unit(S0, S1, P1, P0, b0, 1, k0 + 32, b2, 1, b0, 0, k0, need_mask(k0 + 32));
+    // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1.  It
+    // reads ahead the operands of unit 2t+1: K(t+1) half 0, V(t) half 0.
+    unit(S0, S1, P1, P0, OA, OB, b1, 0, b0, 0, b0, 1, k0 + 32, b2, 1, b0, 0, k0, need_mask(k0 + 32));
     // unit 2t+1: S(2t+2) from K(t+1) half 0 (a throw-away after the last
-    // tile); P(2t) with V(t) half 0
-    unit(S1, S0, P0, P1, b1, 0, k0 + kTile, b0, 0, b0, 1, k0 + 32,
+    // tile); P(2t) with V(t) half 0.  It reads ahead the operands of unit
+    // 2t+2: K(t+1) half 1 and V(t) half 1, which the loads of tile t+1 (into
+    // the buffers of K(t) and V(t-1)) leave in place; after the last tile
+    // they are stale and unused.
+    unit(S1, S0, P0, P1, OB, OA, b1, 1, b0, 1, b1, 0, k0 + kTile, b0, 0, b0, 1, k0 + 32,
          t < t_last && need_mask(k0 + kTile));
     wait_vmem();
     __syncthreads();
