@@ -245,3 +245,28 @@ def test_large_batch_several_chunks_per_histogram_workgroup():
     rows = [dict(r) for r in (MIXED + [_params(**PAGE)]) * (B // (len(MIXED) + 1) + 1)][:B]
     d = sampling_inputs(B, SAMPLE_V, seed=13, scale=1.5)
     _check(d["logits"], rows, d["u"], max_near=2)
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23, 24])
+def test_random_settings_sweep(seed):
+    """16 rows of random settings (temperature, top-k, top-p, min-p, the three
+    penalties, bias on or off) over a random vocabulary size, bf16-rounded or
+    fp32 logits: every row against the oracle."""
+    rng = np.random.default_rng(seed)
+    V = int(rng.integers(300, 40000))
+    B = 16
+    d = sampling_inputs(B, V, seed=seed, scale=float(rng.uniform(0.5, 4.0)), history=200,
+                        bf16_logits=bool(seed % 2))
+    counts = np.stack([token_counts(h, V) for h in d["history"]])
+    rows = []
+    for _ in range(B):
+        T = 0.0 if rng.random() < 0.15 else float(rng.uniform(0.05, 2.5))
+        rows.append(_params(temperature=T,
+                            top_k=int(rng.choice([0, 1, 5, 50, 500, V // 2, V + 3])),
+                            top_p=float(rng.choice([1.0, 0.5, 0.9, 0.99, 0.999])),
+                            min_p=float(rng.choice([0.0, 0.0, 0.01, 0.1, 0.5])),
+                            repetition=float(rng.choice([1.0, 1.2, 0.9])),
+                            presence=float(rng.choice([0.0, 0.3, -0.2])),
+                            frequency=float(rng.choice([0.0, 0.05]))))
+    bias = d["bias"][:V] if seed % 3 else None
+    _check(d["logits"], rows, d["u"], bias=bias, counts=counts, max_near=1)
