@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
 # valid only for the kernel sources it was measured on.
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "9de1b4e1f468c8fb", "bytes": 89068893}
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "4e5972fbb100dc4f", "bytes": 89516394}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_attn.h", "sa_rope.h")   # what the prefill kernel is built from
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
