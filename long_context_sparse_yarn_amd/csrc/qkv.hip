@@ -34,7 +34,16 @@
 namespace {
 
 constexpr int kThreads = sa_gemm::kThreads;   // 8 waves: 2 feature halves x 4 token quarters
-constexpr int kTM = sa_gemm::kTM;             // tokens per workgroup
+// Tokens per workgroup by head dimension (256 or 128; overridable for tuning).
+#ifndef SA_QKV_TM64
+#define SA_QKV_TM64 256
+#endif
+#ifndef SA_QKV_TM96
+#define SA_QKV_TM96 128
+#endif
+#ifndef SA_QKV_TM128
+#define SA_QKV_TM128 256
+#endif
 
 // tab[t][i] = (c cos, c sin)(pos0 + t) * inv_freq_i), fp64
 __global__ __launch_bounds__(kThreads) void rope_table_kernel(QkvArgs a) {
@@ -54,12 +63,15 @@ __device__ __forceinline__ float round_bf16(float x) {
   return __uint_as_float(pack_bf16x2(x, 0.f) << 16);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, int n_mt) {
+// 128-token tiles take half the LDS, so two workgroups can share a CU when
+// the registers fit (<= 128 per lane): ask for that occupancy.
+template <int D, int TM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TM == 128 ? 4 : 1)))
+void qkv_rope_append_kernel(QkvArgs a, int n_mt) {
   constexpr int HPW = D == 64 ? 4 : 2;  // heads per workgroup
   constexpr int F = HPW * D;            // features per workgroup (256, 192, 256)
   constexpr int HW = HPW / 2;           // heads per wave
-  using G = sa_gemm::Gemm<F>;
+  using G = sa_gemm::Gemm<F, TM>;
   constexpr int TT = G::TT;
   __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_ELEMS];
 
@@ -70,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
   const int M = a.B * a.T;
   const int H = a.n_q + 2 * a.n_kv;             // heads of the fused width
   const int dqkv = H * D;
-  const int m0 = mt * kTM, f0 = nt * F;
+  const int m0 = mt * TM, f0 = nt * F;
 
   // element offsets of the chunks this lane stages; rows past the ends are
   // clamped (their results are never stored)
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const int m = m0 + 64 * wt + 16 * t + j;
+      const int m = m0 + G::TQ * wt + 16 * t + j;
       if (m >= M) continue;
       const int b = m / a.T, tt = m - b * a.T;
       const int64_t crow = a.row0 + tt;             // cache row of this token
@@ -170,14 +182,14 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(QkvArgs a, in
   }
 }
 
-template <int D>
+template <int D, int TM>
 hipError_t launch_d(const QkvArgs& a, hipStream_t s) {
   constexpr int HPW = D == 64 ? 4 : 2;
   const int M = a.B * a.T;
-  const int n_mt = (M + kTM - 1) / kTM;
+  const int n_mt = (M + TM - 1) / TM;
   const int H = a.n_q + 2 * a.n_kv;
   const int n_nt = (H + HPW - 1) / HPW;
-  hipLaunchKernelGGL(qkv_rope_append_kernel<D>, dim3((unsigned)(n_mt * n_nt)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((qkv_rope_append_kernel<D, TM>), dim3((unsigned)(n_mt * n_nt)), dim3(kThreads), 0,
                      s, a, n_mt);
   return hipGetLastError();
 }
@@ -192,9 +204,9 @@ hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (a.d) {
-    case 64: return launch_d<64>(a, s);
-    case 96: return launch_d<96>(a, s);
-    case 128: return launch_d<128>(a, s);
+    case 64: return launch_d<64, SA_QKV_TM64>(a, s);
+    case 96: return launch_d<96, SA_QKV_TM96>(a, s);
+    case 128: return launch_d<128, SA_QKV_TM128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

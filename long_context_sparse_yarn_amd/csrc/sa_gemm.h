@@ -1,18 +1,18 @@
 // The matrix-core GEMM core shared by the fused qkv projection and the MoE
-// expert layers: C^T (F features x 256 tokens) = W x^T over a contraction of
+// expert layers: C^T (F features x TM tokens) = W x^T over a contraction of
 // K elements, both operands contiguous along K (a linear layer's [out, in]
 // weight rows and the tokens' rows), for a workgroup of 8 waves.
 //
-//  * 64-wide slices of the F weight rows and the 256 token rows go global ->
+//  * 64-wide slices of the F weight rows and the TM token rows go global ->
 //    LDS with 16-byte global_load_lds (no staging registers): slot l of a
 //    1 KB block receives one 16-byte chunk; chunk c of row r sits at slot
 //    c ^ (r & 7), so the operand reads below are free of bank conflicts.
 //    Where the rows come from is the caller's: it hands in, per lane, the
-//    element offset of the chunk it fetches (GemmSlots tells which row and
-//    chunk that is), so tokens can be gathered through an index list.
+//    element offset of the chunk it fetches (w_slot / x_slot tell which row
+//    and chunk that is), so tokens can be gathered through an index list.
 //  * Two LDS stages, one barrier per stage.
 //  * Wave (wf, wt) = (wave & 1, wave >> 1) owns features [F/2 wf, +F/2) and
-//    tokens [64 wt, +64); v_mfma_f32_16x16x32_bf16 leaves lane l with
+//    tokens [TM/4 wt, +TM/4); v_mfma_f32_16x16x32_bf16 leaves lane l with
 //    features 16 f + 4 (l / 16) + r (r < 4) of token 16 t + (l % 16) of its
 //    part in acc[f][t][r].
 #pragma once
@@ -32,16 +32,17 @@ __device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* ld
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <int F>
+template <int F, int TM = kTM>
 struct Gemm {
   static constexpr int WBUF = F * kKS;            // elements per stage
-  static constexpr int XBUF = kTM * kKS;
+  static constexpr int XBUF = TM * kKS;
   static constexpr int LDS_ELEMS = 2 * (WBUF + XBUF);
   static constexpr int WBLK = F * 8 / 64;         // 1 KB blocks per weight stage
-  static constexpr int XBLK = kTM * 8 / 64;
+  static constexpr int XBLK = TM * 8 / 64;
   static constexpr int WBW = WBLK / kWaves, XBW = XBLK / kWaves;   // blocks per wave
   static constexpr int FT = F / 2 / 16;           // 16-feature tiles per wave
-  static constexpr int TT = 4;                    // 16-token tiles per wave
+  static constexpr int TQ = TM / 4;               // tokens per wave
+  static constexpr int TT = TQ / 16;              // 16-token tiles per wave
   static_assert(WBLK % kWaves == 0 && XBLK % kWaves == 0, "blocks split evenly over the waves");
 
   // Row (within the F weight rows, or the 256 tokens) and 16-byte chunk
@@ -71,7 +72,7 @@ struct Gemm {
     };
     // rows of a lane's tiles differ by multiples of 16, so r & 7 = j & 7
     const int swz = j & 7;
-    const int wrow0 = (F / 2) * wf + j, xrow0 = 64 * wt + j;
+    const int wrow0 = (F / 2) * wf + j, xrow0 = TQ * wt + j;
 #pragma unroll
     for (int f = 0; f < FT; ++f)
 #pragma unroll
