@@ -30,9 +30,10 @@ struct SampleArgs {
   int32_t* chunk_arg;                   // [B, C]
   uint32_t* hist_count;                 // [B, kSampleHist]
   unsigned long long* hist_mass;        // [B, kSampleHist]
-  unsigned long long* cand;             // [B, kSampleCap] tokens at or above the min-p key
+  unsigned long long* cand;             // [B, kSampleCap] candidates (key << 32 | ~id)
   uint32_t* ncand;                      // [B]
   unsigned long long* chunk_mass;       // [B, C] mass of each chunk
+  unsigned long long* chunk_kmass;      // [B, C] mass of each chunk above the edge bucket
   int B, V, C;
   int hist_cpw;                         // chunks per histogram workgroup
   int update_counts;

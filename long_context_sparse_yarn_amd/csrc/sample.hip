@@ -122,6 +122,44 @@ __device__ __forceinline__ u64 wave_incl_scan(u64 x) {
   return x;
 }
 
+// Appends to the row's candidate list the entries (key << 32 | ~id) of this
+// thread's kPer ids whose take bit is set.  Same-address atomics serialize
+// in L2, so the workgroup reserves all of its slots with one atomic: each
+// wave counts its ids by ballot, thread 0 adds the waves' counts to the
+// row's counter, and each wave writes from its offset.  Call from the whole
+// workgroup (kPrepThreads threads); s holds kPrepThreads / 64 + 1 words.
+__device__ __forceinline__ void append_candidates(const SampleArgs& a, int b, const uint32_t (&key)[kPer],
+                                                  const int (&id)[kPer], const bool (&take)[kPer], uint32_t* s) {
+  constexpr int kWaves = kPrepThreads / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const u64 below = (1ull << lane) - 1ull;
+  u64 mask[kPer];
+  uint32_t n = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    mask[j] = __ballot(take[j]);
+    n += (uint32_t)__popcll(mask[j]);
+  }
+  if (lane == 0) s[w] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) tot += s[i];
+    s[kWaves] = tot ? atomicAdd(&a.ncand[b], tot) : 0u;
+  }
+  __syncthreads();
+  if (n == 0) return;                                 // wave-uniform
+  uint32_t base = s[kWaves];
+  for (int i = 0; i < w; ++i) base += s[i];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t slot = base + (uint32_t)__popcll(mask[j] & below);
+    if (take[j] && slot < (uint32_t)kCap) a.cand[(int64_t)b * kCap + slot] = ((u64)key[j] << 32) | (uint32_t)~(uint32_t)id[j];
+    base += (uint32_t)__popcll(mask[j]);
+  }
+}
+
 // Row maximum and its lowest id from the per-chunk results: wave 0 loads
 // them (C <= 64) and reduces; every thread gets the result through LDS.
 __device__ __forceinline__ void row_max(const SampleArgs& a, int b, float* m, int* arg, float* sv, int* si) {
@@ -255,6 +293,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
   __shared__ uint32_t hc[kNB];
   __shared__ u64 hm[kNB];
   __shared__ u64 wq[2][kPrepThreads / 64];
+  __shared__ uint32_t s_app[kPrepThreads / 64 + 1];
   for (int i = tid; i < kNB; i += kPrepThreads) {
     hc[i] = 0u;
     hm[i] = 0ull;
@@ -273,29 +312,24 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
       z[j] = v < a.V ? Z[v] : 0.f;
     }
     u64 qsum = 0;
+    uint32_t key[kPer];
+    int id[kPer];
+    bool take[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int v = v0 + j * kPrepThreads;
       const uint32_t k = fkey(z[j]);
+      key[j] = k;
+      id[j] = v;
+      take[j] = gather && v < a.V && k >= km;
       if (v < a.V) {
         atomicAdd(&hc[k >> 20], 1u);
         const u64 q = fixed_mass(rel_weight(z[j], m, cT));
         qsum += q;
         if (q) atomicAdd(&hm[k >> 20], q);
       }
-      if (gather) {
-        const bool take = v < a.V && k >= km;
-        const u64 mask = __ballot(take);
-        if (mask) {
-          uint32_t base = 0;
-          if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
-          base = __shfl(base, 0, 64);
-          const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-          if (take && slot < (uint32_t)kCap)
-            a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
-        }
-      }
     }
+    if (gather) append_candidates(a, b, key, id, take, s_app);
     // the chunk's mass (two buffers: a wave may start the next chunk while
     // thread 0 still reads this one's)
     qsum = wave_sum_u64(qsum);
@@ -331,6 +365,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_hist_kernel(SampleArgs a)
 struct Pick {
   uint32_t digit;             // bucket at which the running weight reaches the target
   u64 cnt_above, mass_above;  // counts and masses of the buckets above it
+  u64 cnt_at;                 // count of the bucket itself
 };
 
 __device__ __forceinline__ void wave_scan3(u64& w, u64& c, u64& m) {
@@ -350,7 +385,7 @@ __device__ __forceinline__ void wave_scan3(u64& w, u64& c, u64& m) {
 // from the top down, the bucket at which the running count (by_mass: mass)
 // first reaches target (target <= the total): first over the 64 sums, then
 // over the 64 buckets of the one that reaches it.  Call from one whole wave.
-__device__ Pick wave_pick(const uint32_t* cnt, const u64* mass, bool by_mass, u64 target) {
+__device__ __forceinline__ Pick wave_pick(const uint32_t* cnt, const u64* mass, bool by_mass, u64 target) {
   const int lane = threadIdx.x & 63;
   const u64 cc = cnt[kNB + 63 - lane], cm = mass[kNB + 63 - lane], cw = by_mass ? cm : cc;
   u64 iw = cw, ic = cc, im = cm;
@@ -369,25 +404,47 @@ __device__ Pick wave_pick(const uint32_t* cnt, const u64* mass, bool by_mass, u6
   p.digit = (uint32_t)(64 * sup + 63 - L2);
   p.cnt_above = ac + __shfl(jc - fc, L2, 64);
   p.mass_above = am + __shfl(jm - fm, L2, 64);
+  p.cnt_at = __shfl(fc, L2, 64);
   return p;
 }
 
 // Lower bound (bucket) on the keys of the kept set when top-k or top-p is on
-// and min-p is off, and how many tokens lie at or above it: top-k's bucket,
-// or top-p's bucket on the whole mass; with both on, top-k's bucket (the
-// top-k mass needs every token above the k-th).  Call from one whole wave.
-__device__ void wave_bound(const uint32_t* cnt, const u64* mass, const sa_sample_params& P, int V, u64 q_all,
-                           uint32_t* blb, u64* nb) {
+// and min-p is off: top-k's bucket, or top-p's bucket on the whole mass;
+// with both on, top-k's bucket (the top-k mass needs every token above the
+// k-th).  nb counts the tokens at or above the bucket; cnt_above and
+// mass_above those above it, cnt_at those in it.
+struct Bound {
+  uint32_t blb;
+  u64 nb, cnt_above, mass_above, cnt_at;
+};
+
+// Call from one whole wave.
+__device__ __forceinline__ Bound wave_bound(const uint32_t* cnt, const u64* mass, const sa_sample_params& P, int V, u64 q_all) {
   const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f;
+  Bound bd;
   if (!kA && !pA) {
-    *blb = 0;
-    *nb = (u64)V;
-    return;
+    bd.blb = 0;
+    bd.nb = (u64)V;
+    bd.cnt_above = bd.mass_above = bd.cnt_at = 0;
+    return bd;
   }
   const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)q_all));
   const Pick p = wave_pick(cnt, mass, !kA, kA ? (u64)P.top_k : tau);
-  *blb = p.digit;
-  *nb = p.cnt_above + cnt[p.digit];
+  bd.blb = p.digit;
+  bd.nb = p.cnt_above + p.cnt_at;
+  bd.cnt_above = p.cnt_above;
+  bd.mass_above = p.mass_above;
+  bd.cnt_at = p.cnt_at;
+  return bd;
+}
+
+// Min-p off, exactly one of top-k and top-p on, too many tokens at or above
+// the bound for the candidate list but few enough in the bound's bucket:
+// the list holds that bucket only (the edge of the kept set), the
+// histogram gives what lies above it.
+__device__ __forceinline__ bool edge_mode(const sa_sample_params& P, int V, const Bound& bd) {
+  const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f;
+  return !(P.min_p > 0.f) && kA != pA && bd.nb > (u64)kCap && bd.cnt_at <= (u64)kCap;
 }
 
 // The row's total mass from the per-chunk sums (one whole wave).
@@ -399,48 +456,69 @@ __device__ __forceinline__ u64 wave_row_mass(const SampleArgs& a, int b) {
 // ---------------------------------------------------------------- gather
 // Rows with top-k or top-p on and min-p off: the tokens at or above the
 // bucket bound, when there are at most 4096 of them, go to the row's
-// candidate list, every chunk in its own workgroup.
+// candidate list; in edge mode the tokens in the bound's bucket do, and
+// each chunk's mass above the bucket goes to chunk_kmass.  Every chunk in
+// its own workgroup.
 __global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs a) {
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const sa_sample_params P = a.params[b];
   if (!params_ok(P, a.u[b]) || P.temperature == 0.f || P.min_p > 0.f) return;
   if (!(P.top_k > 0 && P.top_k < a.V) && !(P.top_p < 1.f)) return;
-  __shared__ float rmv;
-  __shared__ int rmi;
-  __shared__ uint32_t s_blb;
-  __shared__ u64 s_nb;
-  float m;
-  int arg;
-  row_max(a, b, &m, &arg, &rmv, &rmi);
-  if (!(fabsf(m) <= kFltMax)) return;
-  if (tid < 64) {
-    const u64 q_all = wave_row_mass(a, b);
-    uint32_t blb;
-    u64 nb;
-    wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, a.V, q_all, &blb, &nb);
-    if (tid == 0) {
-      s_blb = blb;
-      s_nb = nb;
-    }
-  }
-  __syncthreads();
-  if (s_nb > (u64)kCap) return;                     // the select launch takes the radix path
-  const uint32_t klb = s_blb << 20;
+  // (a row without a finite maximum has no histogram; whatever is gathered
+  // for it, the select launch does not read it)
+  __shared__ Bound s_bd;
+  __shared__ float s_m;
+  __shared__ u64 s_q[kPrepThreads / 64];
   const float* Z = a.zp + (int64_t)b * a.zs;
   const int v0 = c * kSampleChunk + tid;
+  float z[kPer];                                     // in flight while the bound is found
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int v = v0 + j * kPrepThreads;
-    const uint32_t k = v < a.V ? fkey(Z[v]) : 0u;
-    const bool take = v < a.V && k >= klb;
-    const u64 mask = __ballot(take);
-    if (mask) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&a.ncand[b], (uint32_t)__popcll(mask));
-      base = __shfl(base, 0, 64);
-      const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-      if (take && slot < (uint32_t)kCap) a.cand[(int64_t)b * kCap + slot] = ((u64)k << 32) | (uint32_t)~(uint32_t)v;
+    z[j] = v < a.V ? Z[v] : 0.f;
+  }
+  if (tid < 64) {
+    const bool in = lane < a.C;
+    const u64 cm = in ? a.chunk_mass[(int64_t)b * a.C + lane] : 0ull;
+    float mx = in ? a.chunk_max[(int64_t)b * a.C + lane] : -INFINITY;
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft, 64));
+    const Bound bd =
+        wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, a.V, wave_sum_u64(cm));
+    if (tid == 0) {
+      s_bd = bd;
+      s_m = mx;
     }
+  }
+  __syncthreads();
+  const Bound bd = s_bd;
+  const bool edge = edge_mode(P, a.V, bd);
+  if (bd.nb > (u64)kCap && !edge) return;           // the select launch takes the radix path
+  uint32_t key[kPer];
+  int id[kPer];
+  bool take[kPer];
+  u64 q = 0;
+  const float m = s_m, cT = temp_coef(P.temperature);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + j * kPrepThreads;
+    key[j] = fkey(z[j]);
+    id[j] = v;
+    const uint32_t d = key[j] >> 20;
+    take[j] = v < a.V && (edge ? d == bd.blb : d >= bd.blb);
+    if (edge && v < a.V && d > bd.blb) q += fixed_mass(rel_weight(z[j], m, cT));
+  }
+  __shared__ uint32_t s_app[kPrepThreads / 64 + 1];
+  if (edge) {
+    q = wave_sum_u64(q);
+    if (lane == 0) s_q[tid >> 6] = q;              // read after append's barriers
+  }
+  append_candidates(a, b, key, id, take, s_app);
+  if (edge && tid == 0) {
+    u64 t = 0;
+#pragma unroll
+    for (int i = 0; i < kPrepThreads / 64; ++i) t += s_q[i];
+    a.chunk_kmass[(int64_t)b * a.C + c] = t;
   }
 }
 
@@ -467,13 +545,13 @@ struct SelShared {
   u64 val;
   float rmv;
   int rmi;
-  uint32_t blb;
-  u64 nb;
+  uint32_t nlisted;
+  Bound bd;
   int res_token, res_kept;
 };
 
 // Exclusive prefix sums over the workgroup's threads of three values, and totals.
-__device__ void block_scan3(SelShared& S, const u64 (&x)[3], u64 (&excl)[3], u64 (&tot)[3]) {
+__device__ __forceinline__ void block_scan3(SelShared& S, const u64 (&x)[3], u64 (&excl)[3], u64 (&tot)[3]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   u64 inc[3] = {x[0], x[1], x[2]};
 #pragma unroll
@@ -526,33 +604,34 @@ __device__ __forceinline__ void row_pass(const float* Z, int lo, int hi, F f) {
 // the weight (count or mass) of the buckets at and above it first reaches
 // target.  S.digit gets it; S.add_cnt / S.add_mass the counts and masses of
 // the buckets above it.  The caller guarantees that the target is reached.
-__device__ void pick_digit(SelShared& S, const uint32_t* cnt, const u64* mass, int NB, bool by_mass,
+__device__ __forceinline__ void pick_digit(SelShared& S, const uint32_t* cnt, const u64* mass, int NB, bool by_mass,
                            u64 target, u64 above_w) {
   const int t = threadIdx.x;
-  u64 cw[4], cc[4], cm[4];
+  uint32_t cc[4];
+  u64 cm[4];
   u64 x[3] = {0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pos = 4 * t + i;
-    cc[i] = pos < NB ? cnt[NB - 1 - pos] : 0;
-    cm[i] = pos < NB ? mass[NB - 1 - pos] : 0;
-    cw[i] = by_mass ? cm[i] : cc[i];
-    x[0] += cw[i];
+    cc[i] = pos < NB ? cnt[NB - 1 - pos] : 0u;
+    cm[i] = pos < NB ? mass[NB - 1 - pos] : 0ull;
     x[1] += cc[i];
     x[2] += cm[i];
   }
+  x[0] = by_mass ? x[2] : x[1];
   u64 ex[3], tot[3];
   if (t == 0) S.digit = 0;
   block_scan3(S, x, ex, tot);
   u64 run = above_w + ex[0], rc = ex[1], rm = ex[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (run < target && run + cw[i] >= target) {
+    const u64 w = by_mass ? cm[i] : (u64)cc[i];
+    if (run < target && run + w >= target) {
       S.digit = (uint32_t)(NB - 1 - (4 * t + i));
       S.add_cnt = rc;
       S.add_mass = rm;
     }
-    run += cw[i];
+    run += w;
     rc += cc[i];
     rm += cm[i];
   }
@@ -561,7 +640,7 @@ __device__ void pick_digit(SelShared& S, const uint32_t* cnt, const u64* mass, i
 
 // One pass over z': histogram of (key >> digit_shift) & digit_mask over the
 // keys with key >> prefix_shift == prefix.
-__device__ void level_pass(SelShared& S, const float* Z, int V, float m, float cT, uint32_t prefix,
+__device__ __forceinline__ void level_pass(SelShared& S, const float* Z, int V, float m, float cT, uint32_t prefix,
                            int prefix_shift, int digit_shift, uint32_t digit_mask) {
   for (int i = threadIdx.x; i < kNB; i += kSelThreads) {
     S.u.h.c[i] = 0u;
@@ -586,7 +665,7 @@ __device__ void level_pass(SelShared& S, const float* Z, int V, float m, float c
 // The largest key K whose tokens at or above it have count (by_mass: mass)
 // >= target (target <= the row's total), with the mass at or above K.
 // Level 1 from S.c1/m1; levels 2 (12 bits) and 3 (8 bits) by passes over z'.
-__device__ void descend(SelShared& S, const float* Z, int V, float m, float cT, bool by_mass, u64 target,
+__device__ __forceinline__ void descend(SelShared& S, const float* Z, int V, float m, float cT, bool by_mass, u64 target,
                         uint32_t* K, u64* mass_ge) {
   pick_digit(S, S.c1, S.m1, kNB, by_mass, target, 0);
   const uint32_t d1 = S.digit;
@@ -613,7 +692,7 @@ __device__ void descend(SelShared& S, const float* Z, int V, float m, float cT, 
 // ids (one wave's load), a scan over the runs, then one wave's scan of the
 // run holding t.  Returns the id (-1 if t is not below the range's kept
 // mass); *kept gets the range's kept count.
-__device__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t Ks, float m, float cT, u64 t,
+__device__ __forceinline__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t Ks, float m, float cT, u64 t,
                           int* kept) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ng = (hi - lo + 255) / 256;
@@ -687,7 +766,7 @@ __device__ int draw_range(SelShared& S, const float* Z, int lo, int hi, uint32_t
 }
 
 // In-place bitonic sort, descending, of S.u.cand.key[0, n), n a power of two.
-__device__ void sort_desc(SelShared& S, int n) {
+__device__ __forceinline__ void sort_desc(SelShared& S, int n) {
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < n; i += kSelThreads) {
@@ -713,7 +792,7 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 }
 
 // Pads S.u.cand.key[n, 2^ceil(log2 n)) with 0 (sorts last) and sorts.
-__device__ void pad_sort(SelShared& S, int n) {
+__device__ __forceinline__ void pad_sort(SelShared& S, int n) {
   const int np = pow2_at_least(max(n, 2));
   for (int i = n + (int)threadIdx.x; i < np; i += kSelThreads) S.u.cand.key[i] = 0ull;
   __syncthreads();
@@ -722,7 +801,7 @@ __device__ void pad_sort(SelShared& S, int n) {
 
 // Inclusive prefix over the first n candidates of mass_of(e) into S.u.cand.cum.
 template <class F>
-__device__ void cand_prefix(SelShared& S, int n, F mass_of) {
+__device__ __forceinline__ void cand_prefix(SelShared& S, int n, F mass_of) {
   u64 q[4];
   u64 x[3] = {0, 0, 0};
 #pragma unroll
@@ -827,7 +906,7 @@ __device__ __forceinline__ int wave_count(F pred) {
 // sorts, thresholds and draws in registers, with no barrier.  Call from one
 // whole wave.
 template <int R>
-__device__ int finish_in_wave(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
+__device__ __forceinline__ int finish_in_wave(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
                               float m, float cT, u64 q_all, uint32_t Km, int* kept) {
   const int lane = threadIdx.x & 63;
   u64 x[R], cum[R];
@@ -868,13 +947,14 @@ __device__ int finish_in_wave(SelShared& S, int n, bool kA, bool pA, const sa_sa
 // The candidates S.u.cand.key[0, n) (key << 32 | ~id) are every token at or
 // above some key, a prefix of the ranking that holds the kept set.  Returns
 // the token (and the kept count in *kept), or -1.
-__device__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
+__device__ __forceinline__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sample_params& P, float u,
                              float m, float cT, u64 q_all, uint32_t Km, int* kept) {
-  if (n <= 256) {
+  if (n <= 256) {                    // one wave, in registers (64, 128 or 256 slots)
     if (threadIdx.x < 64) {
       int k = 0;
-      const int t = n <= 64 ? finish_in_wave<1>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k)
-                            : finish_in_wave<4>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k);
+      const int t = n <= 64    ? finish_in_wave<1>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k)
+                    : n <= 128 ? finish_in_wave<2>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k)
+                               : finish_in_wave<4>(S, n, kA, pA, P, u, m, cT, q_all, Km, &k);
       if (threadIdx.x == 0) {
         S.res_token = t;
         S.res_kept = k;
@@ -939,7 +1019,7 @@ __device__ int finish_in_lds(SelShared& S, int n, bool kA, bool pA, const sa_sam
 }
 
 // Candidates from the row's list in the workspace into LDS, then finish.
-__device__ int finish_from_list(SelShared& S, const SampleArgs& a, int b, int n, bool kA, bool pA,
+__device__ __forceinline__ int finish_from_list(SelShared& S, const SampleArgs& a, int b, int n, bool kA, bool pA,
                                 const sa_sample_params& P, float u, float m, float cT, u64 q_all, uint32_t Km,
                                 int* kept) {
   for (int i = threadIdx.x; i < n; i += kSelThreads) S.u.cand.key[i] = a.cand[(int64_t)b * kCap + i];
@@ -947,10 +1027,29 @@ __device__ int finish_from_list(SelShared& S, const SampleArgs& a, int b, int n,
   return finish_in_lds(S, n, kA, pA, P, u, m, cT, q_all, Km, kept);
 }
 
+// The chunk that holds the draw, from lane c's kept mass cmv of chunk c
+// (c < C): t = floor(u * total), below the total; S.idx gets the first
+// chunk whose running mass exceeds t and S.val t minus the mass before it.
+// Call from wave 0 (the whole wave).
+__device__ __forceinline__ void pick_chunk(SelShared& S, u64 cmv, int C, float u) {
+  const int lane = threadIdx.x & 63;
+  const u64 inc = wave_incl_scan(cmv);
+  const u64 qn = __shfl(inc, 63, 64);
+  u64 t = (u64)((double)u * (double)qn);
+  if (t >= qn) t = qn - 1;
+  const u64 hit = __ballot(lane < C && inc > t);
+  const int c = hit ? (int)(__ffsll((long long)hit) - 1) : 0;
+  const u64 before = __shfl(inc, c, 64) - __shfl(cmv, c, 64);
+  if (lane == 0) {
+    S.idx = c;
+    S.val = t - before;
+  }
+}
+
 // The draw over the whole row for kept = key >= Ks: kept mass per chunk of
 // 4096 ids (one wave sum per chunk per wave), the chunk that holds the
 // target, then draw_range inside it.
-__device__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V, uint32_t Ks, float m, float cT,
+__device__ __forceinline__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V, uint32_t Ks, float m, float cT,
                         float u, int* kept) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int C = a.C;
@@ -972,20 +1071,7 @@ __device__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V
   u64 x[3] = {0, (u64)nk, 0}, ex[3], tot[3];
   block_scan3(S, x, ex, tot);
   const int kept_all = (int)tot[1];
-  if (tid < 64) {
-    const u64 cmv = tid < C ? S.cm[tid] : 0ull;
-    const u64 inc = wave_incl_scan(cmv);
-    const u64 qn = __shfl(inc, 63, 64);
-    u64 t = (u64)((double)u * (double)qn);
-    if (t >= qn) t = qn - 1;
-    const u64 hit = __ballot(tid < C && inc > t);
-    const int c = hit ? (int)(__ffsll((long long)hit) - 1) : 0;
-    const u64 before = __shfl(inc, c, 64) - __shfl(cmv, c, 64);   // the whole wave takes part
-    if (tid == 0) {
-      S.idx = c;
-      S.val = t - before;
-    }
-  }
+  if (tid < 64) pick_chunk(S, tid < C ? S.cm[tid] : 0ull, C, u);
   __syncthreads();
   const int c = S.idx;
   const u64 t_in = S.val;
@@ -996,108 +1082,204 @@ __device__ int draw_row(SelShared& S, const SampleArgs& a, const float* Z, int V
   return token;
 }
 
+// Edge mode: the row's list holds every token of the bound's bucket bd.blb
+// (n <= 4096, four per thread, kept in registers); the histogram gives the
+// count and mass above the bucket and the gather launch each chunk's mass
+// above it.  Two radix levels over the bucket's low 20 key bits (10 + 10,
+// bins in c1 / m1, unused here) place the threshold exactly: the k-th key,
+// or the key at which the running mass reaches top-p's share.  The kept
+// tokens of the bucket add their masses to their chunks, and the draw runs
+// inside the chunk that holds it.
+__device__ __forceinline__ int finish_edge(SelShared& S, const SampleArgs& a, int b, int n, const Bound& bd, bool kA,
+                           const sa_sample_params& P, float u, float m, float cT, u64 q_all, const float* Z, int V,
+                           int* kept) {
+  constexpr int R = kCap / kSelThreads;
+  constexpr int kLow = 1024;                        // bins per level
+  const int tid = threadIdx.x, C = a.C;
+  const u64* x = S.u.cand.key;                      // masses recomputed where needed
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = tid + r * kSelThreads;
+    if (e < n) S.u.cand.key[e] = a.cand[(int64_t)b * kCap + e];
+  }
+  for (int i = tid; i < kLow; i += kSelThreads) {
+    S.c1[i] = 0u;
+    S.m1[i] = 0ull;
+  }
+  if (tid < C) S.cm[tid] = a.chunk_kmass[(int64_t)b * C + tid];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t k = (uint32_t)(x[tid + r * kSelThreads] >> 32);
+    if (tid + r * kSelThreads < n) {
+      const uint32_t d = (k >> 10) & (kLow - 1);
+      const u64 q = mass_of_key(k, m, cT);
+      atomicAdd(&S.c1[d], 1u);
+      if (q) atomicAdd(&S.m1[d], q);
+    }
+  }
+  __syncthreads();
+  const bool by_mass = !kA;
+  const u64 target = kA ? (u64)P.top_k : max(1ull, (u64)ceil((double)P.top_p * (double)q_all));
+  const u64 above = by_mass ? bd.mass_above : bd.cnt_above;
+  pick_digit(S, S.c1, S.m1, kLow, by_mass, target, above);
+  const uint32_t d1 = S.digit;
+  u64 ac = S.add_cnt, am = S.add_mass;
+  __syncthreads();
+  for (int i = tid; i < kLow; i += kSelThreads) {
+    S.c1[i] = 0u;
+    S.m1[i] = 0ull;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t k = (uint32_t)(x[tid + r * kSelThreads] >> 32);
+    if (tid + r * kSelThreads < n && ((k >> 10) & (kLow - 1)) == d1) {
+      const u64 q = mass_of_key(k, m, cT);
+      atomicAdd(&S.c1[k & (kLow - 1)], 1u);
+      if (q) atomicAdd(&S.m1[k & (kLow - 1)], q);
+    }
+  }
+  __syncthreads();
+  pick_digit(S, S.c1, S.m1, kLow, by_mass, target, above + (by_mass ? am : ac));
+  const uint32_t d2 = S.digit;
+  ac += S.add_cnt + S.c1[d2];                       // the bucket's kept count
+  const uint32_t Ks = (bd.blb << 20) | (d1 << 10) | d2;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t k = (uint32_t)(x[tid + r * kSelThreads] >> 32);
+    if (tid + r * kSelThreads < n && k >= Ks) {
+      const u64 q = mass_of_key(k, m, cT);
+      if (q) atomicAdd(&S.cm[(int)~(uint32_t)x[tid + r * kSelThreads] / kSampleChunk], q);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) pick_chunk(S, tid < C ? S.cm[tid] : 0ull, C, u);
+  __syncthreads();
+  const int c = S.idx;
+  const u64 t_in = S.val;
+  __syncthreads();
+  int k_unused;
+  const int token = draw_range(S, Z, c * kSampleChunk, min(V, (c + 1) * kSampleChunk), Ks, m, cT, t_in, &k_unused);
+  *kept = (int)(bd.cnt_above + ac);
+  return token;
+}
+
 __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(SampleArgs a) {
   __shared__ SelShared S;
   const int b = blockIdx.x, tid = threadIdx.x;
   const sa_sample_params P = a.params[b];
   const float u = a.u[b];
-  int token = -1, kept = 0;
-  float m;
-  int arg;
-  row_max(a, b, &m, &arg, &S.rmv, &S.rmi);
+  // the row maximum and its lowest id, the row's total mass and its listed
+  // candidates, in one round trip by wave 0 (the mass is meaningful only for
+  // rows the histogram launch processed)
+  if (tid < 64) {
+    float bv = tid < a.C ? a.chunk_max[(int64_t)b * a.C + tid] : 0.f;
+    int ba = tid < a.C ? a.chunk_arg[(int64_t)b * a.C + tid] : -1;
+    const u64 cm = tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull;
+    const uint32_t nl = a.ncand[b];
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+      const float ov = __shfl_xor(bv, sft, 64);
+      const int oa = __shfl_xor(ba, sft, 64);
+      if (better(ov, oa, bv, ba)) {
+        bv = ov;
+        ba = oa;
+      }
+    }
+    const u64 total = wave_sum_u64(cm);
+    if (tid == 0) {
+      S.rmv = bv;
+      S.rmi = ba;
+      S.val = total;
+      S.nlisted = nl;
+    }
+  }
+  __syncthreads();
+  const int arg = S.rmi;
+  const float m = arg >= 0 ? S.rmv : -INFINITY;
+  const u64 q_all = S.val;             // the row's total mass
+  const uint32_t listed = S.nlisted;
+  __syncthreads();
+  // each path stores its result as soon as it has it (nothing stays live
+  // across the other paths' code)
+  auto emit = [&](int token, int kept) {
+    if (tid == 0) {
+      a.tokens[b] = token;
+      if (a.n_kept) a.n_kept[b] = token >= 0 ? kept : 0;
+      if (a.update_counts && a.counts && token >= 0) a.counts[(int64_t)b * a.V + token] += 1;
+    }
+  };
   const bool ok = params_ok(P, u);
-  const bool greedy = ok && P.temperature == 0.f;
-  if (greedy && arg >= 0) {
-    token = arg;
-    kept = 1;
+  if (ok && P.temperature == 0.f) {                 // greedy
+    emit(arg, 1);
+    return;
   }
-  if (ok && !greedy && fabsf(m) <= kFltMax) {
-    const int V = a.V;
-    const float* Z = a.zp + (int64_t)b * a.zs;
-    const float cT = temp_coef(P.temperature);
-    const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
-    const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;
+  if (!ok || !(fabsf(m) <= kFltMax)) {
+    emit(-1, 0);
+    return;
+  }
+  const int V = a.V;
+  const float* Z = a.zp + (int64_t)b * a.zs;
+  const float cT = temp_coef(P.temperature);
+  const bool kA = P.top_k > 0 && P.top_k < V, pA = P.top_p < 1.f, mA = P.min_p > 0.f;
+  const uint32_t Km = mA ? minp_key(m, cT, P.min_p) : 0u;
+  int kept;
+  // one call site per finish (each inlines a large body)
+  int n_list = -1;
+  if (mA && listed <= (uint32_t)kCap && !(kA && pA && (int)listed < P.top_k)) {
+    n_list = (int)listed;                           // the min-p candidates of the histogram launch
+  } else if (!mA && !kA && !pA) {
+    // ---- no truncation: the chunk masses locate the draw
+    if (tid < 64) pick_chunk(S, tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull, a.C, u);
+    __syncthreads();
+    const int c = S.idx;
+    const u64 t_in = S.val;
+    __syncthreads();
+    int k_unused;
+    emit(draw_range(S, Z, c * kSampleChunk, min(V, (c + 1) * kSampleChunk), 0u, m, cT, t_in, &k_unused), V);
+    return;
+  } else if (!mA) {
     if (tid < 64) {
-      const u64 x = wave_row_mass(a, b);
-      if (tid == 0) S.val = x;
+      const Bound bd = wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, V, q_all);
+      if (tid == 0) S.bd = bd;
     }
     __syncthreads();
-    const u64 q_all = S.val;           // the row's total mass
-    __syncthreads();
-    const uint32_t listed = a.ncand[b];
-    bool done = false;
-    if (mA && listed <= (uint32_t)kCap && !(kA && pA && (int)listed < P.top_k)) {
-      // ---- the min-p candidates gathered by the histogram launch
-      token = finish_from_list(S, a, b, (int)listed, kA, pA, P, u, m, cT, q_all, Km, &kept);
-      done = true;
-    } else if (!mA && !kA && !pA) {
-      // ---- no truncation: the chunk masses locate the draw
-      if (tid < 64) {
-        const u64 cmv = tid < a.C ? a.chunk_mass[(int64_t)b * a.C + tid] : 0ull;
-        const u64 inc = wave_incl_scan(cmv);
-        u64 t = (u64)((double)u * (double)q_all);
-        if (t >= q_all) t = q_all - 1;
-        const u64 hit = __ballot(tid < a.C && inc > t);
-        const int c = hit ? (int)(__ffsll((long long)hit) - 1) : 0;
-        const u64 before = __shfl(inc, c, 64) - __shfl(cmv, c, 64);
-        if (tid == 0) {
-          S.idx = c;
-          S.val = t - before;
-        }
-      }
-      __syncthreads();
-      const int c = S.idx;
-      const u64 t_in = S.val;
-      __syncthreads();
-      int k_unused;
-      token = draw_range(S, Z, c * kSampleChunk, min(V, (c + 1) * kSampleChunk), 0u, m, cT, t_in, &k_unused);
-      kept = V;
-      done = true;
-    }
-    if (!done) {
-      if (!mA) {
-        if (tid < 64) {
-          uint32_t blb;
-          u64 nb;
-          wave_bound(a.hist_count + (int64_t)b * kHist, a.hist_mass + (int64_t)b * kHist, P, V, q_all, &blb,
-                     &nb);
-          if (tid == 0) {
-            S.blb = blb;
-            S.nb = nb;
-          }
-        }
-        __syncthreads();
-        if (S.nb <= (u64)kCap) {
-          // ---- gathered by the gather launch: every token at or above the bound
-          token = finish_from_list(S, a, b, (int)min(listed, (uint32_t)kCap), kA, pA, P, u, m, cT, q_all, Km,
-                                   &kept);
-          done = true;
-        }
-      }
-    }
-    if (!done) {
-      // ---- large kept set: radix levels over z', then the draw
-      for (int i = tid; i < kNB; i += kSelThreads) {
-        S.c1[i] = a.hist_count[(int64_t)b * kHist + i];
-        S.m1[i] = a.hist_mass[(int64_t)b * kHist + i];
-      }
-      __syncthreads();
-      uint32_t Kk = 0, Kp = 0;
-      u64 qk = q_all;
-      if (kA) descend(S, Z, V, m, cT, false, (u64)P.top_k, &Kk, &qk);
-      if (pA) {
-        const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
-        u64 unused;
-        descend(S, Z, V, m, cT, true, tau, &Kp, &unused);
-      }
-      token = draw_row(S, a, Z, V, max(max(Kk, Kp), Km), m, cT, u, &kept);
+    const Bound& bd = S.bd;                         // read from LDS where needed
+    if (bd.nb <= (u64)kCap) {
+      n_list = (int)min(listed, (uint32_t)kCap);    // every token at or above the bound
+    } else if (edge_mode(P, V, bd)) {
+      // ---- gathered by the gather launch: the bound's bucket
+      const int token = finish_edge(S, a, b, (int)min(listed, (uint32_t)kCap), bd, kA, P, u, m, cT, q_all, Z, V,
+                                    &kept);
+      emit(token, kept);
+      return;
     }
   }
-  if (tid == 0) {
-    a.tokens[b] = token;
-    if (a.n_kept) a.n_kept[b] = token >= 0 ? kept : 0;
-    if (a.update_counts && a.counts && token >= 0) a.counts[(int64_t)b * a.V + token] += 1;
+  if (n_list >= 0) {
+    // ---- a candidate list that holds the whole kept set
+    const int token = finish_from_list(S, a, b, n_list, kA, pA, P, u, m, cT, q_all, Km, &kept);
+    emit(token, kept);
+    return;
   }
+  // ---- large kept set: radix levels over z' (top-k's key, then top-p's
+  // on the top-k mass), then the draw
+  for (int i = tid; i < kNB; i += kSelThreads) {
+    S.c1[i] = a.hist_count[(int64_t)b * kHist + i];
+    S.m1[i] = a.hist_mass[(int64_t)b * kHist + i];
+  }
+  __syncthreads();
+  uint32_t Kk = 0, Kp = 0;
+  u64 qk = q_all;
+  if (kA) descend(S, Z, V, m, cT, false, (u64)P.top_k, &Kk, &qk);
+  if (pA) {
+    const u64 tau = max(1ull, (u64)ceil((double)P.top_p * (double)qk));
+    u64 unused;
+    descend(S, Z, V, m, cT, true, tau, &Kp, &unused);
+  }
+  const int token = draw_row(S, a, Z, V, max(max(Kk, Kp), Km), m, cT, u, &kept);
+  emit(token, kept);
 }
 
 __global__ __launch_bounds__(256) void sample_count_kernel(const int32_t* ids, int H, int64_t stride,

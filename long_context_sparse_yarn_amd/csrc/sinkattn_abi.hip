@@ -812,7 +812,7 @@ int moe_layer(const void* x, int N, int d_model, const void* w_router, int E, in
 
 namespace {
 struct SampleLayout {
-  size_t zp, cmax, carg, hcount, hmass, cand, ncand, rmass, total;
+  size_t zp, cmax, carg, hcount, hmass, cand, ncand, rmass, kmass, total;
 };
 SampleLayout sample_layout(int B, int V) {
   const size_t C = ((size_t)V + kSampleChunk - 1) / kSampleChunk;
@@ -827,6 +827,7 @@ SampleLayout sample_layout(int B, int V) {
   L.cand = take((size_t)B * kSampleCap * 8);
   L.ncand = take((size_t)B * 4);
   L.rmass = take((size_t)B * C * 8);
+  L.kmass = take((size_t)B * C * 8);
   L.total = o;
   return L;
 }
@@ -889,6 +890,7 @@ int sample_tokens(const float* logits, int B, int V, int64_t logits_stride, cons
   a.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
   a.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
   a.chunk_mass = reinterpret_cast<unsigned long long*>(w + L.rmass);
+  a.chunk_kmass = reinterpret_cast<unsigned long long*>(w + L.kmass);
   a.B = B;
   a.V = V;
   a.C = (V + kSampleChunk - 1) / kSampleChunk;

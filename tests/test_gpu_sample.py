@@ -29,9 +29,14 @@ sa = pytest.importorskip("long_context_sparse_yarn_amd")
 DELTA = 1e-5
 
 
+def _f32(x):
+    """The value a float field of sa_sample_params carries."""
+    return float(np.float32(x))
+
+
 def _oracle_row(z, bias, counts, p, u):
-    return sample(z, bias, counts, p["repetition"], p["presence"], p["frequency"], p["temperature"],
-                  p["top_k"], p["top_p"], p["min_p"], float(u))
+    return sample(z, bias, counts, p["repetition"], p["presence"], p["frequency"], _f32(p["temperature"]),
+                  p["top_k"], _f32(p["top_p"]), _f32(p["min_p"]), float(u))
 
 
 def _near_variants(z, bias, counts, p, u):
@@ -40,8 +45,8 @@ def _near_variants(z, bias, counts, p, u):
     for dp, dm, du in itertools.product((-1, 0, 1), repeat=3):
         q = dict(p)
         if q["top_p"] < 1.0:
-            q["top_p"] = min(1.0, q["top_p"] * (1 + dp * DELTA))
-        q["min_p"] = q["min_p"] * (1 + dm * DELTA)
+            q["top_p"] = min(1.0, _f32(q["top_p"]) * (1 + dp * DELTA))
+        q["min_p"] = _f32(q["min_p"]) * (1 + dm * DELTA)
         uu = min(max(float(u) + du * DELTA, 0.0), np.nextafter(1.0, 0.0))
         tok, _, keep = _oracle_row(z, bias, counts, q, uu)
         out.add((tok, int(keep.sum()) if keep is not None else (1 if tok >= 0 else 0)))
@@ -142,6 +147,32 @@ def test_large_kept_sets_take_the_radix_path(bf16):
     d = sampling_inputs(len(rows), SAMPLE_V, seed=6, scale=1.0, bf16_logits=bf16)
     tok, kept = _check(d["logits"], rows, d["u"])
     assert kept[0] >= 20000 and kept[3] == SAMPLE_V and kept[1] > 4096
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_edge_bucket_path(bf16):
+    """One truncation rule on, more than 4096 tokens at or above its bucket,
+    at most 4096 in the bucket itself (the full vocabulary, logits of scale
+    2): the bucket alone is gathered and sorted, the histogram and per-chunk
+    sums supply what lies above it, and the draw stays in one chunk."""
+    rows = [_params(temperature=1.0, top_p=0.9), _params(temperature=0.8, top_k=8000),
+            _params(temperature=1.5, top_p=0.99), _params(temperature=1.0, top_k=5000),
+            _params(temperature=0.6, top_p=0.97), _params(temperature=2.0, top_k=30000)]
+    d = sampling_inputs(len(rows), SAMPLE_V, seed=16, scale=2.0, bf16_logits=bf16)
+    tok, kept = _check(d["logits"], rows, d["u"])
+    assert kept[1] >= 8000 and kept[3] >= 5000 and kept[0] > 4096
+
+
+def test_dense_buckets_take_the_radix_path():
+    """Logits packed into a few buckets (1.5 + 0.05 N(0, 1)): the bound's
+    bucket holds more than 4096 tokens, so single-rule rows too descend the
+    radix levels."""
+    rows = [_params(temperature=1.0, top_p=0.9), _params(temperature=0.5, top_k=30000),
+            _params(temperature=0.05, top_p=0.5), _params(temperature=1.0, top_k=100)]
+    d = sampling_inputs(len(rows), SAMPLE_V, seed=17, scale=1.0)
+    logits = (1.5 + 0.05 * d["logits"]).astype(np.float32)
+    tok, kept = _check(logits, rows, d["u"])
+    assert kept[1] >= 30000 and kept[3] >= 100
 
 
 def test_ties_are_kept_whole():
