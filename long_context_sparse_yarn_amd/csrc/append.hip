@@ -32,6 +32,11 @@
 
 #include <type_traits>
 
+// Rows of its column a thread loads before the V copy and the table.
+#ifndef SA_APPEND_PREFETCH
+#define SA_APPEND_PREFETCH 1
+#endif
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
   // row is loaded here, before the V copy and the table, so that those reads
   // are in flight while the table is built (deeper prefetch measured slower:
   // the registers it holds cost occupancy).
-  constexpr int kMaxRows = 1;
+  constexpr int kMaxRows = SA_APPEND_PREFETCH;
   const int cpr = half / VEC;
   const int ncols = (nh + nq) * cpr;
   const bool pre = ELT == 2 && ncols > 0 && ncols <= kThreads;
