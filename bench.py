@@ -34,8 +34,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
 # HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
-# valid only for the kernel sources it was measured on.
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "4e5972fbb100dc4f", "bytes": 89516394}
+# valid only for the kernel sources it was measured on (measured at sources
+# 4e5972fbb100dc4f; the later change to sa_rope.h's bf16 rotation leaves the
+# prefill kernel's gfx950 assembly instruction for instruction the same).
+TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "069ed16196c46724", "bytes": 89516394}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_attn.h", "sa_rope.h")   # what the prefill kernel is built from
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 

@@ -113,37 +113,35 @@ __device__ __forceinline__ void rot8_bf16(u32x4 a, u32x4 b, const float2* fe,
   };
   const uint64_t live = __builtin_amdgcn_ballot_w64(true);
   float y1[8], y2[8];
-  uint64_t okm = live;
+  uint64_t okm[8];                    // per pair: the lanes whose fp32 values stand (wave-uniform)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) fast(i, &y1[i], &y2[i], &okm);
+  for (int i = 0; i < 8; ++i) {
+    okm[i] = live;
+    fast(i, &y1[i], &y2[i], &okm[i]);
+  }
   u32x4 ra, rb;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     ra[j] = pack_bf16x2(y1[2 * j], y1[2 * j + 1]);
     rb[j] = pack_bf16x2(y2[2 * j], y2[2 * j + 1]);
   }
-  if (okm != live) {
-    // rare: find the pairs that failed again and take their fp64 rotation
+  // rare: the pairs some lane could not decide take the fp64 rotation on
+  // those lanes (no recomputation of the others)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float f1, f2;
-      uint64_t m = live;
-      fast(i, &f1, &f2, &m);
-      const bool mine = (m >> __lane_id()) & 1;
-      if (!mine) {
-        const double u = (double)((i & 1) ? bf16_hi(a[i >> 1]) : bf16_lo(a[i >> 1]));
-        const double v = (double)((i & 1) ? bf16_hi(b[i >> 1]) : bf16_lo(b[i >> 1]));
-        const double2 e = de[i];
-        const uint32_t r1 = f64_to_bf16_bits(rot_first(u, v, e.x, e.y));
-        const uint32_t r2 = f64_to_bf16_bits(rot_second(u, v, e.x, e.y));
-        const int j = i >> 1;
-        if (i & 1) {
-          ra[j] = (ra[j] & 0xFFFFu) | (r1 << 16);
-          rb[j] = (rb[j] & 0xFFFFu) | (r2 << 16);
-        } else {
-          ra[j] = (ra[j] & 0xFFFF0000u) | r1;
-          rb[j] = (rb[j] & 0xFFFF0000u) | r2;
-        }
+  for (int i = 0; i < 8; ++i) {
+    if (okm[i] != live && !((okm[i] >> __lane_id()) & 1)) {
+      const double u = (double)((i & 1) ? bf16_hi(a[i >> 1]) : bf16_lo(a[i >> 1]));
+      const double v = (double)((i & 1) ? bf16_hi(b[i >> 1]) : bf16_lo(b[i >> 1]));
+      const double2 e = de[i];
+      const uint32_t r1 = f64_to_bf16_bits(rot_first(u, v, e.x, e.y));
+      const uint32_t r2 = f64_to_bf16_bits(rot_second(u, v, e.x, e.y));
+      const int j = i >> 1;
+      if (i & 1) {
+        ra[j] = (ra[j] & 0xFFFFu) | (r1 << 16);
+        rb[j] = (rb[j] & 0xFFFFu) | (r2 << 16);
+      } else {
+        ra[j] = (ra[j] & 0xFFFF0000u) | r1;
+        rb[j] = (rb[j] & 0xFFFF0000u) | r2;
       }
     }
   }
