@@ -26,16 +26,20 @@
 //  3. gather (chunks x rows), rows with top-k or top-p and no min-p: one
 //     wave reads the bucket of the k-th token or of the top-p crossing off
 //     the histogram; when at most 4096 tokens lie at or above it, every
-//     chunk adds its share to the candidate list.
+//     chunk adds its share to the candidate list.  Otherwise, with one rule
+//     on and at most 4096 tokens in that bucket (edge mode), every chunk
+//     adds the bucket's tokens and writes its mass above the bucket.
 //  4. select (one 1024-thread workgroup per row): greedy rows take the
 //     merged argmax.  Candidates (a prefix of the ranking that holds the
 //     kept set) are sorted by key then id (one wave in registers up to 256,
 //     a bitonic sort in LDS beyond), the thresholds read off their prefix
 //     masses, and the kept ones re-sorted by id for the draw.  Without any
-//     truncation the chunk masses locate the draw.  Larger kept sets take
-//     two more radix levels (12 + 8 bits, one pass each over z') per
-//     threshold, then per-chunk kept masses and one scan of the chunk that
-//     holds the target.
+//     truncation the chunk masses locate the draw.  In edge mode two radix
+//     levels over the bucket's tokens (in LDS) place the threshold, and the
+//     per-chunk masses above the bucket plus the bucket's kept tokens
+//     locate the draw.  Other large kept sets take two more radix levels
+//     (12 + 8 bits, one pass each over z') per threshold, then per-chunk
+//     kept masses and one scan of the chunk that holds the target.
 #pragma clang fp contract(off)
 
 #include "sa_device.h"
