@@ -1100,6 +1100,10 @@ __device__ __forceinline__ int finish_edge(SelShared& S, const SampleArgs& a, in
   constexpr int R = kCap / kSelThreads;
   constexpr int kLow = 1024;                        // bins per level
   const int tid = threadIdx.x, C = a.C;
+  if (n <= 0) {                                     // the bound's bucket always holds a token
+    *kept = 0;
+    return -1;
+  }
   const u64* x = S.u.cand.key;                      // masses recomputed where needed
 #pragma unroll
   for (int r = 0; r < R; ++r) {
