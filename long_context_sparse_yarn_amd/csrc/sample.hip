@@ -58,6 +58,13 @@ constexpr int kPer = kSampleChunk / kPrepThreads;   // 16 entries per thread
 #endif
 constexpr int kHistThreads = SA_HIST_THREADS;
 constexpr int kHistPer = kSampleChunk / kHistThreads;
+// The prep launch likewise: 512 threads per chunk were 1 us faster per call
+// than 256 at 8 rows and even at 64; 1024 lost 3 us at 64 rows.
+#ifndef SA_PREP_THREADS
+#define SA_PREP_THREADS 512
+#endif
+constexpr int kPrepOnlyThreads = SA_PREP_THREADS;     // the prep launch
+constexpr int kPrepOnlyPer = kSampleChunk / kPrepOnlyThreads;
 constexpr int kNB = kSampleBuckets;
 constexpr int kHist = kSampleHist;                  // 4096 buckets, then 64 sums of 64 buckets
 constexpr int kSelThreads = 1024;
@@ -201,7 +208,7 @@ __device__ __forceinline__ void row_max(const SampleArgs& a, int b, float* m, in
 }
 
 // ------------------------------------------------------------------ prep
-__global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kPrepOnlyThreads) void sample_prep_kernel(SampleArgs a) {
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const sa_sample_params P = a.params[b];
   const bool pen = a.counts && (P.repetition != 1.f || P.presence != 0.f || P.frequency != 0.f);
@@ -209,28 +216,28 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
   const float* Bi = a.bias ? a.bias + (int64_t)b * a.bias_stride : nullptr;
   const int32_t* Cn = pen ? a.counts + (int64_t)b * a.V : nullptr;
   const int v0 = c * kSampleChunk + tid;
-  float z[kPer];
+  float z[kPrepOnlyPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
+  for (int j = 0; j < kPrepOnlyPer; ++j) {
+    const int v = v0 + j * kPrepOnlyThreads;
     z[j] = v < a.V ? L[v] : 0.f;
   }
   if (Bi) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int v = v0 + j * kPrepThreads;
+    for (int j = 0; j < kPrepOnlyPer; ++j) {
+      const int v = v0 + j * kPrepOnlyThreads;
       if (v < a.V) z[j] = z[j] + Bi[v];
     }
   }
   if (pen) {
-    int n[kPer];
+    int n[kPrepOnlyPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int v = v0 + j * kPrepThreads;
+    for (int j = 0; j < kPrepOnlyPer; ++j) {
+      const int v = v0 + j * kPrepOnlyThreads;
       n[j] = v < a.V ? Cn[v] : 0;
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kPrepOnlyPer; ++j) {
       if (n[j] > 0) {
         float t = z[j] > 0.f ? z[j] / P.repetition : z[j] * P.repetition;
         t = t - P.presence;
@@ -243,8 +250,8 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
   float best = 0.f;
   int arg = -1;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
+  for (int j = 0; j < kPrepOnlyPer; ++j) {
+    const int v = v0 + j * kPrepOnlyThreads;
     if (v < a.V) {
       Z[v] = z[j];
       if (O) O[v] = z[j];
@@ -263,15 +270,15 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
       arg = oa;
     }
   }
-  __shared__ float wv[kPrepThreads / 64];
-  __shared__ int wa[kPrepThreads / 64];
+  __shared__ float wv[kPrepOnlyThreads / 64];
+  __shared__ int wa[kPrepOnlyThreads / 64];
   if ((tid & 63) == 0) {
     wv[tid >> 6] = best;
     wa[tid >> 6] = arg;
   }
   // clear this chunk's share of the row's histogram (filled by the next launch)
   const int share = (kHist + a.C - 1) / a.C;
-  for (int i = c * share + tid; i < min(kHist, (c + 1) * share); i += kPrepThreads) {
+  for (int i = c * share + tid; i < min(kHist, (c + 1) * share); i += kPrepOnlyThreads) {
     a.hist_count[(int64_t)b * kHist + i] = 0u;
     a.hist_mass[(int64_t)b * kHist + i] = 0ull;
   }
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(kPrepThreads) void sample_prep_kernel(SampleArgs a)
   if (tid == 0) {
     float bv = wv[0];
     int ba = wa[0];
-    for (int w = 1; w < kPrepThreads / 64; ++w)
+    for (int w = 1; w < kPrepOnlyThreads / 64; ++w)
       if (better(wv[w], wa[w], bv, ba)) {
         bv = wv[w];
         ba = wa[w];
@@ -1324,7 +1331,7 @@ hipError_t launch_sample(const SampleArgs& args, hipStream_t s) {
   // SA_HIST_WGS workgroups (one and a half per CU; swept 128-768), up to 8
   a.hist_cpw = max(1, min(8, (a.B * a.C) / SA_HIST_WGS));
   const dim3 grid(a.C, a.B);
-  hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepOnlyThreads), 0, s, a);
   hipLaunchKernelGGL(sample_hist_kernel, dim3((a.C + a.hist_cpw - 1) / a.hist_cpw, a.B), dim3(kHistThreads), 0, s,
                      a);
   hipLaunchKernelGGL(sample_gather_kernel, grid, dim3(kPrepThreads), 0, s, a);
