@@ -47,8 +47,6 @@
 
 namespace {
 
-constexpr int kPrepThreads = 256;
-constexpr int kPer = kSampleChunk / kPrepThreads;   // 16 entries per thread
 // The histogram launch has one workgroup per chunk at small batches (one
 // per CU at 8 rows), so it runs more threads per chunk to hide its loads
 // and its contended LDS atomics (1024 against 256: 2 us less per call at
@@ -65,6 +63,13 @@ constexpr int kHistPer = kSampleChunk / kHistThreads;
 #endif
 constexpr int kPrepOnlyThreads = SA_PREP_THREADS;     // the prep launch
 constexpr int kPrepOnlyPer = kSampleChunk / kPrepOnlyThreads;
+// And the gather launch: 512 threads were 1.3 us (top-k 50) and 1.5 us
+// (flat top-p) faster per call than 256; 1024 lost 2.5 us at 64 rows.
+#ifndef SA_GATHER_THREADS
+#define SA_GATHER_THREADS 512
+#endif
+constexpr int kGatherThreads = SA_GATHER_THREADS;     // the gather launch
+constexpr int kGatherPer = kSampleChunk / kGatherThreads;
 constexpr int kNB = kSampleBuckets;
 constexpr int kHist = kSampleHist;                  // 4096 buckets, then 64 sums of 64 buckets
 constexpr int kSelThreads = 1024;
@@ -485,7 +490,7 @@ __device__ __forceinline__ u64 wave_row_mass(const SampleArgs& a, int b) {
 // candidate list; in edge mode the tokens in the bound's bucket do, and
 // each chunk's mass above the bucket goes to chunk_kmass.  Every chunk in
 // its own workgroup.
-__global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kGatherThreads) void sample_gather_kernel(SampleArgs a) {
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const sa_sample_params P = a.params[b];
   if (!params_ok(P, a.u[b]) || P.temperature == 0.f || P.min_p > 0.f) return;
@@ -494,13 +499,13 @@ __global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs 
   // for it, the select launch does not read it)
   __shared__ Bound s_bd;
   __shared__ float s_m;
-  __shared__ u64 s_q[kPrepThreads / 64];
+  __shared__ u64 s_q[kGatherThreads / 64];
   const float* Z = a.zp + (int64_t)b * a.zs;
   const int v0 = c * kSampleChunk + tid;
-  float z[kPer];                                     // in flight while the bound is found
+  float z[kGatherPer];                                     // in flight while the bound is found
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
+  for (int j = 0; j < kGatherPer; ++j) {
+    const int v = v0 + j * kGatherThreads;
     z[j] = v < a.V ? Z[v] : 0.f;
   }
   if (tid < 64) {
@@ -520,30 +525,30 @@ __global__ __launch_bounds__(kPrepThreads) void sample_gather_kernel(SampleArgs 
   const Bound bd = s_bd;
   const bool edge = edge_mode(P, a.V, bd);
   if (bd.nb > (u64)kCap && !edge) return;           // the select launch takes the radix path
-  uint32_t key[kPer];
-  int id[kPer];
-  bool take[kPer];
+  uint32_t key[kGatherPer];
+  int id[kGatherPer];
+  bool take[kGatherPer];
   u64 q = 0;
   const float m = s_m, cT = temp_coef(P.temperature);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + j * kPrepThreads;
+  for (int j = 0; j < kGatherPer; ++j) {
+    const int v = v0 + j * kGatherThreads;
     key[j] = fkey(z[j]);
     id[j] = v;
     const uint32_t d = key[j] >> 20;
     take[j] = v < a.V && (edge ? d == bd.blb : d >= bd.blb);
     if (edge && v < a.V && d > bd.blb) q += fixed_mass(rel_weight(z[j], m, cT));
   }
-  __shared__ uint32_t s_app[kPrepThreads / 64 + 1];
+  __shared__ uint32_t s_app[kGatherThreads / 64 + 1];
   if (edge) {
     q = wave_sum_u64(q);
     if (lane == 0) s_q[tid >> 6] = q;              // read after append's barriers
   }
-  append_candidates<kPer, kPrepThreads>(a, b, key, id, take, s_app);
+  append_candidates<kGatherPer, kGatherThreads>(a, b, key, id, take, s_app);
   if (edge && tid == 0) {
     u64 t = 0;
 #pragma unroll
-    for (int i = 0; i < kPrepThreads / 64; ++i) t += s_q[i];
+    for (int i = 0; i < kGatherThreads / 64; ++i) t += s_q[i];
     a.chunk_kmass[(int64_t)b * a.C + c] = t;
   }
 }
@@ -1334,7 +1339,7 @@ hipError_t launch_sample(const SampleArgs& args, hipStream_t s) {
   hipLaunchKernelGGL(sample_prep_kernel, grid, dim3(kPrepOnlyThreads), 0, s, a);
   hipLaunchKernelGGL(sample_hist_kernel, dim3((a.C + a.hist_cpw - 1) / a.hist_cpw, a.B), dim3(kHistThreads), 0, s,
                      a);
-  hipLaunchKernelGGL(sample_gather_kernel, grid, dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_gather_kernel, grid, dim3(kGatherThreads), 0, s, a);
   hipLaunchKernelGGL(sample_select_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
