@@ -132,17 +132,36 @@ typedef struct {
 } sa_kv_snapshot;
 
 /* Create a handle over caller-owned buffers k, v (device, B*capacity*n_kv*
- * d_h elements each).  `offset` rows (0 .. capacity) are taken as already
- * written (a pre-filled prefix; K rows already rotated).  capacity must be
- * a positive multiple of 32. */
+ * d_h elements each) ("MoE-Xtend" README, KV CACHE: one preallocated cache
+ * per layer, K and V of shape [B, T_cache, H_kv, d], sized
+ * min(prompt + max_tokens, max_context) rows by the caller; the V buffer
+ * here is blocked as described above).  `offset` rows (0 .. capacity) are
+ * taken as already written (a pre-filled prefix; K rows already rotated).
+ * capacity must be a positive multiple of 32.  The handle is host memory
+ * the library allocates; *out is set only on SA_OK.
+ * SA_ERR_ARG: null out/k/v, unaligned k/v, B, n_kv or d_h not positive;
+ * SA_ERR_DTYPE: unknown dtype; SA_ERR_SHAPE: capacity not a positive
+ * multiple of 32, d_h not a multiple of 8 or above 256; SA_ERR_CAPACITY:
+ * offset outside [0, capacity]. */
 int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B,
                     int64_t capacity, int n_kv, int d_h, int64_t offset);
+/* The same call under the name the cache's interface gives its
+ * constructor ("MoE-Xtend" README, KV CACHE: init_cache); identical
+ * arguments, results and errors. */
+int kv_cache_init(sa_kv_cache** out, void* k, void* v, int dtype, int B,
+                  int64_t capacity, int n_kv, int d_h, int64_t offset);
+/* Free the host handle (the caller's K/V buffers are untouched).  Work
+ * already enqueued with the handle is unaffected (kernels take plain
+ * pointers).  A null handle is SA_ERR_ARG. */
 int kv_cache_destroy(sa_kv_cache* c);
-/* Positions written so far (the next append's position); -1 for a null
+/* Positions written so far: the global position of the next append
+ * ("MoE-Xtend" README, KV CACHE: offset advances on extend; DESIGN
+ * CONTRACTS: RoPE and masks use this absolute position).  -1 for a null
  * handle. */
 int64_t kv_cache_offset(const sa_kv_cache* c);
 /* Oldest position the cache holds: base for a linear cache, max(0, offset -
- * W) for a ring; -1 for a null handle. */
+ * W) for a ring of W rows ("GPT-OSS-Lite" README, Why these metrics
+ * matter: windowed layers keep only their window); -1 for a null handle. */
 int64_t kv_cache_base(const sa_kv_cache* c);
 
 /* Append T_new rows to every sequence ("MoE-Xtend" README, KV CACHE: extend

@@ -140,6 +140,24 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    """Bytes a workspace tensor holds, whatever its dtype."""
+    return t.numel() * t.element_size()
+
+
+def _out_like(q: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
+    """`out` if it can receive a result shaped like q, else a new tensor.
+    A given `out` must match q's shape, dtype and device and be contiguous."""
+    if out is None:
+        return torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype and device (%s %s %s vs %s %s %s)" % (
+            tuple(out.shape), out.dtype, out.device, tuple(q.shape), q.dtype, q.device))
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    return out
+
+
 @dataclass(frozen=True)
 class Yarn:
     d_h: int
@@ -383,8 +401,7 @@ def sinkattn_prefill(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, windo
         raise ValueError("sinks must be float32 [n_q]")
     if q.dtype != cache.dtype:
         raise TypeError("q dtype differs from the cache's")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out)
     _check(_sinkattn_prefill(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"), _dev(out, "out"),
                              B, T_q, n_q, cache.n_kv, d, int(window), float(sm_scale),
                              int(q_offset), _stream(stream)))
@@ -402,8 +419,7 @@ def sinkattn_prefill_rope(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, 
         raise ValueError("sinks must be float32 [n_q]")
     if q.dtype != cache.dtype:
         raise TypeError("q dtype differs from the cache's")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out)
     ys = y.c_struct()
     _check(_sinkattn_prefill_rope(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"),
                                   _dev(out, "out"), B, T_q, n_q, cache.n_kv, d, int(window),
@@ -439,7 +455,7 @@ def qkv_rope_append(cache: KVCache, x: torch.Tensor, w_qkv: torch.Tensor, b_qkv:
     ys = y.c_struct()
     _check(_sinkattn_qkv(cache.handle, _dev(x, "x"), _dev(w_qkv, "w_qkv"), _dev(b_qkv, "b_qkv"),
                          _dev(q_out, "q_out"), B, T, dm, int(n_q), ctypes.byref(ys),
-                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                         _dev(workspace, "workspace"), _nbytes(workspace),
                          _stream(stream)))
     return q_out
 
@@ -465,7 +481,7 @@ def moe_dispatch(ids: torch.Tensor, E: int, stream=None):
     start = torch.empty(E + 1, dtype=torch.int32, device=ids.device)
     ws = torch.empty(max(int(_moe_dispatch_ws(N, E)), 16), dtype=torch.uint8, device=ids.device)
     _check(_moe_dispatch(_dev(ids, "ids"), N, int(E), k, _dev(rows, "rows"), _dev(start, "start"),
-                         _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+                         _dev(ws, "workspace"), _nbytes(ws), _stream(stream)))
     return rows, start
 
 
@@ -495,7 +511,7 @@ def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w13: torch.Tensor, w2: to
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _check(_moe_layer(_dev(x, "x"), N, dm, _dev(w_router, "w_router"), E, int(k), _dev(w13, "w13"),
                       _dev(w2, "w2"), ffn, p13, p2, ffn_s, _dev(out, "out"),
-                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                      _dev(workspace, "workspace"), _nbytes(workspace),
                       _stream(stream)))
     return out
 
@@ -522,11 +538,10 @@ def sinkattn_decode(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window
         raise TypeError("q dtype differs from the cache's")
     if workspace is None:
         workspace = decode_workspace(cache, n_q)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out)
     _check(_sinkattn_decode(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"), _dev(out, "out"),
                             B, n_q, cache.n_kv, d, int(window), float(sm_scale),
-                            _dev(workspace, "workspace"), workspace.numel() * 4,
+                            _dev(workspace, "workspace"), _nbytes(workspace),
                             _stream(stream)))
     return out
 
@@ -587,7 +602,7 @@ def sample_tokens(logits: torch.Tensor, params: torch.Tensor, u: torch.Tensor,
                           _dev(params, "params"), _dev(u, "u"), 1 if update_counts else 0,
                           _dev(tokens, "tokens"), _dev(kept, "n_kept") if kept is not None else None,
                           _dev(proc, "processed") if proc is not None else None,
-                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _dev(workspace, "workspace"), _nbytes(workspace),
                           _stream(stream)))
     out = [tokens]
     if want_kept:

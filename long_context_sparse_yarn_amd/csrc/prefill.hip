@@ -41,15 +41,6 @@
 #include "sa_rope.h"
 
 
-#ifndef SA_RD_AHEAD
-#define SA_RD_AHEAD 4
-#endif
-#ifndef SA_INTERLEAVE
-#define SA_INTERLEAVE 0
-#endif
-#ifndef SA_VALU_LEAD
-#define SA_VALU_LEAD 0
-#endif
 // 1: where it pays (d = 96 with two N tiles per wave), each unit's LDS
 // operands (K for its scores, V for its PV) are read during the previous
 // unit's vector work; 0: always at the start of the unit.
@@ -71,8 +62,6 @@ __device__ __forceinline__ void lds_direct16(const void* src, const uint16_t* ld
 }
 // Wait for this wave's global loads (including those into LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-template <int Mask, int N>
-__device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(Mask, N, 0); }
 
 // LDS placement of K: rows are not padded (d/8 sixteen-byte slots each) and
 // chunk k of row r sits in slot k ^ f(r).  The operand reads take rows
@@ -481,26 +470,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   scores(S0, 0, 0);
   if (need_mask(t0 * kTile)) apply_mask(S0, t0 * kTile);
 
-  // Instruction order of a unit's main stretch: a few operand reads ahead,
-  // then each pair of MFMAs with one more operand read and its share of the
-  // softmax's vector work, so that the matrix cores and the vector units
-  // work side by side and only a few operands are in flight.
-  auto interleave = [&]() {
-    if constexpr (!SA_INTERLEAVE) return;
-    constexpr int kRd = 2 * KS + DT;                      // LDS operand reads per unit
-    constexpr int kAhead = SA_RD_AHEAD < kRd ? SA_RD_AHEAD : kRd;
-    constexpr int kMf = 2 * KS * NT + DT * NT;            // MFMAs per unit
-    constexpr int kValu = (NT * 27 - SA_VALU_LEAD + kMf / 2 - 1) / (kMf / 2);
-    sched_group<0x100, kAhead>();               // LDS reads
-    if constexpr (SA_VALU_LEAD > 0) sched_group<0x002, SA_VALU_LEAD>();
-#pragma unroll
-    for (int i = 0; i < kMf / 2; ++i) {
-      if (i < kRd - kAhead) sched_group<0x100, 1>();
-      sched_group<0x008, 2>();                  // MFMA
-      sched_group<0x002, kValu>();              // VALU
-    }
-  };
-
   // One unit: Sc = S(u) in, Sn = S(u+1) out (from K buffer kbn, half hn,
   // first key k0n); Pp = P(u-1) in (V buffer vbp, half hp), Pc = P(u) out;
   // S(u) can be recomputed from K buffer kbc, half hc, first key k0c.  The
@@ -526,7 +495,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     if constexpr (kPhaseSplit) __builtin_amdgcn_sched_barrier(0);
     if constexpr (kOpsAhead) load_ops(on, kbx, hx, vbx, vx);
     probs(Sc, Pc, ls);
-    interleave();
     bool bad = false;
 #pragma unroll
     for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || m_run[n] == -INFINITY;

@@ -200,6 +200,11 @@ int kv_cache_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64
   return cache_new(out, k, v, dtype, B, capacity, n_kv, d_h, offset, false);
 }
 
+int kv_cache_init(sa_kv_cache** out, void* k, void* v, int dtype, int B, int64_t capacity,
+                  int n_kv, int d_h, int64_t offset) {
+  return kv_cache_create(out, k, v, dtype, B, capacity, n_kv, d_h, offset);
+}
+
 int kv_ring_create(sa_kv_cache** out, void* k, void* v, int dtype, int B, int window, int n_kv,
                    int d_h) {
   if (window <= 0 || window % 32)

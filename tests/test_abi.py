@@ -88,6 +88,17 @@ def test_cache_create_validation():
     assert st == SA_OK and B._kv_cache_offset(h) == 40
     assert B._kv_cache_offset(None) == -1
     assert B._kv_cache_destroy(h) == SA_OK
+    assert B._kv_cache_destroy(None) == SA_ERR_ARG
+    # kv_cache_init: the constructor under the cache interface's own name
+    lib = ctypes.CDLL(B.LIB_PATH)
+    init = lib.kv_cache_init
+    init.restype = ctypes.c_int
+    init.argtypes = B._kv_cache_create.argtypes
+    hi = ctypes.c_void_p()
+    assert init(ctypes.byref(hi), FAKE_K, FAKE_V, 0, 2, 256, 2, 64, 17) == SA_OK
+    assert B._kv_cache_offset(hi) == 17 and B._kv_cache_base(hi) == 0
+    assert init(ctypes.byref(ctypes.c_void_p()), FAKE_K, FAKE_V, 0, 2, 100, 2, 64, 0) == SA_ERR_SHAPE
+    assert B._kv_cache_destroy(hi) == SA_OK
 
 
 def test_errors_are_reported_before_any_launch():
@@ -200,6 +211,39 @@ def test_decode_workspace_size_bound():
     b = B._sinkattn_decode_ws(8, 64, 8, 64, 256)
     assert a >= b > 0
     assert B._sinkattn_decode_ws(8, 63, 8, 64, 256) == 0
+
+
+def test_binding_counts_workspace_bytes_of_any_dtype():
+    """The binding hands the C-ABI the workspace's size in bytes whatever its
+    dtype, so a too-small workspace of a narrow dtype is refused by the
+    library's size check instead of being written past its end."""
+    import torch
+    need = B._sinkattn_decode_ws(2, 8, 2, 64, 256)
+    for dt in (torch.float32, torch.bfloat16, torch.uint8, torch.int64):
+        esz = torch.tensor([], dtype=dt).element_size()
+        small = torch.empty((need - 1) // esz, dtype=dt)          # one element short of `need`
+        assert B._nbytes(small) == small.numel() * esz < need
+        big = torch.empty((need + esz - 1) // esz, dtype=dt)
+        assert B._nbytes(big) >= need
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=10)
+    q, o, s = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000)
+    small = torch.empty((need - 1) // 2, dtype=torch.bfloat16)
+    assert B._sinkattn_decode(q, h, s, o, 2, 8, 2, 64, 0, 0.125, o, B._nbytes(small),
+                              None) == SA_ERR_ARG
+    B._kv_cache_destroy(h)
+
+
+def test_binding_checks_out_before_any_launch():
+    import torch
+    q = torch.empty((2, 5, 8, 64), dtype=torch.bfloat16)
+    assert B._out_like(q, None).shape == q.shape
+    good = torch.empty_like(q)
+    assert B._out_like(q, good) is good
+    for bad in (torch.empty((2, 5, 8, 32), dtype=torch.bfloat16),        # shape
+                torch.empty((2, 5, 8, 64), dtype=torch.float32),         # dtype
+                torch.empty((2, 5, 64, 8), dtype=torch.bfloat16).transpose(2, 3)):  # layout
+        with pytest.raises(ValueError):
+            B._out_like(q, bad)
 
 
 def ring(dtype=0, Bn=2, W=128, n_kv=2, d=64):

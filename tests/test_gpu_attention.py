@@ -113,27 +113,29 @@ def test_mask_edges_exact(W, offset):
 
 
 DECODE_CASES = [
-    # B, prefix, steps, n_q, n_kv, d, window, dtype
-    (2, 1000, 6, 64, 8, 64, 0, "bf16"),
-    (2, 1000, 6, 64, 8, 64, 128, "bf16"),
-    (1, 300, 4, 8, 4, 96, 0, "bf16"),
-    (3, 77, 5, 16, 1, 128, 50, "bf16"),
-    (1, 5000, 3, 32, 8, 64, 0, "bf16"),
-    (1, 120, 4, 8, 2, 64, 0, "f32"),
-    (1, 120, 4, 8, 2, 64, 32, "f32"),
+    # B, prefix, steps, n_q, n_kv, d, window, dtype, sink_inf
+    (2, 1000, 6, 64, 8, 64, 0, "bf16", False),
+    (2, 1000, 6, 64, 8, 64, 128, "bf16", False),
+    (1, 300, 4, 8, 4, 96, 0, "bf16", False),
+    (3, 77, 5, 16, 1, 128, 50, "bf16", False),
+    (1, 5000, 3, 32, 8, 64, 0, "bf16", False),
+    (1, 2000, 3, 16, 4, 64, 512, "bf16", False),       # band wider than one split: lo inside a split
+    (2, 1000, 3, 64, 8, 64, 0, "bf16", True),          # no sink, split span + merge
+    (2, 1000, 3, 64, 8, 64, 128, "bf16", True),        # no sink, single-split span
+    (1, 150, 3, 8, 2, 96, 0, "bf16", True),            # no sink, whole cache in one split
+    (1, 120, 4, 8, 2, 64, 0, "f32", False),
+    (1, 120, 4, 8, 2, 64, 32, "f32", False),
+    (1, 300, 2, 8, 2, 64, 0, "f32", True),
 ]
 
 
-@pytest.mark.parametrize("B,prefix,steps,n_q,n_kv,d,W,dtype", DECODE_CASES)
-def test_decode_matches_oracle(B, prefix, steps, n_q, n_kv, d, W, dtype):
-    rng = np.random.default_rng(prefix + d + steps)
+def _decode_sweep(B, prefix, steps, n_q, n_kv, d, W, dtype, sinks, pk, pv, rng, kscale=None):
+    """Append the prefix, then run `steps` decode steps on the GPU and in the
+    oracle; returns the max-abs difference of each step."""
     y = Yarn()
     sm = 1.0 / np.sqrt(d)
     C = ((prefix + steps + 31) // 32) * 32 + 32
-    sinks = rng.standard_normal(n_q).astype(np.float32)
     s_t = torch.from_numpy(sinks).cuda()
-    pk = _draw((B, prefix, n_kv, d), rng, dtype)
-    pv = _draw((B, prefix, n_kv, d), rng, dtype)
     cache = sa.KVCache.empty(B, C, n_kv, d, dtype=TORCH_DT[dtype], fill=float("nan"))
     cache.append(dev(pk, dtype), dev(pv, dtype))
     ws = sa.decode_workspace(cache, n_q)
@@ -141,9 +143,12 @@ def test_decode_matches_oracle(B, prefix, steps, n_q, n_kv, d, W, dtype):
     oc = OracleKVCache(B, C, n_kv, d)
     oc.append(pk.astype(np.float64), pv.astype(np.float64))
     ly = lib_yarn(d, y)
+    errs = []
     for s in range(steps):
         q = _draw((B, 1, n_q, d), rng, dtype)
         k = _draw((B, 1, n_kv, d), rng, dtype)
+        if kscale is not None:
+            k = (bf16_round if dtype == "bf16" else np.float32)(k * kscale)
         v = _draw((B, 1, n_kv, d), rng, dtype)
         o = cache.offset
         qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
@@ -154,8 +159,76 @@ def test_decode_matches_oracle(B, prefix, steps, n_q, n_kv, d, W, dtype):
         torch.cuda.synchronize()
         want, _, _ = decode_step(oc, q, k, v, sinks, W, sm, inv, c, dtype)
         got = host(out)
-        assert np.all(np.isfinite(got))
-        assert max_abs(got, want) <= TOL[dtype], (s, max_abs(got, want))
+        assert np.all(np.isfinite(got)), s
+        errs.append(max_abs(got, want))
+    return errs
+
+
+@pytest.mark.parametrize("B,prefix,steps,n_q,n_kv,d,W,dtype,sink_inf", DECODE_CASES)
+def test_decode_matches_oracle(B, prefix, steps, n_q, n_kv, d, W, dtype, sink_inf):
+    rng = np.random.default_rng(prefix + d + steps + 7 * sink_inf)
+    sinks = (np.full(n_q, -np.inf, np.float32) if sink_inf
+             else rng.standard_normal(n_q).astype(np.float32))
+    pk = _draw((B, prefix, n_kv, d), rng, dtype)
+    pv = _draw((B, prefix, n_kv, d), rng, dtype)
+    errs = _decode_sweep(B, prefix, steps, n_q, n_kv, d, W, dtype, sinks, pk, pv, rng)
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("W,sink_inf", [(0, False), (0, True), (128, False)])
+def test_decode_growing_logits(W, sink_inf):
+    """Keys whose size grows 20-fold along the cache: the scores of later
+    key blocks pass the running max by far more than the lazy slack (2^8 in
+    probability), many times within one split, so the kernel's rescale runs
+    mid-span; the largest scaled logits reach ~100 (e^100 would overflow an
+    unscaled fp32 sum)."""
+    B, prefix, steps, n_q, n_kv, d = 1, 2400, 2, 16, 2, 64
+    rng = np.random.default_rng(31 + W)
+    growth = (1.0 + 19.0 * np.arange(prefix) / prefix).astype(np.float32)[None, :, None, None]
+    pk = bf16_round(_draw((B, prefix, n_kv, d), rng, "bf16") * growth)
+    pv = _draw((B, prefix, n_kv, d), rng, "bf16")
+    sinks = (np.full(n_q, -np.inf, np.float32) if sink_inf
+             else rng.standard_normal(n_q).astype(np.float32))
+    errs = _decode_sweep(B, prefix, steps, n_q, n_kv, d, W, "bf16", sinks, pk, pv, rng,
+                         kscale=20.0)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("W", [0, 128, 512])
+@pytest.mark.parametrize("n_rows", [201, 1000, 65536])
+def test_decode_mask_edges_exact(W, n_rows):
+    """Decode's band and causal edges, bit-exact: the query sits at p = n_rows-1
+    (its own row just appended); a probe key j gets a +30 logit and a one-hot
+    value.  The probe coordinate of the output is ~1 iff j is allowed
+    (p-W < j <= p) and exactly 0 otherwise; rows past p hold NaN and must
+    not leak.  201 rows run as one split, 1000 and 65536 through split
+    partials and the merge (W = 512 with its lower edge inside a split)."""
+    B, n_q, n_kv, d = 1, 8, 1, 64
+    C = ((n_rows + 31) // 32) * 32 + 64
+    cache = sa.KVCache.empty(B, C, n_kv, d, fill=float("nan"))
+    z = torch.zeros((B, n_rows, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    cache.append(z, z)
+    p = n_rows - 1
+    q = torch.zeros((B, 1, n_q, d), dtype=torch.bfloat16, device="cuda")
+    q[..., 0] = 1.0
+    sinks = torch.full((n_q,), -float("inf"), device="cuda")
+    ws = sa.decode_workspace(cache, n_q)
+    for j in (p, p - 1, p - W + 1, p - W, 0):
+        if j < 0 or (W == 0 and j in (p - W + 1, p - W)):
+            continue
+        cache.k[0, j, 0, 0] = 30.0
+        cache.v[0, j // 32, 0, 1, j % 32] = 1.0           # V[j][1] in the blocked layout
+        out = sa.sinkattn_decode(q, cache, sinks, W, 1.0, workspace=ws)
+        torch.cuda.synchronize()
+        o = out[0, 0].float().cpu().numpy()
+        assert np.all(np.isfinite(o)), (p, j)
+        allowed = j <= p and (W == 0 or j > p - W)
+        if allowed:
+            assert np.all(o[:, 1] > 0.99), (W, p, j, o[:, 1])
+        else:
+            assert np.all(o[:, 1] == 0.0), (W, p, j, o[:, 1])
+        cache.k[0, j, 0, 0] = 0.0
+        cache.v[0, j // 32, 0, 1, j % 32] = 0.0
 
 
 @pytest.mark.parametrize("W", [0, 7])
