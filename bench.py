@@ -1,21 +1,33 @@
 """Throughput of the sink-GQA attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 1000] [--no-extra] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extra] [--no-cpu]
 
-One step = the whole hot path over one batch of the GPT-OSS-Lite-shaped
-prefill (B=4, T=4096, n_q=8, n_kv=4, d_h=96, bf16, YaRN s=32 base 1.5e5):
-for each of its two layer kinds (128-token band, full causal) the cache
-rewound to 0, RoPE from the raw Q and K into working buffers, K/V appended,
-and sink attention over the chunk.  Inputs are resident in HBM
-before timing starts.  The value is algorithmic attention TFLOP/s of the
-step (4*d*n_q*B*sum_p|A(p)| flops: allowed query/key pairs only).
+One step = the whole hot path over one batch of the prefill-to-decode
+handover workload (the largest that fits one GPU): B=1, n_q=64, n_kv=8,
+d_h=64, bf16, YaRN s=32 base 1.5e5, a cache pre-filled with 65,536 rows.
+For each of its two layer kinds (128-token band, full causal): the cache
+rewound to the prefix, RoPE of the 2048-token chunk's Q and K at positions
+65,536.. with K/V appended in the same pass, sink attention of the chunk at
+offset 65,536, and a snapshot; then 32 decode steps (RoPE + append of one
+token, sink attention against the cache) per layer, a restore, and 32 more
+steps under another seed.  Inputs are resident in HBM before timing starts.
+The value is algorithmic attention TFLOP/s of the step (4*d*n_q*B*sum_p|A(p)|
+flops over the allowed query/key pairs of the chunk and of every decode
+query).
 
 Extra objects on the same JSON line:
-  roofline      the full-causal prefill kernel (the step's dominant kernel),
-                timed with HIP events on its stream, against dense bf16 MFMA
-  cpu_baseline  the fp64 oracle on a bounded sample of the same step
-  extra         gpt-oss-shaped prefill (B1 T8192 64/8 d64) and long-context
-                decode (B8, 131072 cached rows, 64/8 d64) per-kernel figures
+  roofline      the full-causal prefill kernel of the chunk (the step's
+                dominant kernel), timed with HIP events on its stream inside
+                the timed steps, against dense bf16 MFMA
+  decode_kv     the long-context decode workload's full-causal layer (B8,
+                131,072 cached rows): KV GB/s of its attention kernels
+  handover      per-layer prefill figures and the decode sweeps' figures
+  cpu_baseline  the fp64 oracle on bounded samples: the handover step (the
+                value) and, with the extras, the other prefill and decode
+                workloads
+  extra         GPT-OSS-Lite prefill (B4 T4096 8/4 d96) and gpt-oss prefill
+                (B1 T8192 64/8 d64) steps, long-context decode per layer, and
+                the fused projection, MoE layer and sampling figures
 """
 import argparse
 import json
@@ -32,12 +44,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
-# HBM bytes per launch of the full-causal GPT-OSS-Lite prefill kernel, from
-# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a 512 MiB copy);
-# valid only for the kernel sources it was measured on (measured at sources
-# 4e5972fbb100dc4f; the later change to sa_rope.h's bf16 rotation leaves the
-# prefill kernel's gfx950 assembly instruction for instruction the same).
-TRAFFIC_FULL_PREFILL = {"sources_sha256_16": "069ed16196c46724", "bytes": 89516394}
+# HBM bytes per launch of the roofline kernel, from rocprofv3 FETCH_SIZE x 2.0 +
+# WRITE_SIZE x 1.0 (factors from a 512 MiB copy: FETCH_SIZE reads 256 MiB,
+# WRITE_SIZE 512 MiB), keyed by (workload, window); valid only while the
+# kernel sources hash to the value they were measured with.
+TRAFFIC = {}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_attn.h", "sa_rope.h")   # what the prefill kernel is built from
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
@@ -76,13 +87,17 @@ def attn_flops(B, n_q, d, q_offset, T, window):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra-only", choices=("sampling", "moe", "qkv"), default=None,
                     help="print only that extra leg's figures (for profiling it alone)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="oracle seconds per sampled workload")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="GPU clock settle before the warmup steps: back-to-back launches of "
+                         "the step's full-causal prefill for this long (untimed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 3 times (reference dispatch for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -181,6 +196,186 @@ def time_prefill_step(w, sa, torch, steps, warmup):
     STEP_STATS.clear()
     STEP_STATS.update(median=float(np.median(per_step)), min=float(np.min(per_step)))
     return layers, ms_step, b2b, in_step
+
+
+class HandoverLayer:
+    """Device state of one layer of the handover workload: the cache with its
+    pre-filled prefix, the chunk's raw Q/K/V, and the decode tokens of both
+    sweeps (seed 0, then seed 1)."""
+
+    def __init__(self, w, layer, sa, torch):
+        import workloads as wl
+        x = wl.prefill_inputs(w, layer)
+        dt = torch.bfloat16
+        up = lambda a: torch.from_numpy(a).cuda().to(dt)
+        self.host = x
+        self.layer = layer
+        self.window = w.windows[layer]
+        self.q0, self.k0, self.v = up(x["q"]), up(x["k"]), up(x["v"])
+        self.qw = torch.empty_like(self.q0)
+        self.out = torch.empty_like(self.q0)
+        self.sinks = torch.from_numpy(x["sinks"]).cuda()
+        self.cache = sa.KVCache.empty(w.B, w.capacity, w.n_kv, w.d_h, dtype=dt)
+        self.cache.append(up(x["prefix_k"]), up(x["prefix_v"]))
+        self.snap0 = self.cache.snapshot()
+        self.snap1 = None
+        self.yarn = sa.Yarn(w.d_h, w.yarn.base, w.yarn.factor, w.yarn.orig_ctx, w.yarn.alpha,
+                            w.yarn.beta)
+        self.toks = [[{k: up(a) for k, a in wl.decode_token(w, layer, s, seed=w.seed + sw).items()}
+                      for s in range(w.decode_steps)] for sw in range(2)]
+        self.qtok = torch.empty_like(self.toks[0][0]["q"])
+        self.dout = torch.empty((2, w.decode_steps) + tuple(self.qtok.shape), dtype=dt,
+                                device="cuda")
+        self.ws = sa.decode_workspace(self.cache, w.n_q)
+
+    def prefill(self, w, sa, ev=None):
+        self.cache.restore(self.snap0)
+        self.cache.append_rope_qk(self.q0, self.k0, self.v, self.yarn, q_out=self.qw)
+        if ev is not None:
+            ev[0].record()
+        sa.sinkattn_prefill(self.qw, self.cache, self.sinks, self.window, w.sm_scale, w.prefix,
+                            out=self.out)
+        if ev is not None:
+            ev[1].record()
+        self.snap1 = self.cache.snapshot()
+
+    def decode(self, w, sa, sweep, s):
+        t = self.toks[sweep][s]
+        self.cache.append_rope_qk(t["q"], t["k"], t["v"], self.yarn, q_out=self.qtok)
+        sa.sinkattn_decode(self.qtok, self.cache, self.sinks, self.window, w.sm_scale,
+                           workspace=self.ws, out=self.dout[sweep, s])
+
+
+def handover_step(layers, w, sa, ev=None, sweep_ev=None):
+    """One step of the handover workload: both layers' chunk prefill (each
+    ending with a snapshot), then two decode sweeps, each starting from a
+    restore of that snapshot; within a sweep, token s runs through both
+    layers before token s+1."""
+    for L in layers:
+        L.prefill(w, sa, ev if (ev is not None and L.window == 0) else None)
+    for sweep in range(2):
+        if sweep_ev is not None:
+            sweep_ev[sweep][0].record()
+        for L in layers:
+            L.cache.restore(L.snap1)
+        for s in range(w.decode_steps):
+            for L in layers:
+                L.decode(w, sa, sweep, s)
+        if sweep_ev is not None:
+            sweep_ev[sweep][1].record()
+
+
+def handover_flops(w):
+    """(prefill flops per layer kind, decode flops per layer kind) of one step."""
+    pre = {W: attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, W) for W in w.windows}
+    base = w.prefix + w.T
+    dec = {W: 2 * sum(attn_flops(w.B, w.n_q, w.d_h, base + s, 1, W) for s in range(w.decode_steps))
+           for W in w.windows}
+    return pre, dec
+
+
+def decode_bytes(w, pos, W):
+    """Algorithmic bytes of one decode attention call at query position pos:
+    each allowed K and V row once, q read, out written (bf16)."""
+    rows = min(pos + 1, W) if W > 0 else pos + 1
+    return (rows * w.n_kv * w.d_h * 2 * 2 + 2 * w.n_q * w.d_h * 2) * w.B
+
+
+def settle_clock(fn, torch, ms):
+    """Back-to-back launches of fn for about `ms` milliseconds (untimed), so
+    the timed steps start at the clock the GPU holds under this load."""
+    if ms <= 0:
+        return 0
+    t_end = time.perf_counter() + ms * 1e-3
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
+def time_handover(w, sa, torch, steps, warmup, settle_ms):
+    """Times exactly `steps` handover steps after `warmup` untimed ones (and
+    the clock settle).  The only events inside the timed region are its two
+    end marks and one pair around the full-causal prefill launch of each
+    step (the roofline kernel, live on its stream).  A second pass of the
+    same steps, after the timed region, carries events at the step
+    boundaries (spread) and around each decode sweep."""
+    layers = [HandoverLayer(w, i, sa, torch) for i in range(len(w.windows))]
+    full = [L for L in layers if L.window == 0][0]
+    full.prefill(w, sa)
+    n_settle = settle_clock(lambda: sa.sinkattn_prefill(full.qw, full.cache, full.sinks, 0,
+                                                        w.sm_scale, w.prefix, out=full.out),
+                            torch, settle_ms)
+    for _ in range(warmup):
+        handover_step(layers, w, sa)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(E(), E()) for _ in range(steps)]
+    t0, t1 = E(), E()
+    torch.cuda.synchronize()
+    t0.record()
+    for k in range(steps):
+        handover_step(layers, w, sa, ev=evs[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    live = [a.elapsed_time(b) for a, b in evs]
+    # second pass: step spread and decode sweeps
+    marks = [E() for _ in range(steps + 1)]
+    sweeps = [[(E(), E()), (E(), E())] for _ in range(steps)]
+    marks[0].record()
+    for k in range(steps):
+        handover_step(layers, w, sa, sweep_ev=sweeps[k])
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    per_step = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)]
+    sweep_ms = [a.elapsed_time(b) for sw in sweeps for a, b in sw]
+    # each layer's prefill over back-to-back launches on the live buffers
+    b2b = {}
+    for L in layers:
+        L.prefill(w, sa)
+        a, b = E(), E()
+        a.record()
+        for _ in range(KERNEL_REPEAT):
+            sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, w.prefix, out=L.out)
+        b.record()
+        torch.cuda.synchronize()
+        b2b[L.window] = a.elapsed_time(b) / KERNEL_REPEAT
+    # leave every layer as a step leaves it (outputs of the last step)
+    handover_step(layers, w, sa)
+    torch.cuda.synchronize()
+    return {"layers": layers, "ms_step": ms_step, "live": live, "per_step": per_step,
+            "sweep_ms": sweep_ms, "b2b": b2b, "settle_launches": n_settle}
+
+
+def handover_figures(w, t):
+    pre, dec = handover_flops(w)
+    layers = []
+    for L in t["layers"]:
+        ms = float(np.mean(t["live"])) if L.window == 0 else t["b2b"][L.window]
+        f = prefill_figures(w, L, t["b2b"][L.window], ms if L.window == 0 else None)
+        if L.window == 0:
+            f["kernel_ms_in_step_median"] = round(float(np.median(t["live"])), 4)
+            f["kernel_ms_in_step_min"] = round(float(np.min(t["live"])), 4)
+        layers.append(f)
+    base = w.prefix + w.T
+    by_sweep = sum(decode_bytes(w, base + s, W) for s in range(w.decode_steps) for W in w.windows)
+    fl_sweep = sum(dec.values()) / 2
+    sw = float(np.mean(t["sweep_ms"]))
+    return {"layers": layers,
+            "decode_sweep": {"steps": w.decode_steps, "layers": len(w.windows),
+                             "ms": round(sw, 4), "us_per_token": round(sw * 1e3 / w.decode_steps, 2),
+                             "alg_mb": round(by_sweep / 1e6, 2),
+                             "gbs": round(by_sweep / (sw * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(by_sweep / (sw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "gflop": round(fl_sweep / 1e9, 3),
+                             "timing": "events around each sweep (restore, then per token and layer "
+                                       "RoPE + append and sink attention), second pass"},
+            "gflop_step": {"prefill": {str(k): round(v / 1e9, 2) for k, v in pre.items()},
+                           "decode": {str(k): round(v / 1e9, 3) for k, v in dec.items()}}}
 
 
 def abi_call_figures(w, L, sa, torch):
@@ -586,47 +781,8 @@ def sample_extra(sa, torch):
     return res
 
 
-def cpu_baseline(w, layers, budget_s):
-    """The oracle as it stands on a bounded sample of the timed step:
-    RoPE of all of Q and K (fp64) and attention for a seeded sample of query
-    rows per layer, scaled to the whole step by algorithmic flops."""
+def _cpu_info():
     from threadpoolctl import threadpool_info
-    from oracle.attention import attend_query
-    from oracle.rounding import round_to
-    from oracle.yarn import rope_apply, yarn_concentration, yarn_inv_freq
-
-    y = w.yarn
-    inv = yarn_inv_freq(w.d_h, y.base, y.factor, y.orig_ctx, y.alpha, y.beta)
-    c = yarn_concentration(y.factor)
-    rng = np.random.default_rng(0)
-    t_rope = 0.0
-    t_attn = 0.0
-    fl_sample = 0.0
-    fl_total = 0.0
-    n_rows = 0
-    checks = []
-    per_layer = budget_s / len(layers)
-    for L in layers:
-        x = L.host
-        t = time.perf_counter()
-        q_rot = round_to(rope_apply(x["q"].astype(np.float64), 0, inv, c), "bf16")
-        k_rot = round_to(rope_apply(x["k"].astype(np.float64), 0, inv, c), "bf16")
-        t_rope += time.perf_counter() - t
-        V = x["v"]
-        fl_total += attn_flops(w.B, w.n_q, w.d_h, 0, w.T, L.window)
-        out_gpu = L.out.float().cpu().numpy()
-        t_start = time.perf_counter()
-        while time.perf_counter() - t_start < per_layer:
-            b = int(rng.integers(w.B))
-            tq = int(rng.integers(w.T))
-            t = time.perf_counter()
-            o = attend_query(q_rot[b, tq], k_rot[b], V[b], x["sinks"], tq, L.window, w.sm_scale)
-            t_attn += time.perf_counter() - t
-            n = min(tq + 1, L.window) if L.window > 0 else tq + 1
-            fl_sample += 4.0 * w.d_h * w.n_q * n
-            n_rows += 1
-            checks.append(float(np.max(np.abs(o - out_gpu[b, tq]))))
-    est = t_rope + t_attn * (fl_total / fl_sample)
     info = threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] + [1])
     model = None
@@ -637,14 +793,110 @@ def cpu_baseline(w, layers, budget_s):
                 break
     except OSError:
         pass
-    return {"value": round(fl_total / est / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": "fp64 numpy oracle: RoPE of all Q and K of both layers (%.2f s) plus "
-                      "attention of %d seeded random query rows (all heads, %.2f s, %.3g of the "
-                      "step's flops); whole-step time extrapolated by flops" % (
-                          t_rope, n_rows, t_attn, fl_sample / fl_total),
-            "est_step_s": round(est, 2),
+    return int(cores), model
+
+
+def cpu_prefill_sample(w, layers, budget_s, extra_flops=0.0):
+    """The oracle as it stands on a bounded sample of a prefill step: RoPE
+    of all of the chunk's Q and K (fp64), the append (the oracle's cache is
+    the prefix with the rotated chunk after it), and attention of seeded
+    random query rows (all heads) per layer; the whole step's time is
+    extrapolated by algorithmic flops (extra_flops: decode queries of the
+    step, which cost the oracle what a prefill row of the same span does).
+    Also returns the largest difference between those oracle rows and the
+    GPU's output rows."""
+    from oracle.attention import attend_query
+    from oracle.rounding import round_to
+    from oracle.yarn import rope_apply, yarn_concentration, yarn_inv_freq
+
+    y = w.yarn
+    inv = yarn_inv_freq(w.d_h, y.base, y.factor, y.orig_ctx, y.alpha, y.beta)
+    c = yarn_concentration(y.factor)
+    rng = np.random.default_rng(0)
+    t_fixed = t_attn = fl_sample = 0.0
+    fl_total = float(extra_flops)
+    n_rows = 0
+    checks = []
+    per_layer = budget_s / len(layers)
+    for L in layers:
+        x = L.host
+        t = time.perf_counter()
+        q_rot = round_to(rope_apply(x["q"].astype(np.float64), w.prefix, inv, c), "bf16")
+        k_rot = round_to(rope_apply(x["k"].astype(np.float64), w.prefix, inv, c), "bf16")
+        if w.prefix:
+            K = np.concatenate([x["prefix_k"].astype(np.float64), k_rot], axis=1)
+            V = np.concatenate([x["prefix_v"].astype(np.float64), x["v"].astype(np.float64)], axis=1)
+        else:
+            K, V = k_rot, x["v"]
+        t_fixed += time.perf_counter() - t
+        fl_total += attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window)
+        out_gpu = L.out.float().cpu().numpy()
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < per_layer:
+            b = int(rng.integers(w.B))
+            tq = int(rng.integers(w.T))
+            p = w.prefix + tq
+            t = time.perf_counter()
+            o = attend_query(q_rot[b, tq], K[b], V[b], x["sinks"], p, L.window, w.sm_scale)
+            t_attn += time.perf_counter() - t
+            n = min(p + 1, L.window) if L.window > 0 else p + 1
+            fl_sample += 4.0 * w.d_h * w.n_q * n
+            n_rows += 1
+            checks.append(float(np.max(np.abs(o - out_gpu[b, tq]))))
+        del K, V
+    est = t_fixed + t_attn * (fl_total / fl_sample)
+    return {"value": round(fl_total / est / 1e12, 6), "unit": "TFLOP/s", "est_step_s": round(est, 2),
+            "sample": "fp64 numpy oracle on %s: RoPE of all Q and K of the chunk and the append "
+                      "(%.2f s) plus attention of %d seeded random query rows (all heads, %.2f s, "
+                      "%.3g of the step's flops); whole-step time extrapolated by flops" % (
+                          w.name, t_fixed, n_rows, t_attn, fl_sample / fl_total),
             "parity_sample_max_abs": round(max(checks), 5) if checks else None}
+
+
+def cpu_decode_sample(w, budget_s):
+    """The oracle on the long-context decode workload: one decode query (all
+    heads of one sequence) of the full layer at the first step's position,
+    against sequence 0's pre-filled rows (drawn as the GPU run draws them)
+    plus the appended row, timed repeatedly; the 64 steps of all sequences
+    of both layers are extrapolated by algorithmic bytes (the oracle's cost
+    is the pass over the allowed rows)."""
+    import workloads as wl
+    from oracle.attention import attend_query
+    from oracle.rounding import round_to
+    from oracle.yarn import rope_apply, yarn_concentration, yarn_inv_freq
+
+    y = w.yarn
+    inv = yarn_inv_freq(w.d_h, y.base, y.factor, y.orig_ctx, y.alpha, y.beta)
+    c = yarn_concentration(y.factor)
+    pk = wl.normal((1, w.prefix, w.n_kv, w.d_h), w.dtype, w.seed, w.cfg_idx, 0, wl.T_PREFIX_K)
+    pv = wl.normal((1, w.prefix, w.n_kv, w.d_h), w.dtype, w.seed, w.cfg_idx, 0, wl.T_PREFIX_V)
+    tok = wl.decode_token(w, 0, 0)
+    t = time.perf_counter()
+    p = w.prefix
+    q_rot = round_to(rope_apply(tok["q"][:1].astype(np.float64), p, inv, c), "bf16")
+    k_rot = round_to(rope_apply(tok["k"][:1].astype(np.float64), p, inv, c), "bf16")
+    K = np.concatenate([pk.astype(np.float64), k_rot], axis=1)
+    V = np.concatenate([pv.astype(np.float64), tok["v"][:1].astype(np.float64)], axis=1)
+    t_fixed = time.perf_counter() - t
+    sinks = wl.sinks(w, 0)
+    n, t_attn = 0, 0.0
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < budget_s or n == 0:
+        t = time.perf_counter()
+        attend_query(q_rot[0, 0], K[0], V[0], sinks, p, 0, w.sm_scale)
+        t_attn += time.perf_counter() - t
+        n += 1
+    by_call = decode_bytes(w.with_(B=1), p, 0)
+    by_total = sum(decode_bytes(w, w.prefix + s, W) for s in range(w.decode_steps) for W in w.windows)
+    fl_total = sum(attn_flops(w.B, w.n_q, w.d_h, w.prefix + s, 1, W)
+                   for s in range(w.decode_steps) for W in w.windows)
+    est = t_fixed + (t_attn / n) * (by_total / by_call)
+    return {"value": round(by_total / est / 1e9, 3), "unit": "GB/s",
+            "tflops": round(fl_total / est / 1e12, 6), "est_64_steps_s": round(est, 1),
+            "sample": "fp64 numpy oracle on %s: %d timed decode queries (sequence 0, all heads, "
+                      "full layer, %d allowed rows, %.2f s each) plus RoPE and the append "
+                      "(%.2f s); all sequences, both layers and all %d steps extrapolated by "
+                      "algorithmic bytes" % (w.name, n, p + 1, t_attn / n, t_fixed, w.decode_steps)}
 
 
 def main():
@@ -671,56 +923,97 @@ def main():
         leg = {"sampling": sample_extra, "moe": moe_extra, "qkv": qkv_extra}[args.extra_only]
         print(json.dumps({args.extra_only: leg(sa, torch)}), flush=True)
         return
-    w = wl.LITE_PREFILL
-    layers, ms_step, kern_ms, in_step = time_prefill_step(w, sa, torch, args.steps, args.warmup)
-    fl_step = sum(attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window) for L in layers)
-    value = fl_step / (ms_step * 1e-3) / 1e12
-    per_layer = [prefill_figures(w, L, kern_ms[i], in_step[i]) for i, L in enumerate(layers)]
-    for i, p in IN_STEP_STATS.items():
-        per_layer[i]["kernel_ms_in_step_median"] = round(p[0], 4)
-        per_layer[i]["kernel_ms_in_step_min"] = round(p[1], 4)
-    step_stats = dict(STEP_STATS)
-    full = [p for p in per_layer if p["window"] == 0][0]
-    full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
+
+    # ---- the headline: the handover workload
+    w = wl.HANDOVER
+    t = time_handover(w, sa, torch, args.steps, args.warmup, args.settle_ms)
+    pre, dec = handover_flops(w)
+    fl_step = sum(pre.values()) + sum(dec.values())
+    value = fl_step / (t["ms_step"] * 1e-3) / 1e12
+    ho = handover_figures(w, t)
+    full = [f for f in ho["layers"] if f["window"] == 0][0]
+    traffic = TRAFFIC.get(("handover", 0))
     roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": full["frac_mfma"],
-                "traffic": (TRAFFIC_FULL_PREFILL["bytes"]
-                            if kernel_sources_hash() == TRAFFIC_FULL_PREFILL["sources_sha256_16"]
-                            else None),
+                "traffic": (traffic["bytes"] if traffic and
+                            kernel_sources_hash() == traffic["sources_sha256_16"] else None),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                 "kernel": prefill_kernel_name(w.d_h, False) + " (full causal)",
+                "kernel_gflop": full["gflop"],
                 "kernel_ms": full["kernel_ms"], "kernel_timing": full["kernel_timing"]}
     line = {
         "metric": "sink-GQA attention prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "step_spread": {"median_ms": round(step_stats["median"], 4), "min_ms": round(step_stats["min"], 4),
-                        "pass": "the same steps again after the timed region, an event at each step boundary"},
+        "warmup": args.warmup, "ms_per_step": round(t["ms_step"], 4),
+        "step_spread": {"median_ms": round(float(np.median(t["per_step"])), 4),
+                        "min_ms": round(float(np.min(t["per_step"])), 4),
+                        "pass": "the same steps again after the timed region, an event at each "
+                                "step boundary"},
         "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "global_batch": w.B, "seq_len": w.T, "n_q": w.n_q,
-                   "n_kv": w.n_kv, "d_h": w.d_h, "windows": list(w.windows),
+        "config": {"workload": w.name, "global_batch": w.B, "prefix_rows": w.prefix,
+                   "chunk": w.T, "decode_steps": "2 sweeps x %d (restore between)" % w.decode_steps,
+                   "n_q": w.n_q, "n_kv": w.n_kv, "d_h": w.d_h, "windows": list(w.windows),
                    "yarn": {"base": w.yarn.base, "factor": w.yarn.factor,
                             "orig_ctx": w.yarn.orig_ctx}, "parallelism": "single GPU"},
+        "settle": {"ms": args.settle_ms, "launches": t["settle_launches"],
+                   "what": "back-to-back full-causal prefill launches before the warmup steps, "
+                           "untimed, so the timed steps run at the clock this load holds"},
         "roofline": roofline,
-        "layers": per_layer,
-        "abi_calls": abi_call_figures(w, layers[full_i], sa, torch),
-        "ring": ring_prefill_figures(w, [L for L in layers if L.window > 0][0], sa, torch),
+        "handover": ho,
     }
+
+    # ---- long-context decode: the second headline figure (KV GB/s)
+    ld = decode_extra(sa, torch)
+    fd = ld["full"]
+    line["decode_kv"] = {"workload": ld["workload"], "layer": "full causal",
+                         "gbs": fd["gbs"], "frac_hbm": fd["frac_hbm"],
+                         "attn_kernel_us": fd["attn_kernel_us"], "step_us": fd["step_us"],
+                         "alg_mb_per_step": fd["alg_mb_per_step"], "peak_gbs": PEAK_HBM_GBS,
+                         "timing": "events around each step's attention launches (split-KV kernel "
+                                   "+ merge), 64 steps"}
+    cpu = {}
     if not args.no_extra:
+        lw = wl.LITE_PREFILL
+        layers, ms_step, kern_ms, in_step = time_prefill_step(lw, sa, torch, 20, 200)
+        fl = sum(attn_flops(lw.B, lw.n_q, lw.d_h, lw.prefix, lw.T, L.window) for L in layers)
+        per_layer = [prefill_figures(lw, L, kern_ms[i], in_step[i]) for i, L in enumerate(layers)]
+        for i, p in IN_STEP_STATS.items():
+            per_layer[i]["kernel_ms_in_step_median"] = round(p[0], 4)
+            per_layer[i]["kernel_ms_in_step_min"] = round(p[1], 4)
+        full_i = [i for i, L in enumerate(layers) if L.window == 0][0]
+        line["extra"] = {"gpt_oss_lite_prefill": {
+            "workload": lw.name, "ms_per_step": round(ms_step, 4),
+            "tflops_step": round(fl / (ms_step * 1e-3) / 1e12, 1), "layers": per_layer,
+            "abi_calls": abi_call_figures(lw, layers[full_i], sa, torch),
+            "ring": ring_prefill_figures(lw, [L for L in layers if L.window > 0][0], sa, torch)}}
+        if not args.no_cpu:
+            cpu["gpt-oss-lite prefill"] = cpu_prefill_sample(lw, layers, args.cpu_seconds)
+        del layers
+        torch.cuda.empty_cache()
         g = wl.GPTOSS_PREFILL
         gl, gms, gk, gin = time_prefill_step(g, sa, torch, 20, 200)
-        line["extra"] = {"gpt_oss_prefill": {"workload": g.name, "ms_per_step": round(gms, 4),
-                                             "layers": [prefill_figures(g, L, gk[i], gin[i])
-                                                        for i, L in enumerate(gl)]}}
+        fl = sum(attn_flops(g.B, g.n_q, g.d_h, g.prefix, g.T, L.window) for L in gl)
+        line["extra"]["gpt_oss_prefill"] = {"workload": g.name, "ms_per_step": round(gms, 4),
+                                            "tflops_step": round(fl / (gms * 1e-3) / 1e12, 1),
+                                            "layers": [prefill_figures(g, L, gk[i], gin[i])
+                                                       for i, L in enumerate(gl)]}
+        if not args.no_cpu:
+            cpu["gpt-oss prefill"] = cpu_prefill_sample(g, gl, args.cpu_seconds)
         del gl
         torch.cuda.empty_cache()
-        line["extra"]["long_decode"] = decode_extra(sa, torch)
+        line["extra"]["long_decode"] = ld
         line["extra"]["qkv_projection"] = qkv_extra(sa, torch)
         line["extra"]["moe_layer"] = moe_extra(sa, torch)
         line["extra"]["sampling"] = sample_extra(sa, torch)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, layers, args.cpu_seconds)
+        head = cpu_prefill_sample(w, t["layers"], 2 * args.cpu_seconds, extra_flops=sum(dec.values()))
+        cores, model = _cpu_info()
+        if not args.no_extra:
+            cpu["long decode"] = cpu_decode_sample(wl.LONG_DECODE, args.cpu_seconds)
+        line["cpu_baseline"] = {**head, "cores": cores, "cpu_model": model,
+                                "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "per_workload": cpu}
     print(json.dumps(line), flush=True)
 
 

@@ -25,9 +25,11 @@
 //    cross-lane max and a rescale of O and l) only when a lane's tile sum
 //    passes 2^64 or a query has no reference yet, in a slow path outside the
 //    steady-state loop; so most tiles need no max, no cross-lane traffic and
-//    no accumulator rescale, and nothing comes near overflow.  Probabilities are rounded
-//    to bf16 once (v_cvt_pk_bf16_f32) and the row sums accumulate those same
-//    rounded values (v_dot2c_f32_bf16), so numerator and denominator agree.
+//    no accumulator rescale, and nothing comes near overflow.  Probabilities
+//    are rounded to bf16 once (v_cvt_pk_bf16_f32); their row sums come from
+//    the matrix cores (an all-ones A operand times the same P^T the PV product
+//    uses), so numerator and denominator agree and the vector units, which
+//    bound the unit, do no summing.
 //  * Masks are computed from positions, only on tiles that cross the
 //    diagonal or the band edge; rows past the last query position are
 //    zero-filled in LDS, so unwritten cache rows are never read.
@@ -125,8 +127,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   int tpos[NT], head[NT];
   bool rvalid[NT];
   u32x4 qop[NT][KS];
-  float m_run[NT], l_run[NT];
-  float neg_ref[NT];   // -m_run, or 0 while there is no reference (m_run = -inf)
+  // Softmax state per query column (every lane of the column holds it):
+  // the reference is -neg_ref, and l_run the sum of the weights against it
+  // (the sink's included).  l_run == 0 means nothing has been weighed yet
+  // (no sink and no allowed key seen): there is no reference, and neg_ref
+  // is 0 until the slow path sets one.
+  float l_run[NT];
+  float neg_ref[NT];
   f32x4 O[DT][NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -142,9 +149,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int ks = 0; ks < KS; ++ks)
       qop[n][ks] = rvalid[n] ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
     const float sg = a.sinks[head[n]] * SA_LOG2E;
-    m_run[n] = sg;                                   // -inf when the sink is off
     neg_ref[n] = sg == -INFINITY ? 0.f : -sg;
-    l_run[n] = (g4 == 0 && sg != -INFINITY) ? 1.0f : 0.0f;
+    l_run[n] = sg != -INFINITY ? 1.0f : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // ---- the parts of a unit of 32 keys (half a tile; key half h of tile t
   // holds keys 64t + 32h + [0, 32)): scores S^T = K Q^T (masked on units
   // that cross the diagonal or the band edge), probabilities against the
-  // current reference m_run, and O^T += V^T P^T.
+  // current reference, and O^T += V^T P^T.
   struct Scores { f32x4 v[2][NT]; };
   auto scores = [&](Scores& S, int buf, int h) {
 #pragma unroll
@@ -357,23 +363,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
         }
     }
   };
-  // p = 2^(s*scale - m_run), rounded to bf16 once; ls = this lane's sum of
-  // those rounded values (v_dot2 against 1).
-  auto probs = [&](const Scores& S, u32x4 (&Pk)[NT], float (&ls)[NT]) {
+  // p = 2^(s*scale + neg_ref), rounded to bf16 once.
+  auto probs = [&](const Scores& S, u32x4 (&Pk)[NT]) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      float acc = 0.f;
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const float p0 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1)], scale, neg_ref[n]));
         const float p1 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1) + 1], scale, neg_ref[n]));
         w[e2] = pack_bf16x2(p0, p1);
-        acc = sum_bf16x2(w[e2], acc);
       }
       Pk[n] = u32x4{w[0], w[1], w[2], w[3]};
-      ls[n] = acc;
     }
+  };
+  // A unit's row sums on the matrix cores: with A all ones, every row of
+  // ONES P^T is the column sum, so each lane receives its query's sum over
+  // the unit's 32 keys, of the same rounded values the PV product uses.
+  // (This keeps the sums off the vector units, which bound the unit.)
+  auto unit_sums = [&](const u32x4 (&Pk)[NT], float (&ls)[NT]) {
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int n = 0; n < NT; ++n) ls[n] = mfma16x16x32(ones, Pk[n], f32x4{0.f, 0.f, 0.f, 0.f})[0];
   };
   auto pv = [&](int buf, int h, const u32x4 (&Pk)[NT]) {
 #pragma unroll
@@ -417,23 +428,24 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 #pragma unroll
       for (int n = 0; n < NT; ++n) O[dt][n] = mfma16x16x32(o.v[dt], Pk[n], O[dt][n]);
   };
-  // Move the reference to the true running max (column max across the four
-  // lanes of a query) and rescale what has been accumulated.
-  auto rescale = [&](const Scores& S) {
+  // Move the reference to the true running max over the scores of Sa and
+  // Sb (column max across the four lanes of a query) and rescale what has
+  // been accumulated.
+  auto rescale = [&](const Scores& Sa, const Scores& Sb) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float mx = -INFINITY;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S.v[mm][n][r]);
-      const float m_new = fmaxf(m_run[n], max_over_col(mx) * scale);
-      // m_run == -inf: nothing accumulated yet (and m_new may be -inf too)
-      const float alpha = (m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fmaxf(Sa.v[mm][n][r], Sb.v[mm][n][r]));
+      const bool none = l_run[n] == 0.f;             // no reference yet (O is 0 too)
+      const float m_cur = none ? -INFINITY : -neg_ref[n];
+      const float m_new = fmaxf(m_cur, max_over_col(mx) * scale);
+      const float alpha = none ? 0.f : fast_exp2(m_cur - m_new);
       l_run[n] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
-      m_run[n] = m_new;
       neg_ref[n] = m_new == -INFINITY ? 0.f : -m_new;
     }
   };
@@ -444,17 +456,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 
   // ---- software pipeline over units.  Unit u computes S(u+1) and
   // O += V(u-1) P(u-1) on the matrix cores while the vector units turn S(u)
-  // into P(u), all in one stretch of straight-line code.  Tile t (units 2t
-  // and 2t+1) first starts the loads of K(t+2) and V(t+1) into LDS and ends
-  // with one barrier.  K and V have three LDS buffers each; with
-  // (b0, b1, b2) rotating one place per tile, K(t), K(t+1), K(t+2) sit in
-  // b0, b1, b2 and V(t-1), V(t), V(t+1) in b2, b0, b1.  After each unit,
-  // P(u) is checked: the reference m_run stays put while every lane's unit
-  // sum stays below 2^64 (so no exponential, partial sum or accumulator
-  // comes near fp32/bf16 overflow); a unit that breaks that, or a query with
-  // no reference yet (no sink and nothing seen), recomputes S(u) from K (still
-  // in LDS), moves the reference to the running max, rescales O (which then
-  // holds units up to u-1) and recomputes P(u).
+  // into P(u), all in one stretch of straight-line code; the row sums of
+  // P(u) then go to the matrix cores too.  Tile t (units 2t and 2t+1) first
+  // starts the loads of K(t+2) and V(t+1) into LDS and ends with one
+  // barrier.  K and V have three LDS buffers each; with (b0, b1, b2)
+  // rotating one place per tile, K(t), K(t+1), K(t+2) sit in b0, b1, b2 and
+  // V(t-1), V(t), V(t+1) in b2, b0, b1.  After each unit, P(u) is checked:
+  // the reference stays put while every lane's unit sum stays below 2^64
+  // (so no exponential, partial sum or accumulator comes near fp32/bf16
+  // overflow); a unit that breaks that, or a query with no reference yet
+  // (no sink and nothing seen), recomputes S(u) from K (still in LDS), moves
+  // the reference to the running max, rescales O (which then holds units up
+  // to u-1) and recomputes P(u) and its sums.
   const int t0 = t_first;
   int b0 = 0, b1 = 1, b2 = 2;
   load_k(0, t0);
@@ -494,10 +507,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     // waves per SIMD, is faster mixed).
     if constexpr (kPhaseSplit) __builtin_amdgcn_sched_barrier(0);
     if constexpr (kOpsAhead) load_ops(on, kbx, hx, vbx, vx);
-    probs(Sc, Pc, ls);
+    probs(Sc, Pc);
+    unit_sums(Pc, ls);
     bool bad = false;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || m_run[n] == -INFINITY;
+    for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || l_run[n] == 0.f;
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       // The compiler may not hoist this recomputation onto the fast path
       // (LDS reads can be speculated): the clobber pins it here.
@@ -505,8 +519,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       Scores Sr;
       scores(Sr, kbc, hc);
       if (need_mask(k0c)) apply_mask(Sr, k0c);
-      rescale(Sr);
-      probs(Sr, Pc, ls);
+      rescale(Sr, Sr);
+      probs(Sr, Pc);
+      unit_sums(Pc, ls);
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
@@ -542,7 +557,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const float inv = 1.0f / sum_over_col(l_run[n]);
+    const float inv = 1.0f / l_run[n];
     if (!rvalid[n]) continue;
     uint16_t* orow = out + (((int64_t)b * a.T_q + tpos[n]) * a.n_q + head[n]) * D;
 #pragma unroll
