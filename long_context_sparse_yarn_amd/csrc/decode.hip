@@ -28,8 +28,10 @@
 //      M = max(sigma', max_c m_c), L = 2^(sigma'-M) + sum_c l_c 2^(m_c-M),
 //      out = sum_c acc_c 2^(m_c-M) / L        (sigma' = sigma * log2 e).
 //    Splits with no allowed key carry m = -inf, l = 0 and drop out.  A span
-//    of at most 256 rows (a band layer) runs as one split per (b, g), whose
-//    wave adds the sink and writes the output itself.
+//    of at most 256 rows (a band layer) runs in one launch instead: a
+//    workgroup per (b, g) whose waves take one or two 32-key blocks each and
+//    fold their partials in LDS in the same fixed way, so a band step costs
+//    one block's memory latency rather than a chain of them.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -42,7 +44,7 @@ constexpr int kThreads = kWaves * 64;
 #endif
 constexpr int kTargetWaves = SA_DEC_WAVES;
 constexpr int kMaxSplits = 256;
-constexpr int64_t kSingleSplitRows = 256;   // spans this short skip the split/merge
+constexpr int64_t kSingleSplitRows = 256;   // spans this short run as one short launch
 constexpr float kSlack = 8.0f;
 
 template <int D>
@@ -70,46 +72,26 @@ __device__ __forceinline__ void load_block(BlockOps<D>& o, const uint16_t* kbase
     o.v[dt] = ld16(vblk + (16 * dt + j) * 32 + 8 * g4);
 }
 
+// One wave's pass over cache blocks [b0, b1) of sequence b, KV head g (keys
+// of the allowed range [lo, hi) only): lane (j, g4) ends with the running
+// reference m_run (base-2 units; -inf while nothing is allowed), its share
+// l_run of the sum of weights (the column's four lanes add up to the sum)
+// and O^T[16 dt + 4 g4 + r][head j] against that reference.  No sink.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
+__device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, int64_t b0,
+                                              int64_t b1, int64_t lo, int64_t hi,
+                                              const u32x4 (&qop)[D / 32], float& m_run,
+                                              float& l_run, f32x4 (&O)[D / 16]) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  const AttnArgs& a = da.at;
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g4 = lane >> 4;
-  const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int S = da.n_splits;
-  const int pairs = a.B * a.n_kv;
-  if (wid >= pairs * S) return;
-  // KV head fastest: waves running side by side read whole cache rows
-  // (all heads of a row are contiguous) and whole 32-key V blocks.
-  const int g = wid % a.n_kv;
-  const int split = (wid / a.n_kv) % S;
-  const int b = wid / (a.n_kv * S);
-  const int pair = b * a.n_kv + g;
   const int64_t C = a.C;
-
-  const int64_t P = a.q_offset;                         // query position
-  const int64_t lo = a.window > 0 ? max((int64_t)0, P - a.window + 1) : 0;
-  const int64_t hi = P + 1;
-  const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
-  const int64_t b0 = kb_lo + (split * nblk) / S;
-  const int64_t b1 = kb_lo + ((split + 1) * nblk) / S;
-
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc);
-
-  // Q^T operand: column j = head g*q_mult + j (zero past q_mult)
-  u32x4 qop[KS];
-  const bool qv = j < a.q_mult;
-  const uint16_t* qrow = q + ((int64_t)b * a.n_q + g * a.q_mult + (qv ? j : 0)) * D;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qop[ks] = qv ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
-
   const float scale = a.sm_scale * SA_LOG2E;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 O[DT];
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -203,28 +185,52 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
       cur[1] = nxt[1];
     }
   }
+}
 
-  l_run = sum_over_col(l_run);
-  if (S == 1) {
-    // One split: fold in the sink here and write the output (no merge pass).
-    if (j < a.q_mult) {
-      const int h = g * a.q_mult + j;
-      const float sg = a.sinks[h] * SA_LOG2E;
-      const float M = fmaxf(m_run, sg);
-      const float wr = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-      const float L = l_run * wr + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
-      const float f = wr / L;
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D;
+// The Q^T operand of (b, g): column j = head g*q_mult + j (zero past q_mult).
+template <int D>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, u32x4 (&qop)[D / 32]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g4 = lane >> 4;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  const bool qv = j < a.q_mult;
+  const uint16_t* qrow = q + ((int64_t)b * a.n_q + g * a.q_mult + (qv ? j : 0)) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 o = O[dt] * f;
-        *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * g4) =
-            u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-      }
-    }
-    return;
-  }
-  // ---- partial of this split: lanes (j < q_mult)
+  for (int ks = 0; ks < D / 32; ++ks) qop[ks] = qv ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
+}
+
+// Split-KV partials: one wave per (b, g, split) over its run of the allowed
+// blocks, written to the workspace for the merge.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
+  constexpr int DT = D / 16;
+  const AttnArgs& a = da.at;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int S = da.n_splits;
+  const int pairs = a.B * a.n_kv;
+  if (wid >= pairs * S) return;
+  // KV head fastest: waves running side by side read whole cache rows
+  // (all heads of a row are contiguous) and whole 32-key V blocks.
+  const int g = wid % a.n_kv;
+  const int split = (wid / a.n_kv) % S;
+  const int b = wid / (a.n_kv * S);
+  const int pair = b * a.n_kv + g;
+
+  const int64_t P = a.q_offset;                         // query position
+  const int64_t lo = a.window > 0 ? max((int64_t)0, P - a.window + 1) : 0;
+  const int64_t hi = P + 1;
+  const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
+  const int64_t b0 = kb_lo + (split * nblk) / S;
+  const int64_t b1 = kb_lo + ((split + 1) * nblk) / S;
+
+  u32x4 qop[D / 32];
+  load_q<D>(a, b, g, qop);
+  float m_run, l_run;
+  f32x4 O[DT];
+  decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O);
+  l_run = sum_over_col(l_run);
   if (j < a.q_mult) {
     const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + j;
     float* acc = da.ws + slot * D;
@@ -239,10 +245,80 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   }
 }
 
-// One workgroup per (b, h).  Thread s < S takes split s's (m, l); the
-// weighted sum of the accumulators runs with the splits dealt round-robin to
-// thread groups (16-byte loads), then the groups are added in group order.
-// Every sum has a fixed order, so the result is deterministic.
+// A span of at most kShortRows rows (a band layer, or the first steps of a
+// sequence) in one launch with no workspace: a workgroup per (b, g) whose
+// waves take one or two 32-key blocks each; the partials meet in LDS and are
+// folded in wave order, with the sink added once, by all of the workgroup's
+// threads.
+// Eight waves at d = 64; four at d = 96 and 128, whose per-wave pass needs
+// more registers than two waves per SIMD leave it.
+template <int D>
+constexpr int short_waves() { return D == 64 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_bf16_kernel(AttnArgs a) {
+  constexpr int DT = D / 16;
+  constexpr int kShortWaves = short_waves<D>();
+  constexpr int kShortThreads = kShortWaves * 64;
+  __shared__ __attribute__((aligned(16))) float acc_s[kShortWaves][16][D];
+  __shared__ float m_s[kShortWaves][16], l_s[kShortWaves][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int pair = blockIdx.x;
+  const int b = pair / a.n_kv, g = pair - (pair / a.n_kv) * a.n_kv;
+
+  const int64_t P = a.q_offset;
+  const int64_t lo = a.window > 0 ? max((int64_t)0, P - a.window + 1) : 0;
+  const int64_t hi = P + 1;
+  const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
+  const int64_t b0 = kb_lo + (wave * nblk) / kShortWaves;
+  const int64_t b1 = kb_lo + ((wave + 1) * nblk) / kShortWaves;
+
+  u32x4 qop[D / 32];
+  load_q<D>(a, b, g, qop);
+  float m_run, l_run;
+  f32x4 O[DT];
+  decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O);
+  l_run = sum_over_col(l_run);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4*>(&acc_s[wave][j][16 * dt + 4 * g4]) = O[dt];
+  if (g4 == 0) {
+    m_s[wave][j] = m_run;
+    l_s[wave][j] = l_run;
+  }
+  __syncthreads();
+  // fold: thread -> (head jq, 4 coordinates)
+  constexpr int CPH = D / 4;
+  for (int i = threadIdx.x; i < a.q_mult * CPH; i += kShortThreads) {
+    const int jq = i / CPH, c = i - jq * CPH;
+    const int h = g * a.q_mult + jq;
+    const float sg = a.sinks[h] * SA_LOG2E;
+    float M = sg;
+#pragma unroll
+    for (int w = 0; w < kShortWaves; ++w) M = fmaxf(M, m_s[w][jq]);
+    float L = (sg == -INFINITY) ? 0.f : fast_exp2(sg - M);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kShortWaves; ++w) {
+      const float mw = m_s[w][jq];
+      const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      L += l_s[w][jq] * sc;
+      o += *reinterpret_cast<const f32x4*>(&acc_s[w][jq][4 * c]) * sc;
+    }
+    o *= 1.0f / L;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D + 4 * c;
+    *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+  }
+}
+
+// One workgroup per (b, h).  Every global load is issued first: thread s < S
+// takes split s's (m, l), and the accumulators are dealt round-robin over the
+// splits to groups of threads (16-byte loads, held in registers); then the
+// maximum and the weights, the weighted sums per group, and the groups added
+// in group order.  Every sum has a fixed order, so the result is
+// deterministic.
 constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
@@ -261,6 +337,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs da) {
   constexpr int CPS = D / 4;                        // f32x4 vectors per split
   constexpr int G = kMergeThreads / CPS;            // split groups
+  constexpr int KMAX = (kMaxSplits + G - 1) / G;    // splits per group at most
   __shared__ float wsh[kMaxSplits];
   __shared__ float red[kMergeThreads / 64];
   __shared__ f32x4 part[G][CPS];
@@ -273,23 +350,34 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int pairs = a.B * a.n_kv;
   const int pair = b * a.n_kv + g;
   const float* ml = da.ws + (int64_t)pairs * S * a.q_mult * D;
-  const float sg = a.sinks[h] * SA_LOG2E;
   const int64_t slot0 = ((int64_t)pair * S) * a.q_mult + jq;   // slot of split 0
   const int64_t sstride = a.q_mult;                            // slots between splits
 
+  const int grp = tid / CPS, c = tid - grp * CPS;
+  f32x4 accs[KMAX];
+  const float* src = da.ws + slot0 * D + 4 * c;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int sp = grp + k * G;
+    accs[k] = (grp < G && sp < S) ? *reinterpret_cast<const f32x4*>(src + sp * sstride * D)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float m = tid < S ? ml[2 * (slot0 + tid * sstride)] : -INFINITY;
+  const float lv = tid < S ? ml[2 * (slot0 + tid * sstride) + 1] : 0.f;
+  const float sg = a.sinks[h] * SA_LOG2E;
+
   const float M = fmaxf(sg, block_reduce(m, red, true));
   const float w = (tid < S && m != -INFINITY) ? fast_exp2(m - M) : 0.f;
   if (tid < S) wsh[tid] = w;
-  const float lpart = tid < S ? ml[2 * (slot0 + tid * sstride) + 1] * w : 0.f;
-  const float L = block_reduce(lpart, red, false) + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
-
-  const int grp = tid / CPS, c = tid - grp * CPS;
+  const float L = block_reduce(lv * w, red, false) + ((sg == -INFINITY) ? 0.f : fast_exp2(sg - M));
+  // block_reduce's barriers made wsh visible
   if (grp < G) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float* src = da.ws + slot0 * D + 4 * c;
-    for (int s = grp; s < S; s += G)
-      acc += *reinterpret_cast<const f32x4*>(src + s * sstride * D) * wsh[s];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int sp = grp + k * G;
+      if (sp < S) acc += accs[k] * wsh[sp];
+    }
     part[grp][c] = acc;
   }
   __syncthreads();
@@ -305,11 +393,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  if (a.n_splits == 1) {
+    hipLaunchKernelGGL(decode_short_bf16_kernel<D>, dim3(a.at.B * a.at.n_kv),
+                       dim3(short_waves<D>() * 64), 0, s, a.at);
+    return hipGetLastError();
+  }
   const int waves = a.at.B * a.at.n_kv * a.n_splits;
   const int grid = (waves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -317,7 +410,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 int decode_splits(int B, int n_kv, int64_t span_rows) {
-  if (span_rows <= kSingleSplitRows) return 1;       // short span: one wave per (b, g)
+  if (span_rows <= kSingleSplitRows) return 1;       // short span: one workgroup per (b, g)
   const int64_t nblk = (span_rows + 31) / 32 + 1;   // a span may straddle one more block
   int64_t s = (kTargetWaves + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   if (s > nblk) s = nblk;
