@@ -469,6 +469,28 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks,
                     float sm_scale, void* workspace, size_t ws_bytes,
                     void* stream);
 
+/* Bytes of the static device array that sinkattn_decode_noalloc keeps its
+ * split partials in (one copy per GPU, held until the process ends). */
+#define SA_DECODE_SCRATCH_BYTES (8u << 20)
+size_t sinkattn_decode_scratch_bytes(void);
+
+/* sinkattn_decode with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * may not call hipMalloc, harnesses that forbid it.  Same arguments (less
+ * the workspace), same kernels, same results bit for bit.  The split
+ * partials go to a static device array of SA_DECODE_SCRATCH_BYTES (8 MiB)
+ * on the current device; its address is looked up (hipGetSymbolAddress)
+ * on the first call on each device.  The call allocates and frees nothing.
+ * SA_ERR_ARG, with nothing enqueued, when this call's partials need more
+ * than the array holds (B * n_q * splits * (d_h + 2) * 4 bytes; e.g. the
+ * B = 8, 64/8-head, d_h = 64 long-context decode needs 4.3 MB); spans of at
+ * most 256 rows need none.  Every call on one GPU shares that GPU's array
+ * and leaves its partials there: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller. */
+int sinkattn_decode_noalloc(const void* q, const sa_kv_cache* c, const float* sinks,
+                            void* out, int B, int n_q, int n_kv, int d_h, int window,
+                            float sm_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

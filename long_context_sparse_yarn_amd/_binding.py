@@ -101,6 +101,9 @@ _sample_tokens = _sig("sample_tokens", _i32, _vp, _i32, _i32, _i64, _vp, _i64, _
 _sinkattn_decode_ws = _sig("sinkattn_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i64)
 _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                         _i32, _f32, _vp, _sz, _vp)
+_sinkattn_decode_noalloc = _sig("sinkattn_decode_noalloc", _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                _i32, _i32, _i32, _f32, _vp)
+_sinkattn_decode_scratch_bytes = _sig("sinkattn_decode_scratch_bytes", _sz)
 
 
 class SinkAttnError(RuntimeError):
@@ -544,6 +547,29 @@ def sinkattn_decode(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window
                             _dev(workspace, "workspace"), _nbytes(workspace),
                             _stream(stream)))
     return out
+
+
+def sinkattn_decode_noalloc(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor, window: int,
+                            sm_scale: float, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """sinkattn_decode without a workspace: the split partials live in the
+    library's static per-GPU scratch (calls on one GPU must not overlap)."""
+    B, T1, n_q, d = q.shape
+    if T1 != 1:
+        raise ValueError("decode takes exactly one query token per sequence")
+    if sinks.dtype != torch.float32 or sinks.numel() != n_q:
+        raise ValueError("sinks must be float32 [n_q]")
+    if q.dtype != cache.dtype:
+        raise TypeError("q dtype differs from the cache's")
+    out = _out_like(q, out)
+    _check(_sinkattn_decode_noalloc(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"),
+                                    _dev(out, "out"), B, n_q, cache.n_kv, d, int(window),
+                                    float(sm_scale), _stream(stream)))
+    return out
+
+
+def decode_scratch_bytes() -> int:
+    return int(_sinkattn_decode_scratch_bytes())
 
 
 def sample_params(B: int, temperature=1.0, top_k=0, top_p=1.0, min_p=0.0, repetition=1.0,

@@ -12,6 +12,7 @@
 #include <vector>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/sinkattn.h"
 #include "sa_kernels.h"
@@ -73,6 +74,42 @@ int yarn_table(const sa_yarn* y, int d_h, double* inv, double* conc) {
 
 std::atomic<uint64_t> g_next_id{1};
 
+}  // namespace
+
+// Decode partials of sinkattn_decode_noalloc: a static device array (each
+// GPU the library runs on holds its own copy until the process ends).  On
+// the host `scratch` names a stand-in, not a device address: its address on
+// a device comes from hipGetSymbolAddress, asked once per device with that
+// device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address in *out when `need` bytes fit;
+// SA_ERR_ARG (nothing touched) when they do not.
+int static_scratch(size_t need, void** out) {
+  if (need > (size_t)SA_DECODE_SCRATCH_BYTES)
+    return fail(SA_ERR_ARG,
+                "decode needs %zu bytes of partials, the static scratch holds %zu: use "
+                "sinkattn_decode with a workspace", need, (size_t)SA_DECODE_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
 }  // namespace
 
 // Offsets, high-water marks and rewrite records are global positions.  A
@@ -911,9 +948,16 @@ size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h, int64_
   return (size_t)((int64_t)B * n_q * S * (d_h + 2) * 4);
 }
 
-int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
-                    int n_q, int n_kv, int d_h, int window, float sm_scale, void* workspace,
-                    size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The decode launch behind both decode entry points.  With a caller
+// workspace (ws_static false) it must hold the bound for the cache's whole
+// capacity; with ws_static the partials go to this library's static device
+// array (below), which must hold what this call's split count needs.
+int decode_impl(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
+                int n_q, int n_kv, int d_h, int window, float sm_scale, void* workspace,
+                size_t ws_bytes, bool ws_static, void* stream) {
   int st = check_attn(q, c, sinks, out, B, 1, n_q, n_kv, d_h);
   if (st != SA_OK) return st;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SA_ERR_ARG, "sm_scale must be finite and > 0");
@@ -958,15 +1002,22 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
     if (d_h != 64 && d_h != 96 && d_h != 128)
       return fail(SA_ERR_SHAPE, "bf16 attention supports d_h in {64, 96, 128}, got %d", d_h);
     if (q_mult > 16) return fail(SA_ERR_SHAPE, "bf16 decode needs n_q/n_kv <= 16");
-    const size_t need = sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, c->capacity);
-    if (!workspace || ws_bytes < need || misaligned(workspace))
-      return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     const int64_t rows = q_row + 1;
     const int64_t span = a.window > 0 ? std::min<int64_t>(a.window, rows) : rows;
     DecodeArgs da;
     da.at = a;
-    da.ws = reinterpret_cast<float*>(workspace);
     da.n_splits = decode_splits(B, n_kv, span);
+    if (ws_static) {
+      const size_t need =
+          da.n_splits > 1 ? (size_t)((int64_t)B * n_q * da.n_splits * (d_h + 2) * 4) : 0;
+      st = static_scratch(need, &workspace);
+      if (st != SA_OK) return st;
+    } else {
+      const size_t need = sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, c->capacity);
+      if (!workspace || ws_bytes < need || misaligned(workspace))
+        return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    }
+    da.ws = reinterpret_cast<float*>(workspace);
     e = launch_decode_bf16(da, (hipStream_t)stream);
   } else {
     e = launch_attn_rows_f32(a, (hipStream_t)stream);
@@ -974,5 +1025,24 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
+}  // namespace
+
+extern "C" {
+
+int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
+                    int n_q, int n_kv, int d_h, int window, float sm_scale, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  return decode_impl(q, c, sinks, out, B, n_q, n_kv, d_h, window, sm_scale, workspace, ws_bytes,
+                     false, stream);
+}
+
+int sinkattn_decode_noalloc(const void* q, const sa_kv_cache* c, const float* sinks, void* out,
+                            int B, int n_q, int n_kv, int d_h, int window, float sm_scale,
+                            void* stream) {
+  return decode_impl(q, c, sinks, out, B, n_q, n_kv, d_h, window, sm_scale, nullptr, 0, true,
+                     stream);
+}
+
+size_t sinkattn_decode_scratch_bytes(void) { return (size_t)SA_DECODE_SCRATCH_BYTES; }
 
 }  // extern "C"

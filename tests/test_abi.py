@@ -246,6 +246,22 @@ def test_binding_checks_out_before_any_launch():
             B._out_like(q, bad)
 
 
+def test_noalloc_decode_refuses_what_its_scratch_cannot_hold():
+    """sinkattn_decode_noalloc checks its partials' size against the static
+    scratch before it touches the device: B 8, 128 query heads over 8 KV
+    heads at d 128 on a 2000-row span need 17 MB of partials."""
+    assert B._sinkattn_decode_scratch_bytes() == 8 << 20
+    st, h = create(Bn=8, C=2048, n_kv=8, d=128, offset=2000)
+    assert st == SA_OK
+    q, o, s = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000)
+    assert B._sinkattn_decode_noalloc(q, h, s, o, 8, 128, 8, 128, 0, 0.125, None) == SA_ERR_ARG
+    assert "static scratch" in sa.last_error()
+    # argument errors come first, as in sinkattn_decode
+    assert B._sinkattn_decode_noalloc(None, h, s, o, 8, 128, 8, 128, 0, 0.125, None) == SA_ERR_ARG
+    assert B._sinkattn_decode_noalloc(q, h, s, o, 8, 127, 8, 128, 0, 0.125, None) == SA_ERR_SHAPE
+    B._kv_cache_destroy(h)
+
+
 def ring(dtype=0, Bn=2, W=128, n_kv=2, d=64):
     h = ctypes.c_void_p()
     st = B._kv_ring_create(ctypes.byref(h), FAKE_K, FAKE_V, dtype, Bn, W, n_kv, d)
