@@ -104,8 +104,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // one LDS arena: three K tiles, three V^T tiles (and, before the first
   // tile arrives, the Q rotation table)
   __shared__ __attribute__((aligned(16))) uint16_t lds[3 * KBUF + 3 * VBUF];
-  auto Kb = [&](int buf) { return lds + buf * KBUF; };
-  auto Vb = [&](int buf) { return lds + 3 * KBUF + buf * VBUF; };
+  auto Kb = [&](int buf) __attribute__((always_inline)) { return lds + buf * KBUF; };
+  auto Vb = [&](int buf) __attribute__((always_inline)) { return lds + 3 * KBUF + buf * VBUF; };
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -127,12 +127,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   int tpos[NT], head[NT];
   bool rvalid[NT];
   u32x4 qop[NT][KS];
-  // Softmax state per query column (every lane of the column holds it):
-  // the reference is -neg_ref, and l_run the sum of the weights against it
-  // (the sink's included).  l_run == 0 means nothing has been weighed yet
-  // (no sink and no allowed key seen): there is no reference, and neg_ref
-  // is 0 until the slow path sets one.
-  float l_run[NT];
+  // Row sums of the probabilities: on the matrix cores at d = 64, where the
+  // vector units bound the unit (4% faster); at d = 96 and 128, where the
+  // matrix cores have more to do per unit, by v_dot2 on the vector units
+  // (the matrix-core sums cost d = 96 8%).
+  constexpr bool kMfmaSums = D == 64;
+  // Softmax state per query column: the reference is -neg_ref (m_ref on the
+  // v_dot2 path, -inf while there is none), l_run the sum of the weights
+  // against it, the sink's included (with matrix-core sums every lane of the
+  // column holds the whole sum; with v_dot2 sums each lane holds the sum over
+  // its own keys).  No reference (no sink and no allowed key seen yet):
+  // l_run == 0 (matrix-core sums) or m_ref == -inf; neg_ref is 0 until the
+  // slow path sets one.
+  float l_run[NT], m_ref[NT];
   float neg_ref[NT];
   f32x4 O[DT][NT];
 #pragma unroll
@@ -150,7 +157,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       qop[n][ks] = rvalid[n] ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
     const float sg = a.sinks[head[n]] * SA_LOG2E;
     neg_ref[n] = sg == -INFINITY ? 0.f : -sg;
-    l_run[n] = sg != -INFINITY ? 1.0f : 0.0f;
+    m_ref[n] = sg;
+    l_run[n] = (sg != -INFINITY && (kMfmaSums || g4 == 0)) ? 1.0f : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     const int c = (s & 3) ^ ((r >> 1) & 3);
     v_goff[i] = (uint32_t)((r >= D ? vblk_stride : 0) + (r % D) * 32 + 8 * c);
   }
-  auto load_k = [&](int buf, int t) {
+  auto load_k = [&](int buf, int t) __attribute__((always_inline)) {
     const int k0 = t * kTile;
     const uint16_t* kt = kbase + (int64_t)k0 * krow_stride;     // uniform
     const bool full = k0 + kTile <= hi;
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       }
     }
   };
-  auto load_v_full = [&](int buf, int t) {
+  auto load_v_full = [&](int buf, int t) __attribute__((always_inline)) {
     const uint16_t* vt = vbase + (int64_t)(t * (kTile / 32)) * vblk_stride;   // uniform
 #pragma unroll
     for (int i = 0; i < VBW; ++i) {
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // Register path: thread c of the workgroup moves chunks c, c + kThreads,
   // ... of the V^T tile (row = 32-key half * D + coordinate, chunk of 8
   // keys); zero = true writes zeros.
-  auto store_v_regs = [&](int buf, int t, bool zero) {
+  auto store_v_regs = [&](int buf, int t, bool zero) __attribute__((always_inline)) {
     const int k0 = t * kTile;
     const uint16_t* vt = vbase + (int64_t)(k0 / 32) * vblk_stride;
     for (int cidx = threadIdx.x; cidx < 8 * D; cidx += kThreads) {
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       st16(&Vb(buf)[v_lds(r, ch)], v);
     }
   };
-  auto load_v = [&](int buf, int t) {
+  auto load_v = [&](int buf, int t) __attribute__((always_inline)) {
     if (t * kTile + kTile <= hi)
       load_v_full(buf, t);
     else
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // that cross the diagonal or the band edge), probabilities against the
   // current reference, and O^T += V^T P^T.
   struct Scores { f32x4 v[2][NT]; };
-  auto scores = [&](Scores& S, int buf, int h) {
+  auto scores = [&](Scores& S, int buf, int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   };
   // Lane (j, g4) holds, for M tile mm and element r, the score of key
   // k0h + 8*g4 + 4*mm + r; keys after the query or outside its band get -inf.
-  auto apply_mask = [&](Scores& S, int k0h) {
+  auto apply_mask = [&](Scores& S, int k0h) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int rel0 = k0h + 8 * g4 - ((int)a.q_offset + tpos[n]);   // key - p at (mm, r) = 0
@@ -363,28 +371,33 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
         }
     }
   };
-  // p = 2^(s*scale + neg_ref), rounded to bf16 once.
-  auto probs = [&](const Scores& S, u32x4 (&Pk)[NT]) {
+  // p = 2^(s*scale + neg_ref), rounded to bf16 once; on the v_dot2 path ls
+  // receives this lane's sum of those rounded values.
+  auto probs = [&](const Scores& S, u32x4 (&Pk)[NT], float (&ls)[NT]) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
+      float acc = 0.f;
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const float p0 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1)], scale, neg_ref[n]));
         const float p1 = fast_exp2(fmaf(S.v[e2 >> 1][n][2 * (e2 & 1) + 1], scale, neg_ref[n]));
         w[e2] = pack_bf16x2(p0, p1);
+        if constexpr (!kMfmaSums) acc = sum_bf16x2(w[e2], acc);
       }
       Pk[n] = u32x4{w[0], w[1], w[2], w[3]};
+      if constexpr (!kMfmaSums) ls[n] = acc;
     }
   };
-  // A unit's row sums on the matrix cores: with A all ones, every row of
-  // ONES P^T is the column sum, so each lane receives its query's sum over
-  // the unit's 32 keys, of the same rounded values the PV product uses.
-  // (This keeps the sums off the vector units, which bound the unit.)
+  // A unit's row sums on the matrix cores (d = 64): with A all ones, every
+  // row of ONES P^T is the column sum, so each lane receives its query's sum
+  // over the unit's 32 keys, of the same rounded values the PV product uses.
   auto unit_sums = [&](const u32x4 (&Pk)[NT], float (&ls)[NT]) {
-    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    if constexpr (kMfmaSums) {
+      const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-    for (int n = 0; n < NT; ++n) ls[n] = mfma16x16x32(ones, Pk[n], f32x4{0.f, 0.f, 0.f, 0.f})[0];
+      for (int n = 0; n < NT; ++n) ls[n] = mfma16x16x32(ones, Pk[n], f32x4{0.f, 0.f, 0.f, 0.f})[0];
+    }
   };
   auto pv = [&](int buf, int h, const u32x4 (&Pk)[NT]) {
 #pragma unroll
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // (DT tiles, from V buffer vb, half vh).  Read one unit ahead, their LDS
   // latency hides behind the previous unit's vector work.
   struct Ops { u32x4 k[KS][2]; u32x4 v[DT]; };
-  auto load_ops = [&](Ops& o, int kb, int kh, int vb, int vh) {
+  auto load_ops = [&](Ops& o, int kb, int kh, int vb, int vh) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -410,7 +423,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o.v[dt] = ld16(&Vb(vb)[va_off + (vh * D + 16 * dt) * 32]);
   };
-  auto scores_ops = [&](Scores& S, const Ops& o) {
+  auto scores_ops = [&](Scores& S, const Ops& o) __attribute__((always_inline)) {
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // Move the reference to the true running max over the scores of Sa and
   // Sb (column max across the four lanes of a query) and rescale what has
   // been accumulated.
-  auto rescale = [&](const Scores& Sa, const Scores& Sb) {
+  auto rescale = [&](const Scores& Sa, const Scores& Sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float mx = -INFINITY;
@@ -439,18 +452,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fmaxf(Sa.v[mm][n][r], Sb.v[mm][n][r]));
-      const bool none = l_run[n] == 0.f;             // no reference yet (O is 0 too)
+      const bool none = kMfmaSums ? l_run[n] == 0.f : m_ref[n] == -INFINITY;   // O is 0 too
       const float m_cur = none ? -INFINITY : -neg_ref[n];
       const float m_new = fmaxf(m_cur, max_over_col(mx) * scale);
       const float alpha = none ? 0.f : fast_exp2(m_cur - m_new);
       l_run[n] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
+      m_ref[n] = m_new;
       neg_ref[n] = m_new == -INFINITY ? 0.f : -m_new;
     }
   };
   // Does the unit starting at key k0h need masking?
-  auto need_mask = [&](int k0h) {
+  auto need_mask = [&](int k0h) __attribute__((always_inline)) {
     return (k0h + 31 > P_min) || (a.window > 0 && k0h < P_max - a.window + 1);
   };
 
@@ -468,7 +482,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // (no sink and nothing seen), recomputes S(u) from K (still in LDS), moves
   // the reference to the running max, rescales O (which then holds units up
   // to u-1) and recomputes P(u) and its sums.
+  // The walk starts and stops on 32-key units (where the loop is peeled,
+  // below): when the first allowed key
+  // lies in the second half of the first tile, unit 2 t_first is skipped
+  // (the pipeline starts at unit 2 t_first + 1 with a zero P before it);
+  // when the last query lies in the first half of the last tile, unit
+  // 2 t_last + 1 is skipped (only P(2 t_last) still enters O).
+  // The loop is peeled (head and tail tiles outside it) only for the shapes
+  // whose registers allow the extra copies of the unit: at d = 96 with two
+  // N tiles per wave (and at d = 128) it would cost a wave per SIMD, so those
+  // walk whole tiles.
+  constexpr bool kPeel = D == 64 || (D == 96 && NT == 1);
   const int t0 = t_first;
+  const bool skip_head = kPeel && (lo & (kTile - 1)) >= 32;
+  const bool skip_tail = kPeel && ((hi - 1) & (kTile - 1)) < 32;
   int b0 = 0, b1 = 1, b2 = 2;
   load_k(0, t0);
   if (t0 + 1 <= t_last) load_k(1, t0 + 1);
@@ -479,9 +506,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   Scores S0, S1;
   u32x4 P0[NT], P1[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) P1[n] = u32x4{0, 0, 0, 0};
-  scores(S0, 0, 0);
-  if (need_mask(t0 * kTile)) apply_mask(S0, t0 * kTile);
+  for (int n = 0; n < NT; ++n) {
+    P0[n] = u32x4{0, 0, 0, 0};
+    P1[n] = u32x4{0, 0, 0, 0};
+  }
+  if (skip_head) {
+    scores(S1, 0, 1);
+    if (need_mask(t0 * kTile + 32)) apply_mask(S1, t0 * kTile + 32);
+  } else {
+    scores(S0, 0, 0);
+    if (need_mask(t0 * kTile)) apply_mask(S0, t0 * kTile);
+  }
 
   // One unit: Sc = S(u) in, Sn = S(u+1) out (from K buffer kbn, half hn,
   // first key k0n); Pp = P(u-1) in (V buffer vbp, half hp), Pc = P(u) out;
@@ -493,7 +528,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   auto unit = [&](const Scores& Sc, Scores& Sn, const u32x4 (&Pp)[NT], u32x4 (&Pc)[NT],
                   const Ops& oc, Ops& on, int kbx, int hx, int vbx, int vx,
                   int kbn, int hn, int k0n, int vbp, int hp, int kbc, int hc, int k0c,
-                  bool mask_next) {
+                  bool mask_next) __attribute__((always_inline)) {
     float ls[NT];
     if constexpr (kOpsAhead) {
       scores_ops(Sn, oc);
@@ -507,11 +542,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     // waves per SIMD, is faster mixed).
     if constexpr (kPhaseSplit) __builtin_amdgcn_sched_barrier(0);
     if constexpr (kOpsAhead) load_ops(on, kbx, hx, vbx, vx);
-    probs(Sc, Pc);
+    probs(Sc, Pc, ls);
     unit_sums(Pc, ls);
     bool bad = false;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom) || l_run[n] == 0.f;
+    for (int n = 0; n < NT; ++n)
+      bad |= !(ls[n] <= kHeadroom) || (kMfmaSums ? l_run[n] == 0.f : m_ref[n] == -INFINITY);
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       // The compiler may not hoist this recomputation onto the fast path
       // (LDS reads can be speculated): the clobber pins it here.
@@ -520,44 +556,91 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       scores(Sr, kbc, hc);
       if (need_mask(k0c)) apply_mask(Sr, k0c);
       rescale(Sr, Sr);
-      probs(Sr, Pc);
+      probs(Sr, Pc, ls);
       unit_sums(Pc, ls);
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) l_run[n] += ls[n];
     if (mask_next) apply_mask(Sn, k0n);
   };
-  // operands of unit 2 t0: K(t0) half 1, V(t0-1) half 1 (zeros)
+  // operands of unit 2 t0: K(t0) half 1, V(t0-1) half 1 (zeros); or, when
+  // that unit is skipped, those of unit 2 t0 + 1: K(t0+1) half 0, V(t0) half 0
   Ops OA, OB;
-  if constexpr (kOpsAhead) load_ops(OA, 0, 1, 2, 1);
-  for (int t = t0; t <= t_last; ++t) {
-    if (t + 2 <= t_last) load_k(b2, t + 2);
-    if (t + 1 <= t_last) load_v(b1, t + 1);
+  if constexpr (kOpsAhead) {
+    if (skip_head)
+      load_ops(OB, 1, 0, 0, 0);
+    else
+      load_ops(OA, 0, 1, 2, 1);
+  }
+  // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1.  It reads
+  // ahead the operands of unit 2t+1: K(t+1) half 0, V(t) half 0.
+  auto first_unit = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * kTile;
-    // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1.  It
-    // reads ahead the operands of unit 2t+1: K(t+1) half 0, V(t) half 0.
-    unit(S0, S1, P1, P0, OA, OB, b1, 0, b0, 0, b0, 1, k0 + 32, b2, 1, b0, 0, k0, need_mask(k0 + 32));
-    // unit 2t+1: S(2t+2) from K(t+1) half 0 (a throw-away after the last
-    // tile); P(2t) with V(t) half 0.  It reads ahead the operands of unit
-    // 2t+2: K(t+1) half 1 and V(t) half 1, which the loads of tile t+1 (into
-    // the buffers of K(t) and V(t-1)) leave in place; after the last tile
-    // they are stale and unused.
+    unit(S0, S1, P1, P0, OA, OB, b1, 0, b0, 0, b0, 1, k0 + 32, b2, 1, b0, 0, k0,
+         need_mask(k0 + 32));
+  };
+  // unit 2t+1: S(2t+2) from K(t+1) half 0 (a throw-away after the last tile);
+  // P(2t) with V(t) half 0.  It reads ahead the operands of unit 2t+2:
+  // K(t+1) half 1 and V(t) half 1, which the loads of tile t+1 (into the
+  // buffers of K(t) and V(t-1)) leave in place; after the last tile they are
+  // stale and unused.
+  auto second_unit = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * kTile;
     unit(S1, S0, P0, P1, OB, OA, b1, 1, b0, 1, b1, 0, k0 + kTile, b0, 0, b0, 1, k0 + 32,
          t < t_last && need_mask(k0 + kTile));
+  };
+  auto tile_loads = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 <= t_last) load_k(b2, t + 2);
+    if (t + 1 <= t_last) load_v(b1, t + 1);
+  };
+  auto tile_end = [&]() __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
     const int k = b0;
     b0 = b1;
     b1 = b2;
     b2 = k;
+  };
+  if constexpr (kPeel) {
+    int t = t0;
+    if (skip_head) {             // tile t0: its second unit only
+      tile_loads(t);
+      second_unit(t);
+      tile_end();
+      ++t;
+    }
+    for (; t < t_last; ++t) {    // whole tiles
+      tile_loads(t);
+      first_unit(t);
+      second_unit(t);
+      tile_end();
+    }
+    if (t == t_last) {           // the last tile (not reached when it was the skipped head's)
+      first_unit(t);
+      if (skip_tail) {
+        pv(b0, 0, P0);           // P(2 t_last) with V(t_last) half 0
+      } else {
+        second_unit(t);
+        pv(b0, 1, P1);           // P(2 t_last + 1) with V(t_last) half 1
+      }
+    } else {
+      pv(b2, 1, P1);             // P(2 t0 + 1) with V(t0) half 1 (rotated to b2)
+    }
+  } else {
+    for (int t = t0; t <= t_last; ++t) {
+      tile_loads(t);
+      first_unit(t);
+      second_unit(t);
+      tile_end();
+    }
+    pv(b2, 1, P1);               // P(2 t_last + 1) with V(t_last) half 1
   }
-  pv(b2, 1, P1);                 // P(2 t_last + 1) with V(t_last) half 1
 
   // ---- normalise and store: lane holds O^T[16*dt + 4*g4 + r][query]
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const float inv = 1.0f / l_run[n];
+    const float inv = 1.0f / (kMfmaSums ? l_run[n] : sum_over_col(l_run[n]));
     if (!rvalid[n]) continue;
     uint16_t* orow = out + (((int64_t)b * a.T_q + tpos[n]) * a.n_q + head[n]) * D;
 #pragma unroll
