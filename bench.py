@@ -796,14 +796,16 @@ def _cpu_info():
     return int(cores), model
 
 
-def cpu_prefill_sample(w, layers, budget_s, extra_flops=0.0):
+def cpu_prefill_sample(w, layers, budget_s, extra_flops=None):
     """The oracle as it stands on a bounded sample of a prefill step: RoPE
     of all of the chunk's Q and K (fp64), the append (the oracle's cache is
     the prefix with the rotated chunk after it), and attention of seeded
-    random query rows (all heads) per layer; the whole step's time is
-    extrapolated by algorithmic flops (extra_flops: decode queries of the
-    step, which cost the oracle what a prefill row of the same span does).
-    Also returns the largest difference between those oracle rows and the
+    random query rows (all heads) per layer.  Each layer's time is
+    extrapolated from its own sampled rows by algorithmic flops (a band
+    row and a full-causal row cost the oracle differently per flop);
+    extra_flops {window: flops} adds a layer's decode queries of the step,
+    which cost the oracle what its prefill rows of the same span do.  Also
+    returns the largest difference between the sampled oracle rows and the
     GPU's output rows."""
     from oracle.attention import attend_query
     from oracle.rounding import round_to
@@ -813,9 +815,11 @@ def cpu_prefill_sample(w, layers, budget_s, extra_flops=0.0):
     inv = yarn_inv_freq(w.d_h, y.base, y.factor, y.orig_ctx, y.alpha, y.beta)
     c = yarn_concentration(y.factor)
     rng = np.random.default_rng(0)
-    t_fixed = t_attn = fl_sample = 0.0
-    fl_total = float(extra_flops)
+    t_fixed = 0.0
+    est = 0.0
+    fl_total = fl_sampled = 0.0
     n_rows = 0
+    t_rows = 0.0
     checks = []
     per_layer = budget_s / len(layers)
     for L in layers:
@@ -829,10 +833,13 @@ def cpu_prefill_sample(w, layers, budget_s, extra_flops=0.0):
         else:
             K, V = k_rot, x["v"]
         t_fixed += time.perf_counter() - t
-        fl_total += attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window)
+        fl_layer = attn_flops(w.B, w.n_q, w.d_h, w.prefix, w.T, L.window)
+        if extra_flops:
+            fl_layer += extra_flops.get(L.window, 0.0)
         out_gpu = L.out.float().cpu().numpy()
+        t_attn = fl_sample = 0.0
         t_start = time.perf_counter()
-        while time.perf_counter() - t_start < per_layer:
+        while time.perf_counter() - t_start < per_layer or fl_sample == 0.0:
             b = int(rng.integers(w.B))
             tq = int(rng.integers(w.T))
             p = w.prefix + tq
@@ -843,13 +850,17 @@ def cpu_prefill_sample(w, layers, budget_s, extra_flops=0.0):
             fl_sample += 4.0 * w.d_h * w.n_q * n
             n_rows += 1
             checks.append(float(np.max(np.abs(o - out_gpu[b, tq]))))
+        est += t_attn * (fl_layer / fl_sample)
+        fl_total += fl_layer
+        fl_sampled += fl_sample
+        t_rows += t_attn
         del K, V
-    est = t_fixed + t_attn * (fl_total / fl_sample)
+    est += t_fixed
     return {"value": round(fl_total / est / 1e12, 6), "unit": "TFLOP/s", "est_step_s": round(est, 2),
             "sample": "fp64 numpy oracle on %s: RoPE of all Q and K of the chunk and the append "
                       "(%.2f s) plus attention of %d seeded random query rows (all heads, %.2f s, "
-                      "%.3g of the step's flops); whole-step time extrapolated by flops" % (
-                          w.name, t_fixed, n_rows, t_attn, fl_sample / fl_total),
+                      "%.3g of the step's flops); each layer's time extrapolated from its own rows "
+                      "by flops" % (w.name, t_fixed, n_rows, t_rows, fl_sampled / fl_total),
             "parity_sample_max_abs": round(max(checks), 5) if checks else None}
 
 
@@ -1007,7 +1018,7 @@ def main():
         line["extra"]["moe_layer"] = moe_extra(sa, torch)
         line["extra"]["sampling"] = sample_extra(sa, torch)
     if not args.no_cpu:
-        head = cpu_prefill_sample(w, t["layers"], 2 * args.cpu_seconds, extra_flops=sum(dec.values()))
+        head = cpu_prefill_sample(w, t["layers"], 2 * args.cpu_seconds, extra_flops=dec)
         cores, model = _cpu_info()
         if not args.no_extra:
             cpu["long decode"] = cpu_decode_sample(wl.LONG_DECODE, args.cpu_seconds)
