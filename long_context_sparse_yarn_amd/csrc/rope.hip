@@ -8,12 +8,13 @@
 //
 // Angles and the pair rotation: sa_rope.h.
 //
-// A workgroup takes a block of consecutive (b, t) rows (up to 32, about four
-// per thread) and all their heads.  Its threads build the block's (c*cos, c*sin) table in LDS
-// once (shared by every head) while their first loads are in flight; each
-// thread then owns one (head, 8-pair chunk) column and walks the rows two
-// at a time, loading both halves of the chunk and writing both rotated
-// halves.  Every output carries the bits of the pair's fp64 rotation rounded
+// A workgroup takes a block of positions t and a group of sequences b (up
+// to 32 rows (b, t), about four per thread) and all their heads.  Its
+// threads build the (c*cos, c*sin) table of the block's positions in LDS
+// once -- shared by every head and every sequence of the group -- while
+// their first loads are in flight; each thread then owns one (head, 8-pair
+// chunk) column and walks its rows, loading both halves of the chunk and
+// writing both rotated halves.  Every output carries the bits of the pair's fp64 rotation rounded
 // once to the storage type; for bf16 rows they come from fp32 arithmetic
 // where an error bound shows that it rounds the same way, and from fp64
 // otherwise (sa_rope.h), since a plain fp32 rotation would lose bf16 ulps
@@ -73,25 +74,35 @@ struct Rot<4> {                      // fp32: 8 values in two 16-byte vectors, f
   }
 };
 
+// Rows of a workgroup: sequences [b0, b0 + bg) x positions [t0, t0 + tb),
+// row r = (b0 + r / tb, t0 + r % tb); the table has tb rows.
 template <int ELT>
-__global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
+__global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int tb, int bg) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int half = a.d >> 1;
-  double2* cs = reinterpret_cast<double2*>(smem);          // [rows][half] fp64
-  float2* cs32 = reinterpret_cast<float2*>(cs + rows * half);   // [rows][half] fp32 (bf16 rows)
+  double2* cs = reinterpret_cast<double2*>(smem);          // [tb][half] fp64
+  float2* cs32 = reinterpret_cast<float2*>(cs + tb * half);   // [tb][half] fp32 (bf16 rows)
   const int cpr = half >> 3;                             // 8-pair chunks per head
   const int per_row = a.H * cpr;                         // <= kThreads (launcher)
   const int rstep = kThreads / per_row;
-  const int row0 = blockIdx.x * rows;
-  const int nrows = min(rows, a.BT - row0);
+  const int B = a.BT / a.T;
+  const int n_tb = (a.T + tb - 1) / tb;
+  const int t0 = (blockIdx.x % n_tb) * tb;
+  const int b0 = (blockIdx.x / n_tb) * bg;
+  const int ntb = min(tb, a.T - t0);                     // positions in this block
   const int q = threadIdx.x % per_row, r0 = threadIdx.x / per_row;
   const int h = q / cpr, ch = q - h * cpr;
   const bool active = r0 < rstep;
   const int64_t rowbytes = (int64_t)a.H * a.d * ELT;
   const int64_t col = ((int64_t)h * a.d + 8 * ch) * ELT;
-  const char* src = reinterpret_cast<const char*>(a.src) + (int64_t)row0 * rowbytes + col;
-  char* dst = reinterpret_cast<char*>(a.x) + (int64_t)row0 * rowbytes + col;
+  const char* src = reinterpret_cast<const char*>(a.src) + col;
+  char* dst = reinterpret_cast<char*>(a.x) + col;
   const int hb = half * ELT;
+  const int rows = tb * bg;
+  auto row_of = [&](int r) -> int64_t {                  // global (b, t) row, or -1
+    const int b = b0 + r / tb, t = r - (r / tb) * tb;
+    return (b < B && t < ntb) ? (int64_t)b * a.T + t0 + t : -1;
+  };
 
   // every row of this thread (at most kRowsPerThread) is loaded up front, so
   // that all of the workgroup's reads are in flight while the table is built
@@ -99,16 +110,16 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
 #pragma unroll
   for (int k = 0; k < kRowsPerThread; ++k) {
     const int r = r0 + k * rstep;
-    if (active && r < nrows) {
-      x1[k].load(src + r * rowbytes);
-      x2[k].load(src + r * rowbytes + hb);
+    const int64_t gr = r < rows ? row_of(r) : -1;
+    if (active && gr >= 0) {
+      x1[k].load(src + gr * rowbytes);
+      x2[k].load(src + gr * rowbytes + hb);
     }
   }
-  for (int e = threadIdx.x; e < nrows * half; e += kThreads) {
-    const int r = e / half, i = e - r * half;
-    const int t = (row0 + r) % a.T;
+  for (int e = threadIdx.x; e < ntb * half; e += kThreads) {
+    const int t = e / half, i = e - t * half;
     double sn, cn;
-    sincos_reduced((double)(a.offset + t) * a.inv_freq[i], &sn, &cn);
+    sincos_reduced((double)(a.offset + t0 + t) * a.inv_freq[i], &sn, &cn);
     const double cc = cn * a.conc, ss = sn * a.conc;
     cs[e] = make_double2(cc, ss);
     if (Rot<ELT>::kF32Table) cs32[e] = make_float2((float)cc, (float)ss);
@@ -119,9 +130,12 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a, int rows) {
 #pragma unroll
   for (int k = 0; k < kRowsPerThread; ++k) {
     const int r = r0 + k * rstep;
-    if (r < nrows)
-      Rot<ELT>::rotate(x1[k], x2[k], &cs32[r * half + 8 * ch], &cs[r * half + 8 * ch], k2,
-                       dst + r * rowbytes, dst + r * rowbytes + hb);
+    const int64_t gr = r < rows ? row_of(r) : -1;
+    if (gr >= 0) {
+      const int t = r % tb;
+      Rot<ELT>::rotate(x1[k], x2[k], &cs32[t * half + 8 * ch], &cs[t * half + 8 * ch], k2,
+                       dst + gr * rowbytes, dst + gr * rowbytes + hb);
+    }
   }
 }
 
@@ -172,13 +186,17 @@ hipError_t launch_rope(const RopeArgs& a, int elt_bytes, hipStream_t s) {
     return hipGetLastError();
   }
   const int rstep = kThreads / (a.H * (half / 8));
-  // rows per workgroup: at most kRowsPerThread per thread (all loaded at once)
+  // rows per workgroup: at most kRowsPerThread per thread (all loaded at once),
+  // as a group of sequences times a block of positions that share one table
   const int rows = rstep * kRowsPerThread < kRows ? rstep * kRowsPerThread : kRows;
-  const int grid = (a.BT + rows - 1) / rows;
-  const size_t lds = (size_t)rows * half * (elt_bytes == 2 ? 24 : 16);
+  const int B = a.BT / a.T;
+  const int bg = B < rows ? B : rows;
+  const int tb = rows / bg;
+  const int grid = ((a.T + tb - 1) / tb) * ((B + bg - 1) / bg);
+  const size_t lds = (size_t)tb * half * (elt_bytes == 2 ? 24 : 16);
   if (elt_bytes == 2)
-    hipLaunchKernelGGL(rope_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a, rows);
+    hipLaunchKernelGGL(rope_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a, tb, bg);
   else
-    hipLaunchKernelGGL(rope_kernel<4>, dim3(grid), dim3(kThreads), lds, s, a, rows);
+    hipLaunchKernelGGL(rope_kernel<4>, dim3(grid), dim3(kThreads), lds, s, a, tb, bg);
   return hipGetLastError();
 }
