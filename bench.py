@@ -8,9 +8,9 @@ d_h=64, bf16, YaRN s=32 base 1.5e5, a cache pre-filled with 65,536 rows.
 For each of its two layer kinds (128-token band, full causal): the cache
 rewound to the prefix, RoPE of the 2048-token chunk's Q and K at positions
 65,536.. with K/V appended in the same pass, sink attention of the chunk at
-offset 65,536, and a snapshot; then 32 decode steps (RoPE + append of one
-token, sink attention against the cache) per layer, a restore, and 32 more
-steps under another seed.  Inputs are resident in HBM before timing starts.
+offset 65,536, and a snapshot; then 32 decode steps per layer (one fused
+call per token: RoPE of its Q and K, append of its K/V row, sink attention
+against the cache), a restore, and 32 more steps under another seed.  Inputs are resident in HBM before timing starts.
 The value is algorithmic attention TFLOP/s of the step (4*d*n_q*B*sum_p|A(p)|
 flops over the allowed query/key pairs of the chunk and of every decode
 query).
@@ -240,10 +240,12 @@ class HandoverLayer:
         self.snap1 = self.cache.snapshot()
 
     def decode(self, w, sa, sweep, s):
+        """The fused step: RoPE of the token's Q and K, append of its K/V row
+        and sink attention in one call (bit-equal to append_rope_qk +
+        sinkattn_decode)."""
         t = self.toks[sweep][s]
-        self.cache.append_rope_qk(t["q"], t["k"], t["v"], self.yarn, q_out=self.qtok)
-        sa.sinkattn_decode(self.qtok, self.cache, self.sinks, self.window, w.sm_scale,
-                           workspace=self.ws, out=self.dout[sweep, s])
+        sa.sinkattn_decode_step(self.cache, t["q"], t["k"], t["v"], self.sinks, self.window,
+                                w.sm_scale, self.yarn, workspace=self.ws, out=self.dout[sweep, s])
 
 
 def handover_step(layers, w, sa, ev=None, sweep_ev=None):
@@ -373,7 +375,7 @@ def handover_figures(w, t):
                              "frac_hbm": round(by_sweep / (sw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                              "gflop": round(fl_sweep / 1e9, 3),
                              "timing": "events around each sweep (restore, then per token and layer "
-                                       "RoPE + append and sink attention), second pass"},
+                                       "fused RoPE + append + sink attention), second pass"},
             "gflop_step": {"prefill": {str(k): round(v / 1e9, 2) for k, v in pre.items()},
                            "decode": {str(k): round(v / 1e9, 3) for k, v in dec.items()}}}
 
@@ -566,12 +568,27 @@ def decode_extra(sa, torch, steps_warm=4):
         torch.cuda.synchronize()
         kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         step_ms = t0.elapsed_time(t1) / w.decode_steps
+        # the same steps through the fused entry point (one call per token)
+        cache.restore(snap)
+        for s in range(steps_warm):
+            sa.sinkattn_decode_step(cache, toks[s]["q"], toks[s]["k"], toks[s]["v"], sinks, W,
+                                    w.sm_scale, y, workspace=ws, out=out)
+        cache.restore(snap)
+        torch.cuda.synchronize()
+        t0.record()
+        for s in range(w.decode_steps):
+            sa.sinkattn_decode_step(cache, toks[s]["q"], toks[s]["k"], toks[s]["v"], sinks, W,
+                                    w.sm_scale, y, workspace=ws, out=out)
+        t1.record()
+        torch.cuda.synchronize()
+        fused_ms = t0.elapsed_time(t1) / w.decode_steps
         rows = [min(w.prefix + s + 1, W) if W > 0 else w.prefix + s + 1
                 for s in range(w.decode_steps)]
         by = np.mean([(r * w.n_kv * w.d_h * 2 * 2 + 2 * w.n_q * w.d_h * 2) * w.B for r in rows])
         gbs = by / (kms * 1e-3) / 1e9
         res["full" if W == 0 else "band%d" % W] = {
             "attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+            "fused_step_us": round(fused_ms * 1e3, 2),
             "alg_mb_per_step": round(by / 1e6, 3), "gbs": round(gbs, 1),
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
             "kv_bytes": w.B * w.capacity * w.n_kv * w.d_h * 2 * 2}

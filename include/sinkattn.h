@@ -469,6 +469,30 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks,
                     float sm_scale, void* workspace, size_t ws_bytes,
                     void* stream);
 
+/* A whole decode step in one attention launch (two with the split merge):
+ * the token at position p = kv_cache_offset(c) (before the call) has its Q
+ * and K rotated at p ("MoE-Xtend" README, ROPE + SCALING), its K/V row
+ * appended at offset p ("MoE-Xtend" README, ARCHITECTURE and KV CACHE:
+ * append at offset = t, then t++), and its query attends to the cache with
+ * that row in it, as sinkattn_decode does.  The results are bit for bit
+ * those of kv_cache_append_rope_qk(c, q, q_rot, n_q, k, v, 1, y) followed by
+ * sinkattn_decode(q_rot, c, ...): the same rotation arithmetic, the same
+ * reduction order.
+ *   q:     device [B, 1, n_q, d_h], unrotated; not modified.
+ *   q_rot: optional device [B, 1, n_q, d_h] that receives the rotated Q;
+ *          NULL: not written.  Must not overlap q or out.
+ *   k, v:  device [B, 1, n_kv, d_h], k unrotated.
+ *   workspace, ws_bytes, window, sm_scale, sinks, out: as sinkattn_decode.
+ * bf16 caches only (SA_ERR_DTYPE otherwise), linear or ring.  Every check
+ * (those of kv_cache_append_rope_qk and of sinkattn_decode) runs before
+ * anything is enqueued; on an error nothing is enqueued and the cache's
+ * offset is unchanged.  On success the offset is p + 1. */
+int sinkattn_decode_step(sa_kv_cache* c, const void* q, void* q_rot,
+                         const void* k, const void* v, const float* sinks,
+                         void* out, int B, int n_q, int n_kv, int d_h,
+                         int window, float sm_scale, const sa_yarn* y,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of the static device array that sinkattn_decode_noalloc keeps its
  * split partials in (one copy per GPU, held until the process ends). */
 #define SA_DECODE_SCRATCH_BYTES (8u << 20)

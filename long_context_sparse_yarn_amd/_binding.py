@@ -104,6 +104,9 @@ _sinkattn_decode = _sig("sinkattn_decode", _i32, _vp, _vp, _vp, _vp, _i32, _i32,
 _sinkattn_decode_noalloc = _sig("sinkattn_decode_noalloc", _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                 _i32, _i32, _i32, _f32, _vp)
 _sinkattn_decode_scratch_bytes = _sig("sinkattn_decode_scratch_bytes", _sz)
+_sinkattn_decode_step = _sig("sinkattn_decode_step", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _f32, ctypes.POINTER(SaYarn), _vp, _sz,
+                             _vp)
 
 
 class SinkAttnError(RuntimeError):
@@ -565,6 +568,38 @@ def sinkattn_decode_noalloc(q: torch.Tensor, cache: KVCache, sinks: torch.Tensor
     _check(_sinkattn_decode_noalloc(_dev(q, "q"), cache.handle, _dev(sinks, "sinks"),
                                     _dev(out, "out"), B, n_q, cache.n_kv, d, int(window),
                                     float(sm_scale), _stream(stream)))
+    return out
+
+
+def sinkattn_decode_step(cache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         sinks: torch.Tensor, window: int, sm_scale: float, y: "Yarn",
+                         q_rot: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One fused decode step: q [B, 1, n_q, d] and k, v [B, 1, n_kv, d] of the
+    token at position cache.offset, unrotated; rotates them, appends the K/V
+    row and attends (bf16).  q_rot, if given, receives the rotated q."""
+    B, T1, n_q, d = q.shape
+    if T1 != 1 or k.shape != (B, 1, cache.n_kv, d) or v.shape != k.shape:
+        raise ValueError("q must be [B, 1, n_q, d] and k, v [B, 1, n_kv, d]")
+    if sinks.dtype != torch.float32 or sinks.numel() != n_q:
+        raise ValueError("sinks must be float32 [n_q]")
+    if q.dtype != cache.dtype or k.dtype != cache.dtype or v.dtype != cache.dtype:
+        raise TypeError("dtype differs from the cache's")
+    if workspace is None:
+        workspace = decode_workspace(cache, n_q)
+    out = _out_like(q, out)
+    qr = 0
+    if q_rot is not None:
+        if q_rot.shape != q.shape or q_rot.dtype != q.dtype:
+            raise ValueError("q_rot must match q")
+        qr = _dev(q_rot, "q_rot")
+    ys = y.c_struct()
+    _check(_sinkattn_decode_step(cache.handle, _dev(q, "q"), qr, _dev(k, "k"), _dev(v, "v"),
+                                 _dev(sinks, "sinks"), _dev(out, "out"), B, n_q, cache.n_kv, d,
+                                 int(window), float(sm_scale), ctypes.byref(ys),
+                                 _dev(workspace, "workspace"), _nbytes(workspace),
+                                 _stream(stream)))
     return out
 
 

@@ -32,8 +32,18 @@
 //    workgroup per (b, g) whose waves take one or two 32-key blocks each and
 //    fold their partials in LDS in the same fixed way, so a band step costs
 //    one block's memory latency rather than a chain of them.
+//  * A whole step in the same launch (launch_decode_step_bf16): the kernels
+//    take the token's unrotated Q, K and V.  Each wave (the workgroup, in the
+//    short kernel) rotates the group's Q heads in LDS with the RoPE kernels'
+//    arithmetic (sa_rope.h, same bits), and the one wave whose run of blocks
+//    holds the token's cache row also rotates K, writes the K and V row to
+//    the cache and, when it reaches that block, puts the row into its
+//    operands in registers (the block's loads may predate the stores).  The
+//    row's raw loads go out before the first block's, the table and the
+//    rotation run while the block loads are in flight.
 #include "sa_device.h"
 #include "sa_kernels.h"
+#include "sa_rope.h"
 
 namespace {
 
@@ -77,11 +87,15 @@ __device__ __forceinline__ void load_block(BlockOps<D>& o, const uint16_t* kbase
 // reference m_run (base-2 units; -inf while nothing is allowed), its share
 // l_run of the sum of weights (the column's four lanes add up to the sum)
 // and O^T[16 dt + 4 g4 + r][head j] against that reference.  No sink.
-template <int D>
+//
+// Hooks (NoStep, or StepHooks for a fused step): pre() before the first
+// block loads, post(qop) after them (fills qop if the hooks own Q), and
+// subst(kb, ops) on each block's operands before they are used.
+template <int D, class Hooks>
 __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, int64_t b0,
                                               int64_t b1, int64_t lo, int64_t hi,
-                                              const u32x4 (&qop)[D / 32], float& m_run,
-                                              float& l_run, f32x4 (&O)[D / 16]) {
+                                              u32x4 (&qop)[D / 32], float& m_run,
+                                              float& l_run, f32x4 (&O)[D / 16], Hooks& hk) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -100,27 +114,33 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   const uint16_t* vpair = vc + ((int64_t)b * (C / 32) * a.n_kv + g) * (int64_t)(D * 32);
   const int64_t vbstride = (int64_t)a.n_kv * D * 32;                      // per 32-key block
 
-  BlockOps<D> cur[2], nxt[2];
+  // Loads are never skipped: a block past the run repeats the run's last
+  // block (block 0 for an empty run; a cache holds at least one), whose
+  // values go unused.  With every load issued, the compiler knows how many
+  // are in flight and waits for exactly the block it is about to use, not
+  // for the prefetched ones behind it.
   auto load2 = [&](BlockOps<D>(&ops)[2], int64_t kb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (kb + u < b1)
-        load_block<D>(ops[u], kpair + (kb + u) * 32 * kstride, vpair + (kb + u) * vbstride,
-                      kstride, j, g4);
+    for (int u = 0; u < 2; ++u) {
+      const int64_t kbu = max((int64_t)0, min(kb + u, b1 - 1));
+      load_block<D>(ops[u], kpair + kbu * 32 * kstride, vpair + kbu * vbstride, kstride, j, g4);
+    }
   };
-  if (b0 < b1) load2(cur, b0);
-  for (int64_t kb = b0; kb < b1; kb += 2) {
-    if (kb + 2 < b1) load2(nxt, kb + 2);
-    const bool two = kb + 1 < b1;
+  // blocks kb, kb + 1 from the operands in cur.  A block at or past b1 (the
+  // repeat load2 made) goes through the same instructions with every key
+  // masked and V zeroed, so that every loaded register is consumed on every
+  // path and the compiler never has to drain the loads in flight.
+  auto process = [&](BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
     f32x4 Sc[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       Sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       Sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u == 1 && !two) break;
+      hk.subst(kb + u, cur[u]);
       const int64_t k0 = (kb + u) * 32;
-      if (k0 + 32 > hi) {    // zero V of keys past the query (unwritten rows)
-        const int valid = (int)(hi - (k0 + 8 * g4));
+      const int64_t top = kb + u < b1 ? hi : k0;     // keys from top on are masked
+      if (k0 + 32 > top) {   // zero V of masked keys (unwritten rows; the repeat)
+        const int valid = (int)max((int64_t)-1, top - (k0 + 8 * g4));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -134,19 +154,15 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) Sc[u][mt] = mfma16x16x32(cur[u].k[mt][ks], qop[ks], Sc[u][mt]);
       // lane (j, g4), element (mt, r): key k0 + 8*g4 + 4*mt + r
-      if (k0 < lo || k0 + 32 > hi) {
+      if (k0 < lo || k0 + 32 > top) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t key = k0 + 8 * g4 + 4 * mt + r;
-            if (key < lo || key >= hi) Sc[u][mt][r] = -INFINITY;
+            if (key < lo || key >= top) Sc[u][mt][r] = -INFINITY;
           }
       }
-    }
-    if (!two) {
-      Sc[1][0] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      Sc[1][1] = Sc[1][0];
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -166,7 +182,6 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if (u == 1 && !two) break;
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -180,10 +195,20 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt] = mfma16x16x32(cur[u].v[dt], Pk, O[dt]);
     }
-    if (kb + 2 < b1) {
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
-    }
+  };
+  // Two operand sets in turn (no register copies, which would wait for the
+  // loads in flight): the loads of one pair of blocks run while the other
+  // pair is computed.
+  BlockOps<D> A[2], Bo[2];
+  hk.pre();
+  load2(A, b0);
+  hk.post(qop);
+  for (int64_t kb = b0; kb < b1; kb += 4) {
+    load2(Bo, kb + 2);
+    process(A, kb);
+    if (kb + 2 >= b1) break;
+    load2(A, kb + 4);
+    process(Bo, kb + 2);
   }
 }
 
@@ -199,15 +224,194 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, u32x4 (&
   for (int ks = 0; ks < D / 32; ++ks) qop[ks] = qv ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
 }
 
-// Split-KV partials: one wave per (b, g, split) over its run of the allowed
-// blocks, written to the workspace for the merge.
+// Plain decode: the cache already holds the token's row, q its rotated Q.
+struct NoStep {
+  __device__ __forceinline__ void pre() {}
+  template <class Q>
+  __device__ __forceinline__ void post(Q&) {}
+  template <class Ops>
+  __device__ __forceinline__ void subst(int64_t, Ops&) {}
+};
+
+// LDS of one fused step for group (b, g): the (c cos, c sin) table of the
+// token's position (fp64 and fp32, as the RoPE kernels keep it), the rotated
+// rows (the group's q_mult Q heads, then the K row) and the raw V row.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
+struct StepStage {
+  static constexpr int H = D / 2;
+  __host__ __device__ static constexpr size_t bytes(int q_mult) {
+    return (size_t)H * 24 + (size_t)(q_mult + 1) * D * 2 + (size_t)D * 2;
+  }
+  double2* tab;
+  float2* tab32;
+  uint16_t* rows;
+  uint16_t* vrow;
+  __device__ __forceinline__ StepStage(char* p, int q_mult)
+      : tab(reinterpret_cast<double2*>(p)),
+        tab32(reinterpret_cast<float2*>(p + H * 16)),
+        rows(reinterpret_cast<uint16_t*>(p + H * 24)),
+        vrow(reinterpret_cast<uint16_t*>(p + H * 24 + (q_mult + 1) * D * 2)) {}
+};
+
+// Ordering of a stage's LDS between the threads that share it: one wave
+// (its LDS operations run in order; the clobber keeps the compiler's order)
+// or a whole workgroup.
+struct WaveSync {
+  __device__ __forceinline__ void operator()() const {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+};
+struct GroupSync {
+  __device__ __forceinline__ void operator()() const { __syncthreads(); }
+};
+
+// A fused step's hooks for group (b, g), run by NTHR threads (tid = 0 ..
+// NTHR-1) that share one stage.
+//   pre:   raw loads -- one (row, 8-pair chunk) item per thread and pass:
+//          both halves of the chunk; the V row (16 bytes per thread).
+//   post:  the table (thread i: pair i, sincos in fp64 as the RoPE kernels),
+//          the rotation of every item (sa_rope::rot8_bf16: the RoPE
+//          kernels' bits) into the stage; the owner also stores the K row,
+//          the V row (blocked layout) and the rotated Q; then every wave
+//          reads its Q^T operand from the stage.
+//   subst: on the block that holds the token's row, the K operand lanes of
+//          that key and the V^T operand lanes of that key take the new row.
+template <int D, int NTHR, class Sync>
+struct StepHooks {
+  static constexpr int H = D / 2;
+  static constexpr int CPR = H / 8;                        // 8-pair chunks per row
+  static constexpr int MAXI = (17 * CPR + NTHR - 1) / NTHR;  // items per thread (q_mult <= 16)
+  const AttnArgs& a;
+  const StepArgs& st;
+  StepStage<D> sg;
+  int b, g, tid;
+  bool owner;         // holds the token's block: rotates K, writes the row
+  int n_items;
+  int64_t kb_new;
+  // the group's rows: Q heads g*q_mult .. (b, g*q_mult + r), the K and V row of (b, g)
+  const uint16_t* qsrc;
+  const uint16_t* ksrc;
+  const uint16_t* vsrc;
+  u32x4 ru[MAXI], rv[MAXI], rvrow;
+  double invf;        // inv_freq of pair tid (tid < H)
+
+  __device__ __forceinline__ StepHooks(const AttnArgs& a_, const StepArgs& st_, char* lds, int b_,
+                                       int g_, int tid_, bool owner_)
+      : a(a_), st(st_), sg(lds, a_.q_mult), b(b_), g(g_), tid(tid_), owner(owner_) {
+    n_items = (a.q_mult + (owner ? 1 : 0)) * CPR;
+    kb_new = st.row / 32;
+    qsrc = reinterpret_cast<const uint16_t*>(st.q_raw) + ((int64_t)b * a.n_q + g * a.q_mult) * D;
+    ksrc = reinterpret_cast<const uint16_t*>(st.k_raw) + ((int64_t)b * a.n_kv + g) * D;
+    vsrc = reinterpret_cast<const uint16_t*>(st.v_raw) + ((int64_t)b * a.n_kv + g) * D;
+  }
+  __device__ __forceinline__ void pre() {
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int it = tid + i * NTHR;
+      if (it < n_items) {
+        const int r = it / CPR, c = (it - r * CPR) * 8;
+        const uint16_t* src = r < a.q_mult ? qsrc + r * D : ksrc;
+        ru[i] = ld16(src + c);
+        rv[i] = ld16(src + c + H);
+      }
+    }
+    if (owner && tid < D / 8) rvrow = ld16(vsrc + 8 * tid);
+    static_assert(H <= NTHR, "one pair of the table per thread");
+    if (tid < H) invf = st.inv_freq[tid];
+  }
+  template <class Q>
+  __device__ __forceinline__ void post(Q& qop) {
+    const Sync sync;
+    if (tid < H) {
+      double sn, cn;
+      sa_rope::sincos_reduced((double)st.pos * invf, &sn, &cn);
+      const double cc = cn * st.conc, ss = sn * st.conc;
+      sg.tab[tid] = make_double2(cc, ss);
+      sg.tab32[tid] = make_float2((float)cc, (float)ss);
+    }
+    if (owner && tid < D / 8) st16(sg.vrow + 8 * tid, rvrow);
+    sync();
+    const float k2 = sa_rope::bf16_rot_k2(st.conc);
+    uint16_t* krow = reinterpret_cast<uint16_t*>(const_cast<void*>(a.kc)) +
+                     (((int64_t)b * a.C + st.row) * a.n_kv + g) * D;
+    uint16_t* qrot = reinterpret_cast<uint16_t*>(st.q_rot) +
+                     ((int64_t)b * a.n_q + g * a.q_mult) * D;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int it = tid + i * NTHR;
+      if (it < n_items) {
+        const int r = it / CPR, c = (it - r * CPR) * 8;
+        u32x4 wa, wb;
+        sa_rope::rot8_bf16(ru[i], rv[i], &sg.tab32[c], &sg.tab[c], k2, &wa, &wb);
+        st16(sg.rows + r * D + c, wa);
+        st16(sg.rows + r * D + c + H, wb);
+        if (owner) {
+          if (r == a.q_mult) {
+            st16(krow + c, wa);
+            st16(krow + c + H, wb);
+          } else if (st.q_rot) {
+            st16(qrot + r * D + c, wa);
+            st16(qrot + r * D + c + H, wb);
+          }
+        }
+      }
+    }
+    if (owner) {
+      uint16_t* vblk = reinterpret_cast<uint16_t*>(const_cast<void*>(a.vc)) +
+                       (((int64_t)b * (a.C / 32) + kb_new) * a.n_kv + g) * (int64_t)(D * 32) +
+                       (st.row & 31);
+      for (int i = tid; i < D; i += NTHR) vblk[i * 32] = sg.vrow[i];
+    }
+    sync();
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qop[ks] = j < a.q_mult ? *reinterpret_cast<const u32x4*>(sg.rows + j * D + 32 * ks + 8 * g4)
+                             : u32x4{0, 0, 0, 0};
+  }
+  template <class Ops>
+  __device__ __forceinline__ void subst(int64_t kb, Ops& ops) {
+    if (kb != kb_new) return;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g4 = lane >> 4;
+    const int kk = (int)(st.row & 31);
+    // K operand: row i = j of M tile mt holds key 8*(j>>2) + 4*mt + (j&3)
+    if (j == 4 * (kk >> 3) + (kk & 3)) {
+      const int mtn = (kk >> 2) & 1;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(sg.rows + a.q_mult * D + 32 * ks + 8 * g4);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          if (mt == mtn) ops.k[mt][ks] = kv;
+      }
+    }
+    // V^T operand: lane (j, g4) holds keys 8*g4 .. 8*g4+7 of coordinate 16*dt + j
+    if (g4 == (kk >> 3)) {
+      const int wn = (kk & 7) >> 1;
+      const bool hi16 = kk & 1;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint32_t nv = sg.vrow[16 * dt + j];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (w == wn)
+            ops.v[dt][w] = hi16 ? ((ops.v[dt][w] & 0xFFFFu) | (nv << 16))
+                                : ((ops.v[dt][w] & 0xFFFF0000u) | nv);
+      }
+    }
+  }
+};
+
+template <int D, bool STEP>
+__device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const StepArgs* st) {
   constexpr int DT = D / 16;
   const AttnArgs& a = da.at;
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g4 = lane >> 4;
-  const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // the wave index is uniform: scalar, so that the block loop runs on scalars
+  const int wid = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = da.n_splits;
   const int pairs = a.B * a.n_kv;
   if (wid >= pairs * S) return;
@@ -226,10 +430,19 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   const int64_t b1 = kb_lo + ((split + 1) * nblk) / S;
 
   u32x4 qop[D / 32];
-  load_q<D>(a, b, g, qop);
   float m_run, l_run;
   f32x4 O[DT];
-  decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O);
+  if constexpr (STEP) {
+    extern __shared__ __attribute__((aligned(16))) char step_lds[];
+    const int64_t kb_new = st->row / 32;
+    StepHooks<D, 64, WaveSync> hk(a, *st, step_lds + (wid % kWaves) * StepStage<D>::bytes(a.q_mult),
+                                  b, g, lane, b0 <= kb_new && kb_new < b1);
+    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+  } else {
+    load_q<D>(a, b, g, qop);
+    NoStep hk;
+    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+  }
   l_run = sum_over_col(l_run);
   if (j < a.q_mult) {
     const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + j;
@@ -245,6 +458,18 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
   }
 }
 
+// Split-KV partials: one wave per (b, g, split) over its run of the allowed
+// blocks, written to the workspace for the merge.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
+  decode_split_body<D, false>(da, nullptr);
+}
+// The same with the step's rotation and append (per-wave stages in dynamic LDS).
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_step_bf16_kernel(DecodeArgs da, StepArgs st) {
+  decode_split_body<D, true>(da, &st);
+}
+
 // A span of at most kShortRows rows (a band layer, or the first steps of a
 // sequence) in one launch with no workspace: a workgroup per (b, g) whose
 // waves take one or two 32-key blocks each; the partials meet in LDS and are
@@ -255,15 +480,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
 template <int D>
 constexpr int short_waves() { return D == 64 ? 8 : 4; }
 
-template <int D>
-__global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_bf16_kernel(AttnArgs a) {
+template <int D, bool STEP>
+__device__ __forceinline__ void decode_short_body(const AttnArgs& a, const StepArgs* st) {
   constexpr int DT = D / 16;
   constexpr int kShortWaves = short_waves<D>();
   constexpr int kShortThreads = kShortWaves * 64;
   __shared__ __attribute__((aligned(16))) float acc_s[kShortWaves][16][D];
   __shared__ float m_s[kShortWaves][16], l_s[kShortWaves][16];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g4 = lane >> 4;
   const int pair = blockIdx.x;
   const int b = pair / a.n_kv, g = pair - (pair / a.n_kv) * a.n_kv;
@@ -276,10 +501,17 @@ __global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_bf16_kerne
   const int64_t b1 = kb_lo + ((wave + 1) * nblk) / kShortWaves;
 
   u32x4 qop[D / 32];
-  load_q<D>(a, b, g, qop);
   float m_run, l_run;
   f32x4 O[DT];
-  decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O);
+  if constexpr (STEP) {   // one stage for the workgroup; every thread takes part
+    extern __shared__ __attribute__((aligned(16))) char step_lds[];
+    StepHooks<D, kShortThreads, GroupSync> hk(a, *st, step_lds, b, g, threadIdx.x, true);
+    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+  } else {
+    load_q<D>(a, b, g, qop);
+    NoStep hk;
+    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+  }
   l_run = sum_over_col(l_run);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -311,6 +543,17 @@ __global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_bf16_kerne
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.n_q + h) * D + 4 * c;
     *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_bf16_kernel(AttnArgs a) {
+  decode_short_body<D, false>(a, nullptr);
+}
+// The same with the step's rotation and append (one stage in dynamic LDS).
+template <int D>
+__global__ __launch_bounds__(short_waves<D>() * 64) void decode_short_step_bf16_kernel(AttnArgs a,
+                                                                                      StepArgs st) {
+  decode_short_body<D, true>(a, &st);
 }
 
 // One workgroup per (b, h).  Every global load is issued first: thread s < S
@@ -407,6 +650,24 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_step_d(const DecodeArgs& a, const StepArgs& st, hipStream_t s) {
+  const size_t stage = StepStage<D>::bytes(a.at.q_mult);
+  if (a.n_splits == 1) {
+    hipLaunchKernelGGL(decode_short_step_bf16_kernel<D>, dim3(a.at.B * a.at.n_kv),
+                       dim3(short_waves<D>() * 64), stage, s, a.at, st);
+    return hipGetLastError();
+  }
+  const int waves = a.at.B * a.at.n_kv * a.n_splits;
+  const int grid = (waves + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(decode_step_bf16_kernel<D>, dim3(grid), dim3(kThreads), kWaves * stage, s, a,
+                     st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int decode_splits(int B, int n_kv, int64_t span_rows) {
@@ -427,6 +688,15 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
     case 64: return launch_d<64>(a, s);
     case 96: return launch_d<96>(a, s);
     case 128: return launch_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_step_bf16(const DecodeArgs& a, const StepArgs& st, hipStream_t s) {
+  switch (a.at.d) {
+    case 64: return launch_step_d<64>(a, st, s);
+    case 96: return launch_step_d<96>(a, st, s);
+    case 128: return launch_step_d<128>(a, st, s);
     default: return hipErrorInvalidValue;
   }
 }

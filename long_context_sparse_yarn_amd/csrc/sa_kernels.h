@@ -115,3 +115,18 @@ struct DecodeArgs {
 int decode_splits(int B, int n_kv, int64_t span_rows);
 int decode_max_splits(int B, int n_kv, int64_t capacity);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+// A whole decode step in the attention launch: the token's Q and K rotated
+// at its position, its K/V row written to the cache, and attention over the
+// cache with that row in it.  DecodeArgs.at.q is unused (q_raw holds Q).
+struct StepArgs {
+  const void* q_raw;    // [B, n_q, d] unrotated
+  void* q_rot;          // optional [B, n_q, d]: receives the rotated Q (null: not written)
+  const void* k_raw;    // [B, n_kv, d] unrotated
+  const void* v_raw;    // [B, n_kv, d]
+  int64_t row;          // cache row that receives the token (same numbering as at.q_offset)
+  int64_t pos;          // the token's global position (its rotation angle)
+  double conc;
+  double inv_freq[SA_MAX_HALF];
+};
+hipError_t launch_decode_step_bf16(const DecodeArgs& a, const StepArgs& st, hipStream_t s);

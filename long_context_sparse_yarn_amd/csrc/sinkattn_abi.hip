@@ -955,13 +955,18 @@ namespace {
 // workspace (ws_static false) it must hold the bound for the cache's whole
 // capacity; with ws_static the partials go to this library's static device
 // array (below), which must hold what this call's split count needs.
+// step != nullptr: a fused step -- q holds the unrotated Q, and the token's
+// row (not yet in the cache: c->offset is the token's position) is written
+// by the kernels; the caller fills step's rotation fields and does the
+// bookkeeping after a successful launch.
 int decode_impl(const void* q, const sa_kv_cache* c, const float* sinks, void* out, int B,
                 int n_q, int n_kv, int d_h, int window, float sm_scale, void* workspace,
-                size_t ws_bytes, bool ws_static, void* stream) {
+                size_t ws_bytes, bool ws_static, StepArgs* step, void* stream) {
   int st = check_attn(q, c, sinks, out, B, 1, n_q, n_kv, d_h);
   if (st != SA_OK) return st;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SA_ERR_ARG, "sm_scale must be finite and > 0");
-  if (c->offset < 1) return fail(SA_ERR_CAPACITY, "decode needs the step's row appended first");
+  const int64_t offset = c->offset + (step ? 1 : 0);     // rows once the token's is in
+  if (offset < 1) return fail(SA_ERR_CAPACITY, "decode needs the step's row appended first");
   // rows handed to the kernel: a ring holds exactly the band (every live
   // slot is allowed, so it is attended as min(offset, W) unmasked rows); a
   // linear cache holds position p at row p - base
@@ -970,15 +975,20 @@ int decode_impl(const void* q, const sa_kv_cache* c, const float* sinks, void* o
     if (window != c->capacity)
       return fail(SA_ERR_ARG, "a ring of %lld rows serves a band of exactly that width (window %d)",
                   (long long)c->capacity, window);
-    q_row = std::min(c->offset, c->capacity) - 1;
+    q_row = std::min(offset, c->capacity) - 1;
     win = 0;
   } else {
-    const int64_t lowest = window > 0 ? std::max<int64_t>(0, c->offset - window) : 0;
+    const int64_t lowest = window > 0 ? std::max<int64_t>(0, offset - window) : 0;
     if (lowest < c->base)
       return fail(SA_ERR_CAPACITY, "keys from position %lld are needed but the cache starts at %lld",
                   (long long)lowest, (long long)c->base);
-    q_row = c->offset - 1 - c->base;
+    q_row = offset - 1 - c->base;
     win = window > 0 ? window : 0;
+  }
+  if (step) {
+    if (c->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "the fused decode step needs a bf16 cache");
+    step->row = c->ring ? c->offset % c->capacity : c->offset - c->base;
+    step->pos = c->offset;
   }
   const int q_mult = n_q / n_kv;
   AttnArgs a;
@@ -1018,7 +1028,8 @@ int decode_impl(const void* q, const sa_kv_cache* c, const float* sinks, void* o
         return fail(SA_ERR_ARG, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     }
     da.ws = reinterpret_cast<float*>(workspace);
-    e = launch_decode_bf16(da, (hipStream_t)stream);
+    e = step ? launch_decode_step_bf16(da, *step, (hipStream_t)stream)
+             : launch_decode_bf16(da, (hipStream_t)stream);
   } else {
     e = launch_attn_rows_f32(a, (hipStream_t)stream);
   }
@@ -1033,14 +1044,47 @@ int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks, voi
                     int n_q, int n_kv, int d_h, int window, float sm_scale, void* workspace,
                     size_t ws_bytes, void* stream) {
   return decode_impl(q, c, sinks, out, B, n_q, n_kv, d_h, window, sm_scale, workspace, ws_bytes,
-                     false, stream);
+                     false, nullptr, stream);
+}
+
+int sinkattn_decode_step(sa_kv_cache* c, const void* q, void* q_rot, const void* k, const void* v,
+                         const float* sinks, void* out, int B, int n_q, int n_kv, int d_h,
+                         int window, float sm_scale, const sa_yarn* y, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  // every check before anything is enqueued or recorded
+  AppendPlan pl;
+  int st = append_plan(c, k, v, 1, &pl);
+  if (st != SA_OK) return st;
+  if (!q || !out) return fail(SA_ERR_ARG, "null argument");
+  const int64_t qbytes = (int64_t)B * n_q * d_h * 2;
+  if (q_rot) {
+    if (misaligned(q_rot)) return fail(SA_ERR_ARG, "q_rot must be 16-byte aligned");
+    const char* r = static_cast<const char*>(q_rot);
+    const char* a = static_cast<const char*>(q);
+    const char* o = static_cast<const char*>(out);
+    if (qbytes > 0 && ((r < a + qbytes && a < r + qbytes) || (r < o + qbytes && o < r + qbytes)))
+      return fail(SA_ERR_ARG, "q_rot overlaps q or out");
+  }
+  StepArgs sp;
+  memset(&sp, 0, sizeof sp);
+  st = yarn_table(y, d_h, sp.inv_freq, &sp.conc);
+  if (st != SA_OK) return st;
+  sp.q_raw = q;
+  sp.q_rot = q_rot;
+  sp.k_raw = k;
+  sp.v_raw = v;
+  st = decode_impl(q, c, sinks, out, B, n_q, n_kv, d_h, window, sm_scale, workspace, ws_bytes,
+                   false, &sp, stream);
+  if (st != SA_OK) return st;
+  appended(c, 1);
+  return ok();
 }
 
 int sinkattn_decode_noalloc(const void* q, const sa_kv_cache* c, const float* sinks, void* out,
                             int B, int n_q, int n_kv, int d_h, int window, float sm_scale,
                             void* stream) {
   return decode_impl(q, c, sinks, out, B, n_q, n_kv, d_h, window, sm_scale, nullptr, 0, true,
-                     stream);
+                     nullptr, stream);
 }
 
 size_t sinkattn_decode_scratch_bytes(void) { return (size_t)SA_DECODE_SCRATCH_BYTES; }

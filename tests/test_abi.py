@@ -262,6 +262,47 @@ def test_noalloc_decode_refuses_what_its_scratch_cannot_hold():
     B._kv_cache_destroy(h)
 
 
+def test_decode_step_checks_before_enqueueing():
+    """sinkattn_decode_step runs the append's and the decode's checks before
+    it enqueues anything, and leaves the offset alone on every error."""
+    ys = B.Yarn(64).c_struct()
+    yp = ctypes.byref(ys)
+    q, qr, o, s = (ctypes.c_void_p(a) for a in (0x30000, 0x60000, 0x40000, 0x50000))
+    k, v, ws = ctypes.c_void_p(0x70000), ctypes.c_void_p(0x80000), ctypes.c_void_p(0x90000)
+    step = B._sinkattn_decode_step
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=255)
+    assert st == SA_OK
+    args = lambda **kw: [kw.get("c", h), kw.get("q", q), kw.get("qr", qr), kw.get("k", k),
+                         kw.get("v", v), s, kw.get("o", o), 2, kw.get("n_q", 8), 2, 64,
+                         kw.get("W", 0), 0.125, kw.get("y", yp), ws, 1 << 20, None]
+    assert step(*args(k=None)) == SA_ERR_ARG
+    assert step(*args(q=None)) == SA_ERR_ARG
+    assert step(*args(y=None)) == SA_ERR_ARG
+    assert step(*args(qr=ctypes.c_void_p(0x30000 + 64))) == SA_ERR_ARG      # q_rot overlaps q
+    assert "overlaps" in sa.last_error()
+    assert step(*args(qr=ctypes.c_void_p(0x40000))) == SA_ERR_ARG           # q_rot is out
+    assert step(*args(qr=ctypes.c_void_p(0x60008))) == SA_ERR_ARG           # misaligned
+    assert step(*args(n_q=7)) == SA_ERR_SHAPE                               # 7 heads over 2 KV heads
+    assert step(*args(n_q=40)) == SA_ERR_SHAPE                              # q_mult 20 > 16
+    assert B._kv_cache_offset(h) == 255
+    B._kv_cache_destroy(h)
+    # a full cache: the append's capacity check
+    st, h = create(Bn=2, C=256, n_kv=2, d=64, offset=256)
+    assert step(*args(c=h)) == SA_ERR_CAPACITY
+    assert B._kv_cache_offset(h) == 256
+    B._kv_cache_destroy(h)
+    # fp32 caches attend through the separate calls
+    st, h = create(dtype=1, Bn=2, C=256, n_kv=2, d=64, offset=3)
+    assert step(*args(c=h)) == SA_ERR_DTYPE
+    assert B._kv_cache_offset(h) == 3
+    B._kv_cache_destroy(h)
+    # a ring takes window == W only
+    st, r = ring()
+    assert step(*args(c=r, W=64)) == SA_ERR_ARG
+    assert B._kv_cache_offset(r) == 0
+    B._kv_cache_destroy(r)
+
+
 def ring(dtype=0, Bn=2, W=128, n_kv=2, d=64):
     h = ctypes.c_void_p()
     st = B._kv_ring_create(ctypes.byref(h), FAKE_K, FAKE_V, dtype, Bn, W, n_kv, d)
