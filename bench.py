@@ -927,6 +927,11 @@ def cpu_decode_sample(w, budget_s):
                       "algorithmic bytes" % (w.name, n, p + 1, t_attn / n, t_fixed, w.decode_steps)}
 
 
+def progress(what):
+    """One line on stderr per finished phase (stdout holds only the JSON line)."""
+    print("[bench] %s" % what, file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -959,6 +964,7 @@ def main():
     fl_step = sum(pre.values()) + sum(dec.values())
     value = fl_step / (t["ms_step"] * 1e-3) / 1e12
     ho = handover_figures(w, t)
+    progress("handover timed: %.4f ms per step" % t["ms_step"])
     full = [f for f in ho["layers"] if f["window"] == 0][0]
     traffic = TRAFFIC.get(("handover", 0))
     roofline = {"bound": "mfma", "achieved": full["tflops"], "peak": PEAK_BF16_TFLOPS,
@@ -994,6 +1000,7 @@ def main():
     # ---- long-context decode: the second headline figure (KV GB/s)
     ld = decode_extra(sa, torch)
     fd = ld["full"]
+    progress("long decode timed")
     line["decode_kv"] = {"workload": ld["workload"], "layer": "full causal",
                          "gbs": fd["gbs"], "frac_hbm": fd["frac_hbm"],
                          "attn_kernel_us": fd["attn_kernel_us"], "step_us": fd["step_us"],
@@ -1015,6 +1022,7 @@ def main():
             "tflops_step": round(fl / (ms_step * 1e-3) / 1e12, 1), "layers": per_layer,
             "abi_calls": abi_call_figures(lw, layers[full_i], sa, torch),
             "ring": ring_prefill_figures(lw, [L for L in layers if L.window > 0][0], sa, torch)}}
+        progress("gpt-oss-lite prefill timed")
         if not args.no_cpu:
             cpu["gpt-oss-lite prefill"] = cpu_prefill_sample(lw, layers, args.cpu_seconds)
         del layers
@@ -1026,14 +1034,18 @@ def main():
                                             "tflops_step": round(fl / (gms * 1e-3) / 1e12, 1),
                                             "layers": [prefill_figures(g, L, gk[i], gin[i])
                                                        for i, L in enumerate(gl)]}
+        progress("gpt-oss prefill timed")
         if not args.no_cpu:
             cpu["gpt-oss prefill"] = cpu_prefill_sample(g, gl, args.cpu_seconds)
         del gl
         torch.cuda.empty_cache()
         line["extra"]["long_decode"] = ld
         line["extra"]["qkv_projection"] = qkv_extra(sa, torch)
+        progress("projection timed")
         line["extra"]["moe_layer"] = moe_extra(sa, torch)
+        progress("MoE layer timed")
         line["extra"]["sampling"] = sample_extra(sa, torch)
+        progress("sampling timed")
     if not args.no_cpu:
         head = cpu_prefill_sample(w, t["layers"], 2 * args.cpu_seconds, extra_flops=dec)
         cores, model = _cpu_info()
