@@ -9,7 +9,7 @@
 // Angles and the pair rotation: sa_rope.h.
 //
 // A workgroup takes a block of positions t and a group of sequences b (up
-// to 32 rows (b, t), about four per thread) and all their heads.  Its
+// to 32 rows (b, t), one per thread and head column) and all their heads.  Its
 // threads build the (c*cos, c*sin) table of the block's positions in LDS
 // once -- shared by every head and every sequence of the group -- while
 // their first loads are in flight; each thread then owns one (head, 8-pair
@@ -31,7 +31,10 @@ using sa_rope::sincos_reduced;
 
 constexpr int kThreads = 256;
 constexpr int kRows = 32;            // most rows per workgroup
-constexpr int kRowsPerThread = 4;    // aim: each thread walks about this many rows
+// rows a thread rotates: one (more workgroups, each table still shared by
+// the group's sequences) measured 10% faster than four (GPT-OSS-Lite Q:
+// 13.2 against 14.6 us; gpt-oss Q 24.1 against 26.8) and 2-4% faster than two
+constexpr int kRowsPerThread = 1;
 
 template <int ELT>
 struct Rot;
