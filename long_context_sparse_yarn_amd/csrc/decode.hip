@@ -49,10 +49,13 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-#ifndef SA_DEC_WAVES
-#define SA_DEC_WAVES 2048
-#endif
-constexpr int kTargetWaves = SA_DEC_WAVES;
+// Split-KV waves to aim for: 2048 (8 per CU) keep HBM busy; with at most 8
+// (b, g) pairs, 1024 do as well and halve the merge's partials (B = 1,
+// 67.6k rows, 64/8 heads: split + merge 27.7 against 29.1 us; at B = 8 the
+// 2048 target is 0.7% faster; 512 and fewer lose the memory parallelism).
+constexpr int kTargetWaves = 2048;
+constexpr int kTargetWavesFewPairs = 1024;
+constexpr int kFewPairs = 8;
 constexpr int kMaxSplits = 256;
 constexpr int64_t kSingleSplitRows = 256;   // spans this short run as one short launch
 constexpr float kSlack = 8.0f;
@@ -673,7 +676,9 @@ hipError_t launch_step_d(const DecodeArgs& a, const StepArgs& st, hipStream_t s)
 int decode_splits(int B, int n_kv, int64_t span_rows) {
   if (span_rows <= kSingleSplitRows) return 1;       // short span: one workgroup per (b, g)
   const int64_t nblk = (span_rows + 31) / 32 + 1;   // a span may straddle one more block
-  int64_t s = (kTargetWaves + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
+  const int64_t pairs = (int64_t)B * n_kv;
+  const int64_t target = pairs <= kFewPairs ? kTargetWavesFewPairs : kTargetWaves;
+  int64_t s = (target + pairs - 1) / pairs;
   if (s > nblk) s = nblk;
   if (s > kMaxSplits) s = kMaxSplits;
   return (int)(s < 1 ? 1 : s);
