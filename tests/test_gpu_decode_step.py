@@ -45,8 +45,9 @@ STEP_CASES = [
 ]
 
 
-def _caches(B, prefix, steps, n_kv, d, rng):
-    C = ((prefix + steps + 31) // 32) * 32 + 32
+def _caches(B, prefix, steps, n_kv, d, rng, C=None):
+    if C is None:
+        C = ((prefix + steps + 31) // 32) * 32 + 32
     pk = _draw((B, prefix, n_kv, d), rng)
     pv = _draw((B, prefix, n_kv, d), rng)
     pair = []
@@ -114,16 +115,17 @@ def test_decode_step_without_q_rot_and_unchanged_inputs():
             assert torch.equal(_bits(a), _bits(b))
 
 
-@pytest.mark.parametrize("W,prefix", [(128, 100), (64, 0)])
-def test_decode_step_on_a_ring(W, prefix):
+@pytest.mark.parametrize("W,prefix,d,n_q,n_kv", [(128, 100, 64, 16, 2), (64, 0, 64, 16, 2),
+                                                  (64, 40, 96, 8, 4), (96, 200, 128, 16, 1)])
+def test_decode_step_on_a_ring(W, prefix, d, n_q, n_kv):
     """A ring cache: the token's slot is p mod W, anywhere in the ring once it
     has wrapped; bit-equal to append_rope_qk + decode on a second ring, and
     within tolerance of the oracle's ring."""
-    rng = np.random.default_rng(W + prefix)
-    B, n_q, n_kv, d, steps = 2, 16, 2, 64, 3 * W // 2 + 5
+    rng = np.random.default_rng(W + prefix + d)
+    B, steps = 2, 3 * W // 2 + 5
     y = Yarn()
     ly = lib_yarn(d, y)
-    sm = 0.125
+    sm = 1.0 / np.sqrt(d)
     sinks = rng.standard_normal(n_q).astype(np.float32)
     s_t = torch.from_numpy(sinks).cuda()
     ra = sa.KVRing.empty(B, W, n_kv, d, fill=float("nan"))
@@ -154,3 +156,32 @@ def test_decode_step_on_a_ring(W, prefix):
     assert ra.offset == rb.offset == prefix + steps
     assert torch.equal(_bits(ra.k), _bits(rb.k)) and torch.equal(_bits(ra.v), _bits(rb.v))
     assert err <= TOL["bf16"], err
+
+
+def test_decode_step_fills_the_cache_to_capacity():
+    """Steps up to the last row of the cache (row C - 1, the last slot of its
+    32-row block), then a step past it is refused with nothing written."""
+    rng = np.random.default_rng(11)
+    B, n_q, n_kv, d = 1, 8, 2, 64
+    y = Yarn()
+    ly = lib_yarn(d, y)
+    s_t = torch.from_numpy(rng.standard_normal(n_q).astype(np.float32)).cuda()
+    C = 64
+    (ca, cb), _, _ = _caches(B, C - 3, 3, n_kv, d, rng, C=C)
+    assert ca.capacity == cb.capacity == C
+    for _ in range(3):
+        q, k, v = _draw((B, 1, n_q, d), rng), _draw((B, 1, n_kv, d), rng), _draw((B, 1, n_kv, d), rng)
+        qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+        qr = ca.append_rope_qk(qd, kd, vd, ly)
+        oa = sa.sinkattn_decode(qr, ca, s_t, 0, 0.125)
+        ob = sa.sinkattn_decode_step(cb, qd, kd, vd, s_t, 0, 0.125, ly)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(oa), _bits(ob))
+    assert cb.offset == C
+    k_before, v_before = cb.k.clone(), cb.v.clone()
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_decode_step(cb, qd, kd, vd, s_t, 0, 0.125, ly)
+    torch.cuda.synchronize()
+    assert cb.offset == C
+    assert torch.equal(_bits(cb.k), _bits(k_before)) and torch.equal(_bits(cb.v), _bits(v_before))
+    assert torch.equal(_bits(ca.k), _bits(cb.k)) and torch.equal(_bits(ca.v), _bits(cb.v))
