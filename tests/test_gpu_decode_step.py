@@ -185,3 +185,41 @@ def test_decode_step_fills_the_cache_to_capacity():
     assert cb.offset == C
     assert torch.equal(_bits(cb.k), _bits(k_before)) and torch.equal(_bits(cb.v), _bits(v_before))
     assert torch.equal(_bits(ca.k), _bits(cb.k)) and torch.equal(_bits(ca.v), _bits(cb.v))
+
+
+def _random_case(seed):
+    r = np.random.default_rng(seed)
+    d = int(r.choice([64, 96, 128]))
+    n_kv = int(r.choice([1, 2, 4, 8]))
+    q_mult = int(r.choice([1, 2, 3, 4, 6, 8, 16]))
+    B = int(r.integers(1, 4))
+    W = int(r.choice([0, 0, 17, 128, 300]))
+    prefix = int(r.integers(0, 3000))
+    steps = int(r.integers(1, 5))
+    return B, prefix, steps, q_mult * n_kv, n_kv, d, W
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_step_random_shapes(seed):
+    """Seeded random shapes (head dimension, group size, batch, band width,
+    cache fill): the fused step stays bit-equal to the separate calls."""
+    B, prefix, steps, n_q, n_kv, d, W = _random_case(seed)
+    rng = np.random.default_rng(seed + 100)
+    y = Yarn()
+    ly = lib_yarn(d, y)
+    sm = 1.0 / np.sqrt(d)
+    s_t = torch.from_numpy(rng.standard_normal(n_q).astype(np.float32)).cuda()
+    (ca, cb), _, _ = _caches(B, prefix, steps, n_kv, d, rng)
+    wa, wb = sa.decode_workspace(ca, n_q), sa.decode_workspace(cb, n_q)
+    qra = torch.empty((B, 1, n_q, d), dtype=torch.bfloat16, device="cuda")
+    qrb = torch.empty_like(qra)
+    for s in range(steps):
+        q, k, v = _draw((B, 1, n_q, d), rng), _draw((B, 1, n_kv, d), rng), _draw((B, 1, n_kv, d), rng)
+        qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+        ca.append_rope_qk(qd, kd, vd, ly, q_out=qra)
+        oa = sa.sinkattn_decode(qra, ca, s_t, W, sm, workspace=wa)
+        ob = sa.sinkattn_decode_step(cb, qd, kd, vd, s_t, W, sm, ly, q_rot=qrb, workspace=wb)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(oa), _bits(ob)), (seed, s)
+        assert torch.equal(_bits(qra), _bits(qrb)), (seed, s)
+    assert torch.equal(_bits(ca.k), _bits(cb.k)) and torch.equal(_bits(ca.v), _bits(cb.v))
