@@ -29,9 +29,10 @@
 //      out = sum_c acc_c 2^(m_c-M) / L        (sigma' = sigma * log2 e).
 //    Splits with no allowed key carry m = -inf, l = 0 and drop out.  A span
 //    of at most 256 rows (a band layer) runs in one launch instead: a
-//    workgroup per (b, g) whose waves take one or two 32-key blocks each and
-//    fold their partials in LDS in the same fixed way, so a band step costs
-//    one block's memory latency rather than a chain of them.
+//    workgroup of four waves per (b, g), each wave one or two 32-key blocks
+//    of a 128-row band, folding their partials in LDS in the same fixed way,
+//    so a band step costs a block's memory latency or two rather than a
+//    chain of them.
 //  * A whole step in the same launch (launch_decode_step_bf16): the kernels
 //    take the token's unrotated Q, K and V.  Each wave (the workgroup, in the
 //    short kernel) rotates the group's Q heads in LDS with the RoPE kernels'
@@ -478,10 +479,13 @@ __global__ __launch_bounds__(kThreads) void decode_step_bf16_kernel(DecodeArgs d
 // waves take one or two 32-key blocks each; the partials meet in LDS and are
 // folded in wave order, with the sink added once, by all of the workgroup's
 // threads.
-// Eight waves at d = 64; four at d = 96 and 128, whose per-wave pass needs
-// more registers than two waves per SIMD leave it.
+// Four waves: a 128-row band is four or five 32-key blocks, so each wave
+// takes one or two, and the fold has four partials to add (the fused step
+// at d = 64, B = 1 and 8: 6.8-7.0 us per launch against 8.1-8.4 with eight
+// waves; two waves 6.6-6.8, but they would walk four blocks each on a
+// 256-row span).
 template <int D>
-constexpr int short_waves() { return D == 64 ? 8 : 4; }
+constexpr int short_waves() { return 4; }
 
 template <int D, bool STEP>
 __device__ __forceinline__ void decode_short_body(const AttnArgs& a, const StepArgs* st) {
