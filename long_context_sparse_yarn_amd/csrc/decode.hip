@@ -27,7 +27,10 @@
 //    and adds the sink exactly once:
 //      M = max(sigma', max_c m_c), L = 2^(sigma'-M) + sum_c l_c 2^(m_c-M),
 //      out = sum_c acc_c 2^(m_c-M) / L        (sigma' = sigma * log2 e).
-//    Splits with no allowed key carry m = -inf, l = 0 and drop out.  A span
+//    Splits with no allowed key carry m = -inf, l = 0 and drop out.  With
+//    few (b, g) pairs (at most 8) a workgroup's four waves take four pieces
+//    of one (b, g)'s run instead and fold their partials in LDS into one
+//    (same formula, no sink), so the merge gathers a quarter as many.  A span
 //    of at most 256 rows (a band layer) runs in one launch instead: a
 //    workgroup of four waves per (b, g), each wave one or two 32-key blocks
 //    of a 128-row band, folding their partials in LDS in the same fixed way,
@@ -57,9 +60,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTargetWaves = 2048;
 constexpr int kTargetWavesFewPairs = 1024;
 constexpr int kFewPairs = 8;
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = 256;                 // waves (partials) per (b, g) at most
 constexpr int64_t kSingleSplitRows = 256;   // spans this short run as one short launch
 constexpr float kSlack = 8.0f;
+// With at most kFewPairs (b, g) pairs each split workgroup folds its waves'
+// partials into one (see decode_split_body).
+__host__ __device__ constexpr bool fold_splits(int pairs) { return pairs <= kFewPairs; }
 
 template <int D>
 struct BlockOps {
@@ -408,30 +414,94 @@ struct StepHooks {
   }
 };
 
-template <int D, bool STEP>
+// The partials of a workgroup's waves (one run each of the same (b, g))
+// meet in LDS and are folded in wave order into the workgroup's one partial
+// (no sink: the merge adds it once).
+template <int D>
+__device__ __forceinline__ void fold_partial(const DecodeArgs& da, int pair, int split, int wave,
+                                             float m_run, float l_run, const f32x4 (&O)[D / 16]) {
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float acc_s[kWaves][16][D];
+  __shared__ float m_s[kWaves][16], l_s[kWaves][16];
+  const AttnArgs& a = da.at;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int S = da.n_splits;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4*>(&acc_s[wave][j][16 * dt + 4 * g4]) = O[dt];
+  if (g4 == 0) {
+    m_s[wave][j] = m_run;
+    l_s[wave][j] = l_run;
+  }
+  __syncthreads();
+  constexpr int CPH = D / 4;
+  float* ml = da.ws + (int64_t)a.B * a.n_kv * S * a.q_mult * D;
+  for (int i = threadIdx.x; i < a.q_mult * CPH; i += kThreads) {
+    const int jq = i / CPH, c = i - jq * CPH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_s[w][jq]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = m_s[w][jq];
+      const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      L += l_s[w][jq] * sc;
+      o += *reinterpret_cast<const f32x4*>(&acc_s[w][jq][4 * c]) * sc;
+    }
+    const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + jq;
+    *reinterpret_cast<f32x4*>(da.ws + slot * D + 4 * c) = o;
+    if (c == 0) {
+      ml[2 * slot] = M;
+      ml[2 * slot + 1] = L;
+    }
+  }
+}
+
+// FOLD false: one wave per (b, g, split), KV head fastest, so that the waves
+// running side by side read whole cache rows (all heads of a row are
+// contiguous) and whole 32-key V blocks; each wave writes its partial.
+// FOLD true (few (b, g) pairs): one workgroup per (b, g, split), (b, g)
+// fastest, its run cut into one contiguous piece per wave and the waves'
+// partials folded into one, so the merge reads a quarter of the partials.
+// With many pairs the per-wave layout streams the cache faster (B = 8,
+// 131k rows, 64/8 heads: 357 us against 392), with 8 pairs the fold wins
+// (B = 1, 67.6k rows: split + merge 27.1 against 27.9 us).
+template <int D, bool STEP, bool FOLD>
 __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const StepArgs* st) {
   constexpr int DT = D / 16;
   const AttnArgs& a = da.at;
   const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g4 = lane >> 4;
   // the wave index is uniform: scalar, so that the block loop runs on scalars
-  const int wid = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = da.n_splits;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g4 = lane >> 4;
+  const int S = da.n_splits;               // partials per (b, g)
   const int pairs = a.B * a.n_kv;
-  if (wid >= pairs * S) return;
-  // KV head fastest: waves running side by side read whole cache rows
-  // (all heads of a row are contiguous) and whole 32-key V blocks.
-  const int g = wid % a.n_kv;
-  const int split = (wid / a.n_kv) % S;
-  const int b = wid / (a.n_kv * S);
+  int b, g, split;
+  if constexpr (FOLD) {
+    const int pr = blockIdx.x % pairs;
+    split = blockIdx.x / pairs;
+    b = pr / a.n_kv;
+    g = pr - b * a.n_kv;
+  } else {
+    const int wid = blockIdx.x * kWaves + wave;
+    if (wid >= pairs * S) return;
+    g = wid % a.n_kv;
+    split = (wid / a.n_kv) % S;
+    b = wid / (a.n_kv * S);
+  }
   const int pair = b * a.n_kv + g;
 
   const int64_t P = a.q_offset;                         // query position
   const int64_t lo = a.window > 0 ? max((int64_t)0, P - a.window + 1) : 0;
   const int64_t hi = P + 1;
   const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
-  const int64_t b0 = kb_lo + (split * nblk) / S;
-  const int64_t b1 = kb_lo + ((split + 1) * nblk) / S;
+  const int64_t pc = FOLD ? (int64_t)split * kWaves + wave : split;   // this wave's piece
+  const int64_t np = FOLD ? (int64_t)S * kWaves : S;                  // pieces per (b, g)
+  const int64_t b0 = kb_lo + (pc * nblk) / np;
+  const int64_t b1 = kb_lo + ((pc + 1) * nblk) / np;
 
   u32x4 qop[D / 32];
   float m_run, l_run;
@@ -439,7 +509,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const St
   if constexpr (STEP) {
     extern __shared__ __attribute__((aligned(16))) char step_lds[];
     const int64_t kb_new = st->row / 32;
-    StepHooks<D, 64, WaveSync> hk(a, *st, step_lds + (wid % kWaves) * StepStage<D>::bytes(a.q_mult),
+    StepHooks<D, 64, WaveSync> hk(a, *st, step_lds + wave * StepStage<D>::bytes(a.q_mult),
                                   b, g, lane, b0 <= kb_new && kb_new < b1);
     decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   } else {
@@ -448,7 +518,9 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const St
     decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   }
   l_run = sum_over_col(l_run);
-  if (j < a.q_mult) {
+  if constexpr (FOLD) {
+    fold_partial<D>(da, pair, split, wave, m_run, l_run, O);
+  } else if (j < a.q_mult) {
     const int64_t slot = ((int64_t)pair * S + split) * a.q_mult + j;
     float* acc = da.ws + slot * D;
 #pragma unroll
@@ -462,16 +534,16 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const St
   }
 }
 
-// Split-KV partials: one wave per (b, g, split) over its run of the allowed
-// blocks, written to the workspace for the merge.
-template <int D>
+// Split-KV partials (per wave, or folded per workgroup), written to the
+// workspace for the merge.
+template <int D, bool FOLD>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs da) {
-  decode_split_body<D, false>(da, nullptr);
+  decode_split_body<D, false, FOLD>(da, nullptr);
 }
 // The same with the step's rotation and append (per-wave stages in dynamic LDS).
-template <int D>
+template <int D, bool FOLD>
 __global__ __launch_bounds__(kThreads) void decode_step_bf16_kernel(DecodeArgs da, StepArgs st) {
-  decode_split_body<D, true>(da, &st);
+  decode_split_body<D, true, FOLD>(da, &st);
 }
 
 // A span of at most kShortRows rows (a band layer, or the first steps of a
@@ -583,12 +655,12 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
-template <int D>
+template <int D, int MAXS>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs da) {
   constexpr int CPS = D / 4;                        // f32x4 vectors per split
   constexpr int G = kMergeThreads / CPS;            // split groups
-  constexpr int KMAX = (kMaxSplits + G - 1) / G;    // splits per group at most
-  __shared__ float wsh[kMaxSplits];
+  constexpr int KMAX = (MAXS + G - 1) / G;          // partials per group at most
+  __shared__ float wsh[MAXS];
   __shared__ float red[kMergeThreads / 64];
   __shared__ f32x4 part[G][CPS];
   const AttnArgs& a = da.at;
@@ -641,6 +713,18 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   }
 }
 
+// The merge, built for 64 partials at most where they fit (fewer loads in
+// the unrolled gather than with the 256 bound: B = 1, 32 partials per
+// (b, g): split + merge 27.1 against 27.7 us; a 32 bound measured 27.5).
+template <int D>
+void launch_merge(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.at.B * a.at.n_q), block(kMergeThreads);
+  if (a.n_splits <= 64)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 64>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, kMaxSplits>), grid, block, 0, s, a);
+}
+
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   if (a.n_splits == 1) {
@@ -648,12 +732,16 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
                        dim3(short_waves<D>() * 64), 0, s, a.at);
     return hipGetLastError();
   }
-  const int waves = a.at.B * a.at.n_kv * a.n_splits;
-  const int grid = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
+  const int pairs = a.at.B * a.at.n_kv;
+  if (fold_splits(pairs))
+    hipLaunchKernelGGL((decode_bf16_kernel<D, true>), dim3(pairs * a.n_splits), dim3(kThreads), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<D, false>), dim3((pairs * a.n_splits + kWaves - 1) / kWaves),
+                       dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
+  launch_merge<D>(a, s);
   return hipGetLastError();
 }
 
@@ -665,13 +753,17 @@ hipError_t launch_step_d(const DecodeArgs& a, const StepArgs& st, hipStream_t s)
                        dim3(short_waves<D>() * 64), stage, s, a.at, st);
     return hipGetLastError();
   }
-  const int waves = a.at.B * a.at.n_kv * a.n_splits;
-  const int grid = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(decode_step_bf16_kernel<D>, dim3(grid), dim3(kThreads), kWaves * stage, s, a,
-                     st);
+  const int pairs = a.at.B * a.at.n_kv;
+  if (fold_splits(pairs))
+    hipLaunchKernelGGL((decode_step_bf16_kernel<D, true>), dim3(pairs * a.n_splits), dim3(kThreads),
+                       kWaves * stage, s, a, st);
+  else
+    hipLaunchKernelGGL((decode_step_bf16_kernel<D, false>),
+                       dim3((pairs * a.n_splits + kWaves - 1) / kWaves), dim3(kThreads),
+                       kWaves * stage, s, a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.at.B * a.at.n_q), dim3(kMergeThreads), 0, s, a);
+  launch_merge<D>(a, s);
   return hipGetLastError();
 }
 
@@ -682,9 +774,10 @@ int decode_splits(int B, int n_kv, int64_t span_rows) {
   const int64_t nblk = (span_rows + 31) / 32 + 1;   // a span may straddle one more block
   const int64_t pairs = (int64_t)B * n_kv;
   const int64_t target = pairs <= kFewPairs ? kTargetWavesFewPairs : kTargetWaves;
-  int64_t s = (target + pairs - 1) / pairs;
-  if (s > nblk) s = nblk;
-  if (s > kMaxSplits) s = kMaxSplits;
+  int64_t w = (target + pairs - 1) / pairs;          // waves per pair
+  if (w > nblk) w = nblk;
+  if (w > kMaxSplits) w = kMaxSplits;
+  const int64_t s = fold_splits((int)pairs) ? w / kWaves : w;   // partials per pair
   return (int)(s < 1 ? 1 : s);
 }
 
