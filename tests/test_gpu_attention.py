@@ -123,6 +123,8 @@ DECODE_CASES = [
     (2, 1000, 3, 64, 8, 64, 0, "bf16", True),          # no sink, split span + merge
     (2, 1000, 3, 64, 8, 64, 128, "bf16", True),        # no sink, single-split span
     (1, 150, 3, 8, 2, 96, 0, "bf16", True),            # no sink, whole cache in one split
+    (1, 320, 12, 8, 2, 64, 0, "bf16", False),          # folded splits: 12 pieces over 11 blocks, one empty
+    (1, 5000, 2, 32, 8, 64, 0, "bf16", True),          # no sink, folded splits
     (1, 120, 4, 8, 2, 64, 0, "f32", False),
     (1, 120, 4, 8, 2, 64, 32, "f32", False),
     (1, 300, 2, 8, 2, 64, 0, "f32", True),

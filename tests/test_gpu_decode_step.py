@@ -38,6 +38,7 @@ STEP_CASES = [
     (2, 200, 40, 64, 8, 64, 0),        # short kernel up to 240 rows, then split + merge
     (2, 1000, 33, 64, 8, 64, 128),     # band: short kernel, every slot of a block
     (1, 3000, 6, 64, 8, 64, 0),        # split + merge, many splits
+    (1, 320, 12, 8, 2, 64, 0),         # folded splits: 12 pieces over 11 blocks, one empty
     (3, 700, 5, 16, 1, 128, 0),        # q_mult 16, d 128
     (2, 250, 12, 24, 4, 96, 0),        # d 96, q_mult 6, across the short/split boundary
     (1, 77, 5, 8, 8, 96, 50),          # q_mult 1, band narrower than a block
