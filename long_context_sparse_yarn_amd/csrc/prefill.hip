@@ -225,14 +225,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   const int hi = P_max + 1;   // keys >= hi are masked for every row here
   const int t_first = lo / kTile, t_last = (hi - 1) / kTile;
 
-  // ---- tile loads.  Full tiles go global -> LDS directly (16 bytes per
-  // lane, lane l of a wave writing LDS slot l of a 1 KB block), each lane
-  // fetching the chunk that the swizzled layout puts in its slot.  K rows
-  // at or past hi (keys after the last query, all masked) are fetched from
-  // row hi-1 so that unwritten cache rows are never read.  V of the one
-  // tile that straddles hi goes through registers instead, with the keys
-  // at or past hi zeroed (their probabilities are exactly 0, but 0 * NaN
-  // would not be).
+  // ---- tile loads.  Tiles go global -> LDS directly (16 bytes per lane,
+  // lane l of a wave writing LDS slot l of a 1 KB block), each lane
+  // fetching the chunk that the swizzled layout puts in its slot.  Keys at
+  // or past hi (after the block's last query) are masked; the rows below
+  // wr (the chunk's end: the caller appended the chunk before attending)
+  // hold written values, so a tile that ends at or below wr loads whole.
+  // Only a tile that crosses wr (the chunk's last query block) is
+  // different: its K rows at or past hi are fetched from row hi-1 and its
+  // V goes through registers with the keys at or past hi zeroed, so that
+  // unwritten cache rows are never read (a probability is exactly 0 there,
+  // but 0 * NaN would not be).
+  const int wr = (int)a.q_offset + a.T_q;
   const int krow_stride = a.n_kv * D;                  // elements per cache row
   const int vblk_stride = a.n_kv * D * 32;             // elements per 32-key block
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.kc) + ((int64_t)b * C * a.n_kv + g) * D;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   auto load_k = [&](int buf, int t) __attribute__((always_inline)) {
     const int k0 = t * kTile;
     const uint16_t* kt = kbase + (int64_t)k0 * krow_stride;     // uniform
-    const bool full = k0 + kTile <= hi;
+    const bool full = k0 + kTile <= wr;
     const int last_row = hi - 1 - k0;
 #pragma unroll
     for (int i = 0; i < KBW; ++i) {
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     }
   };
   auto load_v = [&](int buf, int t) __attribute__((always_inline)) {
-    if (t * kTile + kTile <= hi)
+    if (t * kTile + kTile <= wr)
       load_v_full(buf, t);
     else
       store_v_regs(buf, t, false);
