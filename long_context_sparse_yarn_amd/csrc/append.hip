@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int64_t 
                     kk0);
 }
 
-template <int ELT>
+template <int ELT, int BATCH>
 __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar, int64_t kb0,
                                                                int nblk, int hc, int ngr, int qpg) {
   typedef typename std::conditional<ELT == 2, uint16_t, uint32_t>::type E;
@@ -271,12 +271,28 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(AppendRopeArgs ar
           st16(cdst + r * cd_stride + cc0 + half, w2);
         }
       }
-      for (int r = cr0 + kMaxRows * crstep; r < nk; r += crstep) {
-        const u32x4 u = ld16(csrc + r * cs_stride + cc0), v = ld16(csrc + r * cs_stride + cc0 + half);
-        u32x4 w1, w2;
-        sa_rope::rot8_bf16(u, v, &tab32[r * half + cc0], &tab[r * half + cc0], k2, &w1, &w2);
-        st16(cdst + r * cd_stride + cc0, w1);
-        st16(cdst + r * cd_stride + cc0 + half, w2);
+      // in batches of BATCH rows whose loads are all issued before the first
+      // is used (see the launcher)
+      constexpr int kBatch = BATCH;
+      for (int r = cr0 + kMaxRows * crstep; r < nk; r += kBatch * crstep) {
+        u32x4 u[kBatch], v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int rr = min(r + k * crstep, nk - 1);   // past the block: a repeat, not stored
+          u[k] = ld16(csrc + rr * cs_stride + cc0);
+          v[k] = ld16(csrc + rr * cs_stride + cc0 + half);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int rr = r + k * crstep;
+          if (rr < nk) {
+            u32x4 w1, w2;
+            sa_rope::rot8_bf16(u[k], v[k], &tab32[rr * half + cc0], &tab[rr * half + cc0], k2, &w1,
+                               &w2);
+            st16(cdst + rr * cd_stride + cc0, w1);
+            st16(cdst + rr * cd_stride + cc0 + half, w2);
+          }
+        }
       }
     }
     return;
@@ -379,9 +395,23 @@ hipError_t launch_append_rope(const AppendRopeArgs& ar, int elt_bytes, hipStream
   const int qpg = n_q ? (n_q + ngr - 1) / ngr : 0;
   const int64_t grid = (int64_t)nblk * ngr * a.B;
   const size_t lds = tab;
-  if (elt_bytes == 2)
-    hipLaunchKernelGGL(append_rope_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc, ngr, qpg);
-  else
-    hipLaunchKernelGGL(append_rope_kernel<4>, dim3((unsigned)grid), dim3(kThreads), lds, s, ar, kb0, nblk, hc, ngr, qpg);
+  // With few workgroups (under two per CU) each thread has several rows and
+  // nothing else hides their loads' latency: batches of four rows, loaded
+  // together (one sequence's 2048-row chunk, 64/8 heads, d 64: 320
+  // workgroups, 13.2 against 15.0 us).  With more workgroups the batch's
+  // registers cost a wave per SIMD and one row at a time is faster (the
+  // same heads over 8192 rows: 29.8 against 33.3 us).
+  const bool batch = grid < 2 * 256;
+  if (elt_bytes == 2) {
+    if (batch)
+      hipLaunchKernelGGL((append_rope_kernel<2, 4>), dim3((unsigned)grid), dim3(kThreads), lds, s, ar,
+                         kb0, nblk, hc, ngr, qpg);
+    else
+      hipLaunchKernelGGL((append_rope_kernel<2, 1>), dim3((unsigned)grid), dim3(kThreads), lds, s, ar,
+                         kb0, nblk, hc, ngr, qpg);
+  } else {
+    hipLaunchKernelGGL((append_rope_kernel<4, 1>), dim3((unsigned)grid), dim3(kThreads), lds, s, ar,
+                       kb0, nblk, hc, ngr, qpg);
+  }
   return hipGetLastError();
 }
