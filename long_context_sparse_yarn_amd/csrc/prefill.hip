@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   auto Vb = [&](int buf) __attribute__((always_inline)) { return lds + 3 * KBUF + buf * VBUF; };
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   const int j = lane & 15;
   const int g4 = lane >> 4;
 
@@ -247,8 +247,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   constexpr int VBLK = D / 8;                     // 1 KB blocks per V tile (2D rows of 4 slots)
   constexpr int KBW = (KBLK + NW - 1) / NW;       // blocks per wave
   constexpr int VBW = (VBLK + NW - 1) / NW;
-  // K slot of block wave + i*NW: row k_r, chunk k_c, element offset k_goff
-  // within the tile.
+  // K slot of block wave + i*NW: row k_r, chunk k_c, byte offset k_goff
+  // within the tile (byte offsets from a uniform base: the loads take a
+  // scalar base and a 32-bit vector offset, no 64-bit address arithmetic).
   int k_r[KBW], k_c[KBW];
   uint32_t k_goff[KBW], v_goff[VBW];
 #pragma unroll
@@ -257,14 +258,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     const int r = (s / NSK) & 63;
     k_r[i] = r;
     k_c[i] = (s % NSK) ^ k_swz<D>(r);
-    k_goff[i] = (uint32_t)(r * krow_stride + 8 * k_c[i]);
+    k_goff[i] = (uint32_t)(2 * (r * krow_stride + 8 * k_c[i]));
   }
 #pragma unroll
   for (int i = 0; i < VBW; ++i) {
     const int s = 64 * (wave + i * NW) + lane;
     const int r = (s >> 2) % (2 * D);
     const int c = (s & 3) ^ ((r >> 1) & 3);
-    v_goff[i] = (uint32_t)((r >= D ? vblk_stride : 0) + (r % D) * 32 + 8 * c);
+    v_goff[i] = (uint32_t)(2 * ((r >= D ? vblk_stride : 0) + (r % D) * 32 + 8 * c));
   }
   auto load_k = [&](int buf, int t) __attribute__((always_inline)) {
     const int k0 = t * kTile;
@@ -276,8 +277,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       const int blk = wave + i * NW;
       if (KBLK % NW == 0 || blk < KBLK) {
         const uint32_t off = full ? k_goff[i]
-                                  : (uint32_t)(min(k_r[i], last_row) * krow_stride + 8 * k_c[i]);
-        lds_direct16(kt + off, &Kb(buf)[512 * blk]);
+                                  : (uint32_t)(2 * (min(k_r[i], last_row) * krow_stride + 8 * k_c[i]));
+        lds_direct16(reinterpret_cast<const char*>(kt) + off, &Kb(buf)[512 * blk]);
       }
     }
   };
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int i = 0; i < VBW; ++i) {
       const int blk = wave + i * NW;
       if (VBLK % NW == 0 || blk < VBLK)
-        lds_direct16(vt + v_goff[i], &Vb(buf)[512 * blk]);
+        lds_direct16(reinterpret_cast<const char*>(vt) + v_goff[i], &Vb(buf)[512 * blk]);
     }
   };
   // Register path: thread c of the workgroup moves chunks c, c + kThreads,
