@@ -55,6 +55,11 @@ namespace {
 
 constexpr int kTile = 64;  // keys per tile
 constexpr float kHeadroom = 18446744073709551616.0f;   // 2^64: largest tile sum kept
+// neg_ref of a query with no reference yet: every allowed score then gives
+// p = 2^(s*scale + 2^100) = inf, so the unit's sum fails the headroom test
+// and the slow path sets a reference, with no test of its own per unit;
+// masked scores (-inf) still give p = 0.
+constexpr float kNoRef = 1267650600228229401496703205376.0f;   // 2^100
 
 // 16 bytes from global memory straight into LDS: lane l of the wave writes
 // LDS bytes [16 l, 16 l + 16) of the block at lds_block (uniform per wave).
@@ -137,8 +142,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   // against it, the sink's included (with matrix-core sums every lane of the
   // column holds the whole sum; with v_dot2 sums each lane holds the sum over
   // its own keys).  No reference (no sink and no allowed key seen yet):
-  // l_run == 0 (matrix-core sums) or m_ref == -inf; neg_ref is 0 until the
-  // slow path sets one.
+  // l_run == 0 (matrix-core sums) or m_ref == -inf, and neg_ref = kNoRef
+  // until the slow path sets one.
   float l_run[NT], m_ref[NT];
   float neg_ref[NT];
   f32x4 O[DT][NT];
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     for (int ks = 0; ks < KS; ++ks)
       qop[n][ks] = rvalid[n] ? ld16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
     const float sg = a.sinks[head[n]] * SA_LOG2E;
-    neg_ref[n] = sg == -INFINITY ? 0.f : -sg;
+    neg_ref[n] = sg == -INFINITY ? kNoRef : -sg;
     m_ref[n] = sg;
     l_run[n] = (sg != -INFINITY && (kMfmaSums || g4 == 0)) ? 1.0f : 0.0f;
 #pragma unroll
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt][n] *= alpha;
       m_ref[n] = m_new;
-      neg_ref[n] = m_new == -INFINITY ? 0.f : -m_new;
+      neg_ref[n] = m_new == -INFINITY ? kNoRef : -m_new;
     }
   };
   // Does the unit starting at key k0h need masking?
@@ -549,10 +554,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
     if constexpr (kOpsAhead) load_ops(on, kbx, hx, vbx, vx);
     probs(Sc, Pc, ls);
     unit_sums(Pc, ls);
+    // a query without a reference gets p = inf here (kNoRef), so this one
+    // test also catches it
     bool bad = false;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      bad |= !(ls[n] <= kHeadroom) || (kMfmaSums ? l_run[n] == 0.f : m_ref[n] == -INFINITY);
+    for (int n = 0; n < NT; ++n) bad |= !(ls[n] <= kHeadroom);
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       // The compiler may not hoist this recomputation onto the fast path
       // (LDS reads can be speculated): the clobber pins it here.

@@ -40,6 +40,10 @@ PREFILL_CASES = [
     (1, 0, 128, 8, 2, 64, 0, False, "f32"),            # the tiny fp32 layers
     (1, 0, 128, 8, 2, 64, 32, False, "f32"),
     (2, 19, 77, 6, 3, 40, 9, True, "f32"),
+    (1, 50, 140, 8, 2, 96, 0, True, "bf16"),           # no sink on the v_dot2-sum shapes
+    (1, 0, 100, 16, 2, 128, 64, True, "bf16"),
+    (1, 70, 190, 16, 2, 64, 0, "mixed", "bf16"),       # every other head without a sink
+    (1, 30, 160, 8, 2, 96, 48, "mixed", "bf16"),
 ]
 
 
@@ -52,7 +56,9 @@ def test_prefill_matches_oracle(B, prefix, T, n_q, n_kv, d, W, sink_inf, dtype):
     q = _draw((B, T, n_q, d), rng, dtype)
     k = _draw((B, T, n_kv, d), rng, dtype)
     v = _draw((B, T, n_kv, d), rng, dtype)
-    sinks = np.full(n_q, -np.inf, np.float32) if sink_inf else rng.standard_normal(n_q).astype(np.float32)
+    sinks = np.full(n_q, -np.inf, np.float32) if sink_inf is True else rng.standard_normal(n_q).astype(np.float32)
+    if sink_inf == "mixed":
+        sinks[::2] = -np.inf
     pk = _draw((B, prefix, n_kv, d), rng, dtype)
     pv = _draw((B, prefix, n_kv, d), rng, dtype)
 
