@@ -91,9 +91,15 @@ __device__ __forceinline__ int k_swz(int r) {
 // the 16-lane V^T operand reads conflict-free.
 __device__ __forceinline__ int v_lds(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
 
+// The d = 64 shape is held to three waves per SIMD (168 VGPRs): its walk in
+// threes of tiles would otherwise take 178 and drop to two; the few values
+// this spills live outside the walk (set-up and epilogue).
+template <int D, int NT, int NW>
+constexpr int prefill_min_waves() { return (D == 64 && NT == 2 && NW == 4) ? 3 : 1; }
+
 template <int D, int NT, int NW, bool ROPE>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int BQ, int n_qb,
-                                                               RopeTab rt) {
+__global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW>())) void prefill_bf16_kernel(
+    AttnArgs a, int BQ, int n_qb, RopeTab rt) {
   constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
   constexpr int DT = D / 16;          // coordinate tiles of O^T
@@ -585,24 +591,39 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
   }
   // unit 2t: S(2t+1) from K(t) half 1; P(2t-1) with V(t-1) half 1.  It reads
   // ahead the operands of unit 2t+1: K(t+1) half 0, V(t) half 0.
-  auto first_unit = [&](int t) __attribute__((always_inline)) {
+  // (c0, c1, c2: the buffers b0, b1, b2 of tile t)
+  auto first_unit_at = [&](int t, int c0, int c1, int c2) __attribute__((always_inline)) {
     const int k0 = t * kTile;
-    unit(S0, S1, P1, P0, OA, OB, b1, 0, b0, 0, b0, 1, k0 + 32, b2, 1, b0, 0, k0,
+    unit(S0, S1, P1, P0, OA, OB, c1, 0, c0, 0, c0, 1, k0 + 32, c2, 1, c0, 0, k0,
          need_mask(k0 + 32));
   };
+  auto first_unit = [&](int t) __attribute__((always_inline)) { first_unit_at(t, b0, b1, b2); };
   // unit 2t+1: S(2t+2) from K(t+1) half 0 (a throw-away after the last tile);
   // P(2t) with V(t) half 0.  It reads ahead the operands of unit 2t+2:
   // K(t+1) half 1 and V(t) half 1, which the loads of tile t+1 (into the
   // buffers of K(t) and V(t-1)) leave in place; after the last tile they are
   // stale and unused.
-  auto second_unit = [&](int t) __attribute__((always_inline)) {
+  auto second_unit_at = [&](int t, int c0, int c1) __attribute__((always_inline)) {
     const int k0 = t * kTile;
-    unit(S1, S0, P0, P1, OB, OA, b1, 1, b0, 1, b1, 0, k0 + kTile, b0, 0, b0, 1, k0 + 32,
+    unit(S1, S0, P0, P1, OB, OA, c1, 1, c0, 1, c1, 0, k0 + kTile, c0, 0, c0, 1, k0 + 32,
          t < t_last && need_mask(k0 + kTile));
   };
-  auto tile_loads = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 <= t_last) load_k(b2, t + 2);
-    if (t + 1 <= t_last) load_v(b1, t + 1);
+  auto second_unit = [&](int t) __attribute__((always_inline)) { second_unit_at(t, b0, b1); };
+  auto tile_loads_at = [&](int t, int c1, int c2) __attribute__((always_inline)) {
+    if (t + 2 <= t_last) load_k(c2, t + 2);
+    if (t + 1 <= t_last) load_v(c1, t + 1);
+  };
+  auto tile_loads = [&](int t) __attribute__((always_inline)) { tile_loads_at(t, b1, b2); };
+  // A whole tile with its buffers as constants: three in a row bring the
+  // rotation back to where it started, and with constant buffers the LDS
+  // addresses of the unit's reads fold into the instructions' offsets (no
+  // vector address arithmetic per unit).
+  auto whole_tile_at = [&](int t, int c0, int c1, int c2) __attribute__((always_inline)) {
+    tile_loads_at(t, c1, c2);
+    first_unit_at(t, c0, c1, c2);
+    second_unit_at(t, c0, c1);
+    wait_vmem();
+    __syncthreads();
   };
   auto tile_end = [&]() __attribute__((always_inline)) {
     wait_vmem();
@@ -619,6 +640,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(AttnArgs a, int B
       second_unit(t);
       tile_end();
       ++t;
+    }
+    if (!skip_head) {            // buffers (0, 1, 2) at tile t: whole tiles in threes
+      for (; t + 3 <= t_last; t += 3) {
+        whole_tile_at(t, 0, 1, 2);
+        whole_tile_at(t + 1, 1, 2, 0);
+        whole_tile_at(t + 2, 2, 0, 1);
+      }
     }
     for (; t < t_last; ++t) {    // whole tiles
       tile_loads(t);
