@@ -91,14 +91,16 @@ __device__ __forceinline__ int k_swz(int r) {
 // the 16-lane V^T operand reads conflict-free.
 __device__ __forceinline__ int v_lds(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
 
-// The d = 64 shape is held to three waves per SIMD (168 VGPRs): its walk in
-// threes of tiles would otherwise take 178 and drop to two; the few values
-// this spills live outside the walk (set-up and epilogue).
-template <int D, int NT, int NW>
-constexpr int prefill_min_waves() { return (D == 64 && NT == 2 && NW == 4) ? 3 : 1; }
+// Full-causal walks at d = 64 take whole tiles in threes (LONG): that shape
+// is held to three waves per SIMD (168 VGPRs), which its walk in threes
+// would otherwise take to 178 (two waves); the few values this spills live
+// outside the walk (set-up and epilogue).  Band layers (walks of three
+// tiles or fewer) keep the plain walk and no spills.
+template <int D, int NT, int NW, bool LONG>
+constexpr int prefill_min_waves() { return (LONG && D == 64 && NT == 2 && NW == 4) ? 3 : 1; }
 
-template <int D, int NT, int NW, bool ROPE>
-__global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW>())) void prefill_bf16_kernel(
+template <int D, int NT, int NW, bool ROPE, bool LONG>
+__global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW, LONG>())) void prefill_bf16_kernel(
     AttnArgs a, int BQ, int n_qb, RopeTab rt) {
   constexpr int kThreads = NW * 64;
   constexpr int KS = D / 32;          // contraction steps of S^T = K Q^T
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW>())) void pre
       tile_end();
       ++t;
     }
-    if (!skip_head) {            // buffers (0, 1, 2) at tile t: whole tiles in threes
+    if (LONG && !skip_head) {    // buffers (0, 1, 2) at tile t: whole tiles in threes
       for (; t + 3 <= t_last; t += 3) {
         whole_tile_at(t, 0, 1, 2);
         whole_tile_at(t + 1, 1, 2, 0);
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW>())) void pre
   }
 }
 
-template <int D, int NT, int NW>
+template <int D, int NT, int NW, bool LONG>
 hipError_t launch_d(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
   const int rows = NW * NT * 16;
   if (a.q_mult > rows) return hipErrorInvalidValue;
@@ -701,12 +703,12 @@ hipError_t launch_d(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
   RopeTab rt;
   if (rope) {
     rt = *rope;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, true, LONG>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
   } else {
     rt.conc = 0.0;
     rt.pos_base = 0;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, false, LONG>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, s, a, BQ, n_qb, rt);
   }
   return hipGetLastError();
@@ -741,9 +743,13 @@ constexpr int kBandWindowMax = 512;   // windows up to this use the band shape
 hipError_t launch_prefill_bf16(const AttnArgs& a, const RopeTab* rope, hipStream_t s) {
   const bool band = a.window > 0 && a.window <= kBandWindowMax;
   switch (a.d) {
-    case 64: return band ? launch_d<64, SA_PFB64>(a, rope, s) : launch_d<64, SA_PF64>(a, rope, s);
-    case 96: return band ? launch_d<96, SA_PFB96>(a, rope, s) : launch_d<96, SA_PF96>(a, rope, s);
-    case 128: return band ? launch_d<128, SA_PFB128>(a, rope, s) : launch_d<128, SA_PF128>(a, rope, s);
+    case 64:
+      return band ? launch_d<64, SA_PFB64, false>(a, rope, s) : launch_d<64, SA_PF64, true>(a, rope, s);
+    case 96:
+      return band ? launch_d<96, SA_PFB96, false>(a, rope, s) : launch_d<96, SA_PF96, true>(a, rope, s);
+    case 128:
+      return band ? launch_d<128, SA_PFB128, false>(a, rope, s)
+                  : launch_d<128, SA_PF128, true>(a, rope, s);
     default: return hipErrorInvalidValue;
   }
 }
