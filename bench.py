@@ -48,7 +48,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # WRITE_SIZE x 1.0 (factors from a 512 MiB copy: FETCH_SIZE reads 256 MiB,
 # WRITE_SIZE 512 MiB), keyed by (workload, window); valid only while the
 # kernel sources hash to the value they were measured with.
-TRAFFIC = {("handover", 0): {"sources_sha256_16": "61d38240e073d048", "bytes": 519937279}}
+TRAFFIC = {("handover", 0): {"sources_sha256_16": "e28f661f9e32e3cf", "bytes": 536790981}}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_attn.h", "sa_rope.h")   # what the prefill kernel is built from
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
@@ -56,10 +56,11 @@ KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measu
 def prefill_kernel_name(d, band):
     """Template instance sinkattn_prefill launches for head dim d (tile shape
     from the SA_PF* / SA_PFB* defaults in prefill.hip; `false`: Q arrives
-    rotated)."""
+    rotated; the last flag: a full-causal (long-walk) instance)."""
     src = open(os.path.join(ROOT, "long_context_sparse_yarn_amd", "csrc", "prefill.hip")).read()
     m = re.search(r"#define SA_PF%s%d (\d+), (\d+)" % ("B" if band else "", d), src)
-    return ("prefill_bf16_kernel<%d,%s,%s,false>" % (d, m.group(1), m.group(2)) if m
+    return ("prefill_bf16_kernel<%d,%s,%s,false,%s>" % (d, m.group(1), m.group(2),
+                                                       "false" if band else "true") if m
             else "prefill_bf16_kernel<%d>" % d)
 
 
