@@ -43,6 +43,8 @@ PREFILL_CASES = [
     (1, 50, 140, 8, 2, 96, 0, True, "bf16"),           # no sink on the v_dot2-sum shapes
     (1, 0, 100, 16, 2, 128, 64, True, "bf16"),
     (1, 70, 190, 16, 2, 64, 0, "mixed", "bf16"),       # every other head without a sink
+    (1, 2023, 300, 16, 2, 64, 1000, False, "bf16"),    # a band wider than the band shape takes
+    (1, 2000, 300, 16, 2, 64, 1000, False, "bf16"),    #   the full-causal walk (in threes; first unit skipped)
     (1, 30, 160, 8, 2, 96, 48, "mixed", "bf16"),
 ]
 
