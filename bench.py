@@ -492,6 +492,15 @@ def prefill_figures(w, L, ms_b2b, ms_in_step=None):
             "frac_bound": round(tf / min(PEAK_BF16_TFLOPS, fl / by * PEAK_HBM_GBS / 1e3), 4)}
 
 
+def queue_ahead(torch, cycles=30_000_000):
+    """Queue a spin kernel (torch's, `cycles` GPU clock ticks: milliseconds)
+    so that the launches the host issues next wait behind it: the events
+    between them then time the GPU's work, not the Python loop that issues
+    the calls (a band-layer decode kernel runs in a few microseconds, less
+    than one call's host overhead)."""
+    torch.cuda._sleep(cycles)
+
+
 def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
     """The band layer's decode steps on a W-row ring holding the prefix's last
     W rows (appending the whole prefix keeps only those), restored by
@@ -518,6 +527,7 @@ def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(w.decode_steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_ahead(torch)
     t0.record()
     for s in range(w.decode_steps):
         step(s, evs[s])
@@ -565,6 +575,7 @@ def decode_extra(sa, torch, steps_warm=4):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(w.decode_steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead(torch)
         t0.record()
         for s in range(w.decode_steps):
             step(s, evs[s])
@@ -579,6 +590,7 @@ def decode_extra(sa, torch, steps_warm=4):
                                     w.sm_scale, y, workspace=ws, out=out)
         cache.restore(snap)
         torch.cuda.synchronize()
+        queue_ahead(torch)
         t0.record()
         for s in range(w.decode_steps):
             sa.sinkattn_decode_step(cache, toks[s]["q"], toks[s]["k"], toks[s]["v"], sinks, W,
@@ -600,7 +612,11 @@ def decode_extra(sa, torch, steps_warm=4):
             res["band%d_ring" % W] = ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch)
         del cache, ws, toks
         torch.cuda.empty_cache()
-    return {"workload": w.name, **res}
+    return {"workload": w.name, **res,
+            "timing": "attn_kernel_us: events around each step's attention launches; step_us: "
+                      "the separate calls (append_rope_qk, then decode) per step; fused_step_us: "
+                      "sinkattn_decode_step per step; each over 64 steps queued behind a spin "
+                      "kernel, so the events time the GPU, not the host's calls"}
 
 
 QKV_D_MODEL = {"gpt-oss": 2880, "gpt-oss-lite": 768}   # residual widths (study note; visual guide)
@@ -1010,7 +1026,8 @@ def main():
                          "attn_kernel_us": fd["attn_kernel_us"], "step_us": fd["step_us"],
                          "alg_mb_per_step": fd["alg_mb_per_step"], "peak_gbs": PEAK_HBM_GBS,
                          "timing": "events around each step's attention launches (split-KV kernel "
-                                   "+ merge), 64 steps"}
+                                   "+ merge), 64 steps, queued behind a spin kernel so that the "
+                                   "events time the GPU, not the host's calls"}
     cpu = {}
     if not args.no_extra:
         lw = wl.LITE_PREFILL

@@ -49,6 +49,8 @@
 #include "sa_kernels.h"
 #include "sa_rope.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kWaves = 4;
@@ -101,7 +103,7 @@ __device__ __forceinline__ void load_block(BlockOps<D>& o, const uint16_t* kbase
 // Hooks (NoStep, or StepHooks for a fused step): pre() before the first
 // block loads, post(qop) after them (fills qop if the hooks own Q), and
 // subst(kb, ops) on each block's operands before they are used.
-template <int D, class Hooks>
+template <int D, bool SHORT, class Hooks>
 __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, int64_t b0,
                                               int64_t b1, int64_t lo, int64_t hi,
                                               u32x4 (&qop)[D / 32], float& m_run,
@@ -129,9 +131,10 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // values go unused.  With every load issued, the compiler knows how many
   // are in flight and waits for exactly the block it is about to use, not
   // for the prefetched ones behind it.
-  auto load2 = [&](BlockOps<D>(&ops)[2], int64_t kb) {
+  // nu (1 or 2): how many of the two operand sets to fill and use
+  auto loadn = [&](auto nu, BlockOps<D>(&ops)[2], int64_t kb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < decltype(nu)::value; ++u) {
       const int64_t kbu = max((int64_t)0, min(kb + u, b1 - 1));
       load_block<D>(ops[u], kpair + kbu * 32 * kstride, vpair + kbu * vbstride, kstride, j, g4);
     }
@@ -140,10 +143,11 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // repeat load2 made) goes through the same instructions with every key
   // masked and V zeroed, so that every loaded register is consumed on every
   // path and the compiler never has to drain the loads in flight.
-  auto process = [&](BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
+  auto processn = [&](auto nu, BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
+    constexpr int NU = decltype(nu)::value;
     f32x4 Sc[2][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       Sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       Sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       hk.subst(kb + u, cur[u]);
@@ -176,7 +180,7 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -191,7 +195,7 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -209,7 +213,29 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // Two operand sets in turn (no register copies, which would wait for the
   // loads in flight): the loads of one pair of blocks run while the other
   // pair is computed.
+  using One = std::integral_constant<int, 1>;
+  using Two = std::integral_constant<int, 2>;
+  auto load2 = [&](BlockOps<D>(&ops)[2], int64_t kb) { loadn(Two{}, ops, kb); };
+  auto process = [&](BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
+    processn(Two{}, cur, kb);
+  };
   BlockOps<D> A[2], Bo[2];
+  // A short span's waves (one or two blocks each, none for an empty run)
+  // load and multiply only their own blocks: no repeat of the last one and
+  // no prefetch behind it.
+  if (SHORT && b1 - b0 <= 2) {
+    hk.pre();
+    if (b1 - b0 == 2) {
+      loadn(Two{}, A, b0);
+      hk.post(qop);
+      processn(Two{}, A, b0);
+    } else {
+      loadn(One{}, A, b0);
+      hk.post(qop);
+      processn(One{}, A, b0);
+    }
+    return;
+  }
   hk.pre();
   load2(A, b0);
   hk.post(qop);
@@ -511,11 +537,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const St
     const int64_t kb_new = st->row / 32;
     StepHooks<D, 64, WaveSync> hk(a, *st, step_lds + wave * StepStage<D>::bytes(a.q_mult),
                                   b, g, lane, b0 <= kb_new && kb_new < b1);
-    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+    decode_blocks<D, false>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   } else {
     load_q<D>(a, b, g, qop);
     NoStep hk;
-    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+    decode_blocks<D, false>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   }
   l_run = sum_over_col(l_run);
   if constexpr (FOLD) {
@@ -585,11 +611,11 @@ __device__ __forceinline__ void decode_short_body(const AttnArgs& a, const StepA
   if constexpr (STEP) {   // one stage for the workgroup; every thread takes part
     extern __shared__ __attribute__((aligned(16))) char step_lds[];
     StepHooks<D, kShortThreads, GroupSync> hk(a, *st, step_lds, b, g, threadIdx.x, true);
-    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+    decode_blocks<D, true>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   } else {
     load_q<D>(a, b, g, qop);
     NoStep hk;
-    decode_blocks<D>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
+    decode_blocks<D, true>(a, b, g, b0, b1, lo, hi, qop, m_run, l_run, O, hk);
   }
   l_run = sum_over_col(l_run);
 #pragma unroll
