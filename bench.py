@@ -501,6 +501,21 @@ def queue_ahead(torch, cycles=30_000_000):
     torch.cuda._sleep(cycles)
 
 
+def decode_back_to_back(sa, torch, q, cache, sinks, W, sm_scale, ws, out):
+    """ms per sinkattn_decode launch, KERNEL_REPEAT launches between one pair
+    of events (queued behind a spin kernel): the cache as the last step left
+    it and that step's rotated Q, so every launch does that step's work."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    queue_ahead(torch)
+    a.record()
+    for _ in range(KERNEL_REPEAT):
+        sa.sinkattn_decode(q, cache, sinks, W, sm_scale, workspace=ws, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / KERNEL_REPEAT
+
+
 def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
     """The band layer's decode steps on a W-row ring holding the prefix's last
     W rows (appending the whole prefix keeps only those), restored by
@@ -535,7 +550,10 @@ def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
     torch.cuda.synchronize()
     kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     step_ms = t0.elapsed_time(t1) / w.decode_steps
-    return {"attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+    b2b_ms = decode_back_to_back(sa, torch, qbuf, ring, sinks, W, w.sm_scale, ws, out)
+    return {"attn_kernel_us": round(kms * 1e3, 2),
+            "attn_kernel_us_back_to_back": round(b2b_ms * 1e3, 2),
+            "step_us": round(step_ms * 1e3, 2),
             "kv_bytes": w.B * W * w.n_kv * w.d_h * 2 * 2}
 
 
@@ -598,12 +616,15 @@ def decode_extra(sa, torch, steps_warm=4):
         t1.record()
         torch.cuda.synchronize()
         fused_ms = t0.elapsed_time(t1) / w.decode_steps
+        b2b_ms = decode_back_to_back(sa, torch, qbuf, cache, sinks, W, w.sm_scale, ws, out)
         rows = [min(w.prefix + s + 1, W) if W > 0 else w.prefix + s + 1
                 for s in range(w.decode_steps)]
         by = np.mean([(r * w.n_kv * w.d_h * 2 * 2 + 2 * w.n_q * w.d_h * 2) * w.B for r in rows])
         gbs = by / (kms * 1e-3) / 1e9
         res["full" if W == 0 else "band%d" % W] = {
-            "attn_kernel_us": round(kms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+            "attn_kernel_us": round(kms * 1e3, 2),
+            "attn_kernel_us_back_to_back": round(b2b_ms * 1e3, 2),
+            "step_us": round(step_ms * 1e3, 2),
             "fused_step_us": round(fused_ms * 1e3, 2),
             "alg_mb_per_step": round(by / 1e6, 3), "gbs": round(gbs, 1),
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
@@ -613,7 +634,10 @@ def decode_extra(sa, torch, steps_warm=4):
         del cache, ws, toks
         torch.cuda.empty_cache()
     return {"workload": w.name, **res,
-            "timing": "attn_kernel_us: events around each step's attention launches; step_us: "
+            "timing": "attn_kernel_us: events around each step's attention launches (the "
+                      "events' own cost included: ~2-3 us, which dominates a band layer's figure); "
+                      "attn_kernel_us_back_to_back: %d attention launches at the last step's state "
+                      "between one pair of events; step_us: " % KERNEL_REPEAT +
                       "the separate calls (append_rope_qk, then decode) per step; fused_step_us: "
                       "sinkattn_decode_step per step; each over 64 steps queued behind a spin "
                       "kernel, so the events time the GPU, not the host's calls"}

@@ -133,6 +133,8 @@ DECODE_CASES = [
     (1, 150, 3, 8, 2, 96, 0, "bf16", True),            # no sink, whole cache in one split
     (1, 320, 12, 8, 2, 64, 0, "bf16", False),          # folded splits: 12 pieces over 11 blocks, one empty
     (1, 5000, 2, 32, 8, 64, 0, "bf16", True),          # no sink, folded splits
+    (1, 600, 3, 16, 2, 64, 256, "bf16", False),        # 256-row band: nine blocks, one wave walks three
+    (2, 250, 10, 16, 4, 64, 0, "bf16", True),          # full layer across 256 rows: short, then split
     (1, 120, 4, 8, 2, 64, 0, "f32", False),
     (1, 120, 4, 8, 2, 64, 32, "f32", False),
     (1, 300, 2, 8, 2, 64, 0, "f32", True),

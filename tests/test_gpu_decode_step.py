@@ -43,6 +43,7 @@ STEP_CASES = [
     (2, 250, 12, 24, 4, 96, 0),        # d 96, q_mult 6, across the short/split boundary
     (1, 77, 5, 8, 8, 96, 50),          # q_mult 1, band narrower than a block
     (1, 2000, 4, 32, 4, 128, 512),     # band wider than the short kernel's span
+    (1, 600, 8, 16, 2, 64, 256),       # 256-row band: nine blocks (one wave walks three), then eight
 ]
 
 
