@@ -375,18 +375,38 @@ __global__ __launch_bounds__(NW * 64, (prefill_min_waves<D, NT, NW, LONG>())) vo
   };
   // Lane (j, g4) holds, for M tile mm and element r, the score of key
   // k0h + 8*g4 + 4*mm + r; keys after the query or outside its band get -inf.
+  // A key is allowed when d = p - key >= 0 and, in a band, d < W; with
+  // d >= 0 the second test is an unsigned compare, and without a band its
+  // limit passes every d.  Both tests are evaluated (no short circuit), so
+  // the compiler keeps them as two compares and a select per score rather
+  // than branching around the second.
+  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0xFFFFFFF0u;
   auto apply_mask = [&](Scores& S, int k0h) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const int rel0 = k0h + 8 * g4 - ((int)a.q_offset + tpos[n]);   // key - p at (mm, r) = 0
+      if constexpr (LONG) {
+        // (the full-causal instance, whose masked units are the diagonal's
+        // few, keeps this form: the other costs it spilled registers)
+        const int rel0 = k0h + 8 * g4 - ((int)a.q_offset + tpos[n]);   // key - p at (mm, r) = 0
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
+        for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rel = rel0 + 4 * mm + r;
-          const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
-          S.v[mm][n][r] = ok ? S.v[mm][n][r] : -INFINITY;
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int rel = rel0 + 4 * mm + r;
+            const bool ok = rel <= 0 && (a.window <= 0 || rel > -a.window);
+            S.v[mm][n][r] = ok ? S.v[mm][n][r] : -INFINITY;
+          }
+      } else {
+        const int d0 = (int)a.q_offset + tpos[n] - (k0h + 8 * g4);   // p - key at (mm, r) = 0
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 4 * mm + r;
+            const bool ok = (d0 >= c) & ((uint32_t)d0 < wlim + (uint32_t)c);
+            S.v[mm][n][r] = ok ? S.v[mm][n][r] : -INFINITY;
+          }
+      }
     }
   };
   // p = 2^(s*scale + neg_ref), rounded to bf16 once; on the v_dot2 path ls
