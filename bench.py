@@ -48,7 +48,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # WRITE_SIZE x 1.0 (factors from a 512 MiB copy: FETCH_SIZE reads 256 MiB,
 # WRITE_SIZE 512 MiB), keyed by (workload, window); valid only while the
 # kernel sources hash to the value they were measured with.
-TRAFFIC = {("handover", 0): {"sources_sha256_16": "e28f661f9e32e3cf", "bytes": 536790981}}
+TRAFFIC = {("handover", 0): {"sources_sha256_16": "5d319fe836e3b076", "bytes": 536790269}}
 KERNEL_SOURCES = ("prefill.hip", "sa_device.h", "sa_attn.h", "sa_rope.h")   # what the prefill kernel is built from
 KERNEL_REPEAT = 20             # back-to-back launches per kernel-duration measurement
 
@@ -179,6 +179,7 @@ def time_prefill_step(w, sa, torch, steps, warmup):
     b2b = {}
     for i, L in enumerate(layers):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead(torch)     # a band layer's launch is about as short as a call's host time
         a.record()
         for _ in range(KERNEL_REPEAT):
             sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, L.q_offset,
@@ -341,6 +342,7 @@ def time_handover(w, sa, torch, steps, warmup, settle_ms):
     for L in layers:
         L.prefill(w, sa)
         a, b = E(), E()
+        queue_ahead(torch)     # a band layer's launch is about as short as a call's host time
         a.record()
         for _ in range(KERNEL_REPEAT):
             sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, w.prefix, out=L.out)
@@ -407,6 +409,7 @@ def abi_call_figures(w, L, sa, torch):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead(torch)
         a.record()
         for _ in range(KERNEL_REPEAT):
             fn()
@@ -447,6 +450,7 @@ def ring_prefill_figures(w, L, sa, torch):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead(torch)
         a.record()
         for _ in range(KERNEL_REPEAT):
             fn()
@@ -496,8 +500,9 @@ def queue_ahead(torch, cycles=30_000_000):
     """Queue a spin kernel (torch's, `cycles` GPU clock ticks: milliseconds)
     so that the launches the host issues next wait behind it: the events
     between them then time the GPU's work, not the Python loop that issues
-    the calls (a band-layer decode kernel runs in a few microseconds, less
-    than one call's host overhead)."""
+    the calls (a band-layer decode kernel runs in a few microseconds, and a
+    band-layer prefill or a RoPE pass in ten to twenty, about what a call
+    costs the host)."""
     torch.cuda._sleep(cycles)
 
 
