@@ -179,7 +179,7 @@ def time_prefill_step(w, sa, torch, steps, warmup):
     b2b = {}
     for i, L in enumerate(layers):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        queue_ahead(torch)     # a band layer's launch is about as short as a call's host time
+        queue_ahead(torch, KERNEL_REPEAT)   # a band layer's launch: about a call's host time
         a.record()
         for _ in range(KERNEL_REPEAT):
             sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, L.q_offset,
@@ -342,7 +342,7 @@ def time_handover(w, sa, torch, steps, warmup, settle_ms):
     for L in layers:
         L.prefill(w, sa)
         a, b = E(), E()
-        queue_ahead(torch)     # a band layer's launch is about as short as a call's host time
+        queue_ahead(torch, KERNEL_REPEAT)   # a band layer's launch: about a call's host time
         a.record()
         for _ in range(KERNEL_REPEAT):
             sa.sinkattn_prefill(L.qw, L.cache, L.sinks, L.window, w.sm_scale, w.prefix, out=L.out)
@@ -409,7 +409,7 @@ def abi_call_figures(w, L, sa, torch):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        queue_ahead(torch)
+        queue_ahead(torch, 2 * KERNEL_REPEAT)   # (a restore and a call each)
         a.record()
         for _ in range(KERNEL_REPEAT):
             fn()
@@ -450,7 +450,7 @@ def ring_prefill_figures(w, L, sa, torch):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        queue_ahead(torch)
+        queue_ahead(torch, 5 * KERNEL_REPEAT)   # (up to five calls a pass)
         a.record()
         for _ in range(KERNEL_REPEAT):
             fn()
@@ -496,14 +496,15 @@ def prefill_figures(w, L, ms_b2b, ms_in_step=None):
             "frac_bound": round(tf / min(PEAK_BF16_TFLOPS, fl / by * PEAK_HBM_GBS / 1e3), 4)}
 
 
-def queue_ahead(torch, cycles=30_000_000):
-    """Queue a spin kernel (torch's, `cycles` GPU clock ticks: milliseconds)
-    so that the launches the host issues next wait behind it: the events
-    between them then time the GPU's work, not the Python loop that issues
-    the calls (a band-layer decode kernel runs in a few microseconds, and a
-    band-layer prefill or a RoPE pass in ten to twenty, about what a call
-    costs the host)."""
-    torch.cuda._sleep(cycles)
+def queue_ahead(torch, calls):
+    """Queue a spin kernel (torch's) about as long as the host needs to issue
+    `calls` library calls (30 us each at most, at 2.4 GHz), so that the
+    launches issued next wait behind it: the events between them then time
+    the GPU's work, not the Python loop that issues the calls (a band-layer
+    decode kernel runs in a few microseconds, and a band-layer prefill or a
+    RoPE pass in ten to twenty, about what a call costs the host).  No longer
+    than that: a GPU left nearly idle behind a long spin lowers its clock."""
+    torch.cuda._sleep(int(calls * 30e-6 * 2.4e9))
 
 
 def decode_back_to_back(sa, torch, q, cache, sinks, W, sm_scale, ws, out):
@@ -512,7 +513,7 @@ def decode_back_to_back(sa, torch, q, cache, sinks, W, sm_scale, ws, out):
     it and that step's rotated Q, so every launch does that step's work."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    queue_ahead(torch)
+    queue_ahead(torch, KERNEL_REPEAT)
     a.record()
     for _ in range(KERNEL_REPEAT):
         sa.sinkattn_decode(q, cache, sinks, W, sm_scale, workspace=ws, out=out)
@@ -547,7 +548,7 @@ def ring_decode_figures(w, W, pk, pv, sinks, toks, y, sa, torch):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(w.decode_steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    queue_ahead(torch)
+    queue_ahead(torch, 2 * w.decode_steps)
     t0.record()
     for s in range(w.decode_steps):
         step(s, evs[s])
@@ -598,7 +599,7 @@ def decode_extra(sa, torch, steps_warm=4):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(w.decode_steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        queue_ahead(torch)
+        queue_ahead(torch, 2 * w.decode_steps)
         t0.record()
         for s in range(w.decode_steps):
             step(s, evs[s])
@@ -613,7 +614,7 @@ def decode_extra(sa, torch, steps_warm=4):
                                     w.sm_scale, y, workspace=ws, out=out)
         cache.restore(snap)
         torch.cuda.synchronize()
-        queue_ahead(torch)
+        queue_ahead(torch, w.decode_steps)
         t0.record()
         for s in range(w.decode_steps):
             sa.sinkattn_decode_step(cache, toks[s]["q"], toks[s]["k"], toks[s]["v"], sinks, W,
