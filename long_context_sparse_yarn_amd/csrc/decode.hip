@@ -104,8 +104,8 @@ __device__ __forceinline__ void load_block(BlockOps<D>& o, const uint16_t* kbase
 // block loads, post(qop) after them (fills qop if the hooks own Q), and
 // subst(kb, ops) on each block's operands before they are used.
 template <int D, bool SHORT, class Hooks>
-__device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, int64_t b0,
-                                              int64_t b1, int64_t lo, int64_t hi,
+__device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, int b0,
+                                              int b1, int64_t lo, int64_t hi,
                                               u32x4 (&qop)[D / 32], float& m_run,
                                               float& l_run, f32x4 (&O)[D / 16], Hooks& hk) {
   constexpr int KS = D / 32;
@@ -132,10 +132,10 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // are in flight and waits for exactly the block it is about to use, not
   // for the prefetched ones behind it.
   // nu (1 or 2): how many of the two operand sets to fill and use
-  auto loadn = [&](auto nu, BlockOps<D>(&ops)[2], int64_t kb) {
+  auto loadn = [&](auto nu, BlockOps<D>(&ops)[2], int kb) {
 #pragma unroll
     for (int u = 0; u < decltype(nu)::value; ++u) {
-      const int64_t kbu = max((int64_t)0, min(kb + u, b1 - 1));
+      const int kbu = max(0, min(kb + u, b1 - 1));
       load_block<D>(ops[u], kpair + kbu * 32 * kstride, vpair + kbu * vbstride, kstride, j, g4);
     }
   };
@@ -143,7 +143,7 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // repeat load2 made) goes through the same instructions with every key
   // masked and V zeroed, so that every loaded register is consumed on every
   // path and the compiler never has to drain the loads in flight.
-  auto processn = [&](auto nu, BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
+  auto processn = [&](auto nu, BlockOps<D>(&cur)[2], int kb) __attribute__((always_inline)) {
     constexpr int NU = decltype(nu)::value;
     f32x4 Sc[2][2];
 #pragma unroll
@@ -151,7 +151,7 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
       Sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       Sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       hk.subst(kb + u, cur[u]);
-      const int64_t k0 = (kb + u) * 32;
+      const int64_t k0 = (int64_t)(kb + u) * 32;
       const int64_t top = kb + u < b1 ? hi : k0;     // keys from top on are masked
       if (k0 + 32 > top) {   // zero V of masked keys (unwritten rows; the repeat)
         const int valid = (int)max((int64_t)-1, top - (k0 + 8 * g4));
@@ -215,8 +215,8 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   // pair is computed.
   using One = std::integral_constant<int, 1>;
   using Two = std::integral_constant<int, 2>;
-  auto load2 = [&](BlockOps<D>(&ops)[2], int64_t kb) { loadn(Two{}, ops, kb); };
-  auto process = [&](BlockOps<D>(&cur)[2], int64_t kb) __attribute__((always_inline)) {
+  auto load2 = [&](BlockOps<D>(&ops)[2], int kb) { loadn(Two{}, ops, kb); };
+  auto process = [&](BlockOps<D>(&cur)[2], int kb) __attribute__((always_inline)) {
     processn(Two{}, cur, kb);
   };
   BlockOps<D> A[2], Bo[2];
@@ -239,13 +239,17 @@ __device__ __forceinline__ void decode_blocks(const AttnArgs& a, int b, int g, i
   hk.pre();
   load2(A, b0);
   hk.post(qop);
-  for (int64_t kb = b0; kb < b1; kb += 4) {
+  // One exit, at the top: a break between the two halves gave the loop a
+  // second way back to its head on which the compiler could not tell the
+  // loads still in flight, so it drained every load at the head of each pass.
+  int kb = b0;
+  for (; kb + 2 < b1; kb += 4) {
     load2(Bo, kb + 2);
     process(A, kb);
-    if (kb + 2 >= b1) break;
     load2(A, kb + 4);
     process(Bo, kb + 2);
   }
+  if (kb < b1) process(A, kb);     // the run's last pair, in A
 }
 
 // The Q^T operand of (b, g): column j = head g*q_mult + j (zero past q_mult).
@@ -526,8 +530,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& da, const St
   const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
   const int64_t pc = FOLD ? (int64_t)split * kWaves + wave : split;   // this wave's piece
   const int64_t np = FOLD ? (int64_t)S * kWaves : S;                  // pieces per (b, g)
-  const int64_t b0 = kb_lo + (pc * nblk) / np;
-  const int64_t b1 = kb_lo + ((pc + 1) * nblk) / np;
+  // block indices fit 32 bits (bf16 caches hold fewer than 2^31 rows); the
+  // bounds are uniform, and kept in scalar registers, so the block loop's
+  // compares and clamps are scalar
+  const int b0 = __builtin_amdgcn_readfirstlane((int)(kb_lo + (pc * nblk) / np));
+  const int b1 = __builtin_amdgcn_readfirstlane((int)(kb_lo + ((pc + 1) * nblk) / np));
 
   u32x4 qop[D / 32];
   float m_run, l_run;
@@ -602,8 +609,8 @@ __device__ __forceinline__ void decode_short_body(const AttnArgs& a, const StepA
   const int64_t lo = a.window > 0 ? max((int64_t)0, P - a.window + 1) : 0;
   const int64_t hi = P + 1;
   const int64_t kb_lo = lo / 32, nblk = (hi + 31) / 32 - kb_lo;
-  const int64_t b0 = kb_lo + (wave * nblk) / kShortWaves;
-  const int64_t b1 = kb_lo + ((wave + 1) * nblk) / kShortWaves;
+  const int b0 = __builtin_amdgcn_readfirstlane((int)(kb_lo + (wave * nblk) / kShortWaves));
+  const int b1 = __builtin_amdgcn_readfirstlane((int)(kb_lo + ((wave + 1) * nblk) / kShortWaves));
 
   u32x4 qop[D / 32];
   float m_run, l_run;
