@@ -462,8 +462,9 @@ size_t sinkattn_decode_workspace_bytes(int B, int n_q, int n_kv, int d_h,
  * sinkattn_decode_workspace_bytes(B, n_q, n_kv, d_h, capacity) bytes, whose
  * contents are overwritten.  The allowed key set is split into chunks
  * reduced in parallel and merged in a fixed order (deterministic), with the
- * sink added once at the merge.  bf16: d_h in {64, 96, 128}, n_q/n_kv <= 16;
- * fp32: as sinkattn_prefill. */
+ * sink added once at the merge.  bf16: d_h in {64, 96, 128}, n_q/n_kv <= 16,
+ * cache capacity below 2^31 rows (SA_ERR_SHAPE otherwise); fp32: as
+ * sinkattn_prefill. */
 int sinkattn_decode(const void* q, const sa_kv_cache* c, const float* sinks,
                     void* out, int B, int n_q, int n_kv, int d_h, int window,
                     float sm_scale, void* workspace, size_t ws_bytes,

@@ -1012,6 +1012,8 @@ int decode_impl(const void* q, const sa_kv_cache* c, const float* sinks, void* o
     if (d_h != 64 && d_h != 96 && d_h != 128)
       return fail(SA_ERR_SHAPE, "bf16 attention supports d_h in {64, 96, 128}, got %d", d_h);
     if (q_mult > 16) return fail(SA_ERR_SHAPE, "bf16 decode needs n_q/n_kv <= 16");
+    if (c->capacity > INT32_MAX)   // the kernels keep 32-key block indices in 32 bits
+      return fail(SA_ERR_SHAPE, "bf16 decode needs a capacity below 2^31 rows");
     const int64_t rows = q_row + 1;
     const int64_t span = a.window > 0 ? std::min<int64_t>(a.window, rows) : rows;
     DecodeArgs da;

@@ -137,6 +137,9 @@ def test_errors_are_reported_before_any_launch():
     assert st == SA_OK
     assert P(q, hbig, s, o, 1, 5, 8, 2, 64, 0, 0.125, 0, None) == SA_ERR_SHAPE
     assert "2^31" in sa.last_error()
+    # so does bf16 decode (its block indices are 32-bit)
+    assert D(q, hbig, s, o, 1, 8, 2, 64, 0, 0.125, o, 1 << 20, None) == SA_ERR_SHAPE
+    assert "2^31" in sa.last_error()
     B._kv_cache_destroy(hbig)
     # prefill with in-kernel rotation: yarn checks and bf16 only, nothing launched
     PR = B._sinkattn_prefill_rope
